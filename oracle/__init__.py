@@ -1,0 +1,10 @@
+"""CPU oracle (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may
+import this package. The HIP library never calls it and shares no code with it.
+"""
+from .decoder import (OracleDecoder, rmsnorm, apply_rope, rope_angles, silu, attend, softmax,
+                      kv_head_of, visible_range, greedy)
+
+__all__ = ["OracleDecoder", "rmsnorm", "apply_rope", "rope_angles", "silu", "attend", "softmax",
+           "kv_head_of", "visible_range", "greedy"]
