@@ -30,7 +30,8 @@ choice, stated once here):
     key counts toward W); W = 0 means full causal attention;
   * SwiGLU: silu(gate) * up, silu(u) = u / (1 + exp(-u)); no biases; scores
     scaled by 1/sqrt(hd);
-  * greedy choice = the lowest index among the maximal logits.
+  * greedy choice = the lowest index among the maximal logits, compared in
+    float32 (the precision the GPU path decides in).
 """
 from __future__ import annotations
 
@@ -102,8 +103,12 @@ def attend(q, K, V, n_kv):
 
 
 def greedy(logits):
-    """Index of the maximal logit; the lowest such index on exact ties."""
-    return int(np.argmax(logits))
+    """Index of the maximal logit; the lowest such index on exact ties.
+
+    The choice is taken on the logits rounded to float32, the precision in
+    which the GPU path holds and compares its logits, so both sides decide in
+    the same precision."""
+    return int(np.argmax(np.asarray(logits, dtype=F64).astype(np.float32)))
 
 
 def to_cache(a, kv_fp16):

@@ -334,6 +334,9 @@ def test_greedy_ties_lowest_index():
     assert greedy(np.array([1.0, 3.0, 3.0, 2.0])) == 1
     assert greedy(np.zeros(7)) == 0
     assert greedy(np.array([-np.inf, -5.0, -5.0])) == 1
+    # decided in float32: values equal after rounding to float32 tie
+    assert greedy(np.array([1.0, 1.0 + 1e-12, 0.5])) == 0
+    assert greedy(np.array([1.0, 1.0 + 1e-6, 0.5])) == 1
 
 
 def test_generate_feeds_greedy_tokens():
