@@ -1,0 +1,106 @@
+// Device-side building blocks for gfx950 (CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lf {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half_t;
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;          // threads per workgroup for every step kernel
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Device-side sequence state (first bytes of the per-sequence buffer).
+enum StateSlot : int {
+  kLen = 0,       // positions in the cache = position of the next step
+  kArgmax = 1,    // greedy token of the most recent position
+  kFedEnd = 2,    // argmax of position p is stored as token p+1 only if p+1 >= kFedEnd
+  kBadToken = 3,  // set when a token id outside [0, vocab) was clamped
+};
+
+// 16-byte weight load that bypasses cache residency (weights are read once per step).
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// acc + sum_i w[i] * x[i] over 8 fp16 weights and 8 fp32 inputs.
+__device__ __forceinline__ float dot8(u32x4 w, f32x4 x0, f32x4 x1, float acc) {
+  const h8 h = __builtin_bit_cast(h8, w);
+  acc = fmaf(static_cast<float>(h[0]), x0.x, acc);
+  acc = fmaf(static_cast<float>(h[1]), x0.y, acc);
+  acc = fmaf(static_cast<float>(h[2]), x0.z, acc);
+  acc = fmaf(static_cast<float>(h[3]), x0.w, acc);
+  acc = fmaf(static_cast<float>(h[4]), x1.x, acc);
+  acc = fmaf(static_cast<float>(h[5]), x1.y, acc);
+  acc = fmaf(static_cast<float>(h[6]), x1.z, acc);
+  acc = fmaf(static_cast<float>(h[7]), x1.w, acc);
+  return acc;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
+  const h8 h = __builtin_bit_cast(h8, w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
+}
+
+// Butterfly sum over the whole wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Butterfly sum within aligned groups of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sum over the workgroup (kBlock threads); `red` is kWavesPerBlock floats of LDS.
+// Fixed combination order, so the result is deterministic.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+// (value, index) ordering for greedy choice: larger value wins, lower index on ties.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// Signal that this workgroup has finished writing its results, and find out
+// whether it is the last of `expected` workgroups sharing `counter`. Every
+// thread must call it. The last workgroup sees all others' writes after it
+// returns true, and resets the counter for the next launch.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int* flag_lds) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(counter, 1u);
+    *flag_lds = (prev == expected - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *flag_lds != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+__device__ __forceinline__ void reset_counter(unsigned* counter) {
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace lf

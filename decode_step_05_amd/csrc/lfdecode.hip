@@ -1,0 +1,612 @@
+// Host side of lfdecode: configuration checks, memory layout, weight repack,
+// launch plan of one decode step, hipGraph capture and replay, and the C ABI
+// declared in include/lfdecode.h.
+#include "lfdecode.h"
+#include "lf_kernels.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using lf::half_t;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define LF_HIP(call)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (call);                                                       \
+    if (e_ != hipSuccess) return fail(LF_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Attention split plan of one layer: S workgroups per lane, `chunk` keys each.
+struct AttnPlan {
+  int S, chunk;
+};
+
+AttnPlan attn_plan(const lf_config& c, int layer) {
+  const int visible = c.window[layer] > 0 ? std::min(c.window[layer], c.max_ctx) : c.max_ctx;
+  int S = std::max(1, 256 / c.n_lanes);
+  S = std::min(S, 64);
+  S = std::min(S, visible);
+  const int chunk = (visible + S - 1) / S;
+  S = (visible + chunk - 1) / chunk;
+  return {S, chunk};
+}
+
+// Rows per workgroup of a GEMV with `rows` outputs: a multiple of 8 (4 waves x
+// a row pair) chosen so that about 1024 workgroups cover the matrix.
+int rows_per_block(int rows) {
+  const int target_blocks = 1024;
+  int rpb = (rows + target_blocks - 1) / target_blocks;
+  rpb = (rpb + 7) / 8 * 8;
+  return std::max(rpb, 8);
+}
+
+int validate(const lf_config* c) {
+  if (!c) return fail(LF_EINVAL, "config is null");
+  if (c->n_layers < 1 || c->n_layers > LF_MAX_LAYERS) return fail(LF_EINVAL, "n_layers %d out of [1, %d]", c->n_layers, LF_MAX_LAYERS);
+  if (c->d_model < 8 || c->d_model % 8 || c->d_model > 16384) return fail(LF_EINVAL, "d_model %d: need a multiple of 8 in [8, 16384]", c->d_model);
+  if (c->ffn < 8 || c->ffn % 8 || c->ffn > 16384) return fail(LF_EINVAL, "ffn %d: need a multiple of 8 in [8, 16384]", c->ffn);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return fail(LF_EINVAL, "head_dim %d: need 32, 64 or 128", c->head_dim);
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads) return fail(LF_EINVAL, "n_q_heads %d must be a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return fail(LF_EINVAL, "query heads per kv head %d: need 1, 2 or 4", G);
+  if (c->n_lanes < 1 || c->n_q_heads % c->n_lanes || c->n_kv_heads % c->n_lanes || c->ffn % c->n_lanes)
+    return fail(LF_EINVAL, "n_lanes %d must divide n_q_heads, n_kv_heads and ffn", c->n_lanes);
+  const int kpl = c->n_kv_heads / c->n_lanes;
+  if ((512 / c->head_dim) % kpl) return fail(LF_EINVAL, "kv heads per lane %d must divide %d", kpl, 512 / c->head_dim);
+  if (static_cast<long>(c->n_q_heads) * c->head_dim > 16384) return fail(LF_EINVAL, "n_q_heads * head_dim exceeds 16384");
+  if (c->vocab < 0) return fail(LF_EINVAL, "vocab %d < 0", c->vocab);
+  if (c->max_ctx < 1 || c->max_ctx > 4096) return fail(LF_EINVAL, "max_ctx %d out of [1, 4096]", c->max_ctx);
+  for (int l = 0; l < c->n_layers; ++l)
+    if (c->window[l] < 0) return fail(LF_EINVAL, "window[%d] = %d < 0", l, c->window[l]);
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(LF_EINVAL, "rope_theta must be > 0 and rms_eps >= 0");
+  return LF_OK;
+}
+
+struct Dims {
+  int L, d, hq, hkv, hd, ffn, V, lanes, ctx, qkv_rows, qdim, qpl, kpl, G;
+};
+
+Dims dims(const lf_config& c) {
+  Dims D;
+  D.L = c.n_layers; D.d = c.d_model; D.hq = c.n_q_heads; D.hkv = c.n_kv_heads; D.hd = c.head_dim;
+  D.ffn = c.ffn; D.V = c.vocab; D.lanes = c.n_lanes; D.ctx = c.max_ctx;
+  D.qkv_rows = (D.hq + 2 * D.hkv) * D.hd; D.qdim = D.hq * D.hd;
+  D.qpl = D.hq / D.lanes; D.kpl = D.hkv / D.lanes; D.G = D.hq / D.hkv;
+  return D;
+}
+
+// Byte offsets of everything in the model workspace.
+struct WsLayout {
+  std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
+  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, lm_part, counters, total;
+  int S_max, lm_blocks;
+};
+
+WsLayout ws_layout(const lf_config& c) {
+  const Dims D = dims(c);
+  WsLayout W;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t h = sizeof(half_t);
+  for (int l = 0; l < D.L; ++l) {
+    W.wqkv.push_back(take(static_cast<size_t>(D.qkv_rows) * D.d * h));
+    W.wo.push_back(take(static_cast<size_t>(D.d) * D.qdim * h));
+    W.wgu.push_back(take(static_cast<size_t>(2) * D.ffn * D.d * h));
+    W.wd.push_back(take(static_cast<size_t>(D.d) * D.ffn * h));
+    W.g1.push_back(take(D.d * h));
+    W.g2.push_back(take(D.d * h));
+  }
+  if (D.V) {
+    W.embed = take(static_cast<size_t>(D.V) * D.d * h);
+    W.lm = take(static_cast<size_t>(D.V) * D.d * h);
+    W.gf = take(D.d * h);
+  }
+  W.rope = take(static_cast<size_t>(D.ctx) * (D.hd / 2) * sizeof(float2));
+  W.x = take(D.d * sizeof(float));
+  W.q = take(D.qdim * sizeof(float));
+  W.o = take(D.qdim * sizeof(float));
+  W.act = take(D.ffn * sizeof(float));
+  W.S_max = 1;
+  for (int l = 0; l < D.L; ++l) W.S_max = std::max(W.S_max, attn_plan(c, l).S);
+  W.part_ml = take(static_cast<size_t>(D.hq) * W.S_max * sizeof(float2));
+  W.part_acc = take(static_cast<size_t>(D.hq) * W.S_max * D.hd * sizeof(float));
+  W.lm_blocks = D.V ? (D.V + rows_per_block(D.V) - 1) / rows_per_block(D.V) : 1;
+  W.lm_part = take(static_cast<size_t>(W.lm_blocks) * sizeof(float2));
+  W.counters = take((D.lanes + 4) * sizeof(unsigned));
+  W.total = off;
+  return W;
+}
+
+// Byte offsets in the per-sequence buffer.
+struct KvLayout {
+  size_t state, tokens, logits, K, V, total, cache_bytes;
+};
+
+KvLayout kv_layout(const lf_config& c) {
+  const Dims D = dims(c);
+  KvLayout K;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  K.state = take(64 * sizeof(int32_t));
+  K.tokens = take(static_cast<size_t>(D.ctx + 1) * sizeof(int32_t));
+  K.logits = take(static_cast<size_t>(std::max(D.V, 1)) * sizeof(float));
+  K.cache_bytes = static_cast<size_t>(D.L) * D.lanes * D.ctx * D.kpl * D.hd * sizeof(half_t);
+  K.K = take(K.cache_bytes);
+  K.V = take(K.cache_bytes);
+  K.total = off;
+  return K;
+}
+
+}  // namespace
+
+struct GraphEntry {
+  lf_kv* kv;
+  const void* xin;
+  void* xout;
+  hipGraphExec_t exec;
+};
+
+struct lf_model {
+  lf_config cfg;
+  Dims D;
+  WsLayout W;
+  char* ws;
+  bool use_graph = true;
+  hipStream_t capture_stream = nullptr;  // graphs are recorded here, replayed on the caller's stream
+  std::vector<GraphEntry> graphs;
+
+  template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+};
+
+struct lf_kv {
+  lf_model* m;
+  char* buf;
+  KvLayout K;
+  int32_t len;
+  int32_t* state() const { return reinterpret_cast<int32_t*>(buf + K.state); }
+  int32_t* tokens() const { return reinterpret_cast<int32_t*>(buf + K.tokens); }
+  float* logits() const { return reinterpret_cast<float*>(buf + K.logits); }
+  half_t* kc() const { return reinterpret_cast<half_t*>(buf + K.K); }
+  half_t* vc() const { return reinterpret_cast<half_t*>(buf + K.V); }
+};
+
+namespace {
+
+template <int EPI>
+void launch_gemv(const lf::GemvArgs& a, hipStream_t st) {
+  const int nblk = (a.rows + a.rows_per_block - 1) / a.rows_per_block;
+  const size_t lds = static_cast<size_t>(a.K) * sizeof(float);
+  hipLaunchKernelGGL((lf::k_gemv<EPI, 2, 8>), dim3(nblk), dim3(lf::kBlock), lds, st, a);
+}
+
+template <int HD, int G>
+void launch_attn_t(const lf::AttnArgs& a, int lanes, hipStream_t st) {
+  hipLaunchKernelGGL((lf::k_attn<HD, G, 4>), dim3(a.S, lanes), dim3(lf::kBlock), 0, st, a);
+}
+
+void launch_attn(const lf::AttnArgs& a, int hd, int G, int lanes, hipStream_t st) {
+#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, lanes, st);
+  LF_ATTN_CASE(32, 1) LF_ATTN_CASE(32, 2) LF_ATTN_CASE(32, 4)
+  LF_ATTN_CASE(64, 1) LF_ATTN_CASE(64, 2) LF_ATTN_CASE(64, 4)
+  LF_ATTN_CASE(128, 1) LF_ATTN_CASE(128, 2) LF_ATTN_CASE(128, 4)
+#undef LF_ATTN_CASE
+}
+
+int set_lds_limits() {
+  const int bytes = 16384 * sizeof(float);
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiQKV, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiSwiGLU, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiResid, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiLogits, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  return LF_OK;
+}
+
+// Enqueue every kernel of one step. xin/xout: hidden mode input/output (null in token mode).
+int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
+  const Dims& D = m->D;
+  const WsLayout& W = m->W;
+  const lf_config& c = m->cfg;
+  const bool hidden = D.V == 0;
+  float* resid = hidden ? xout : m->at<float>(W.x);
+  unsigned* counters = m->at<unsigned>(W.counters);
+  const size_t layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
+
+  lf::GemvArgs base{};
+  base.eps = c.rms_eps;
+  base.vocab = D.V;
+  base.state = kv->state();
+  base.tokens = kv->tokens();
+  base.max_ctx = D.ctx;
+  base.hd = D.hd;
+  base.qpl = D.qpl;
+  base.kpl = D.kpl;
+  base.rope = m->at<float2>(W.rope);
+
+  for (int l = 0; l < D.L; ++l) {
+    // RMSNorm + QKV + rotary + KV append
+    lf::GemvArgs a = base;
+    a.W = m->at<half_t>(W.wqkv[l]);
+    a.rows = D.qkv_rows;
+    a.K = D.d;
+    a.rows_per_block = rows_per_block(a.rows);
+    a.gain = m->at<half_t>(W.g1[l]);
+    if (l == 0) {
+      a.in_kind = hidden ? lf::kInNormF32 : lf::kInNormEmbed;
+      a.x = xin;
+      a.emb = hidden ? nullptr : m->at<half_t>(W.embed);
+      a.resid_copy = resid;
+    } else {
+      a.in_kind = lf::kInNormF32;
+      a.x = resid;
+    }
+    a.q = m->at<float>(W.q);
+    a.kc = kv->kc() + l * layer_cache;
+    a.vc = kv->vc() + l * layer_cache;
+    launch_gemv<lf::kEpiQKV>(a, st);
+
+    // attention over the visible keys, split over key ranges, merged in-kernel
+    const AttnPlan P = attn_plan(c, l);
+    lf::AttnArgs t{};
+    t.q = m->at<float>(W.q);
+    t.kc = kv->kc() + l * layer_cache;
+    t.vc = kv->vc() + l * layer_cache;
+    t.state = kv->state();
+    t.part_ml = m->at<float2>(W.part_ml);
+    t.part_acc = m->at<float>(W.part_acc);
+    t.o = m->at<float>(W.o);
+    t.counters = counters;
+    t.max_ctx = D.ctx;
+    t.window = c.window[l];
+    t.S = P.S;
+    t.chunk = P.chunk;
+    t.qpl = D.qpl;
+    t.kpl = D.kpl;
+    t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
+    launch_attn(t, D.hd, D.G, D.lanes, st);
+
+    // O projection + residual
+    a = base;
+    a.W = m->at<half_t>(W.wo[l]);
+    a.rows = D.d;
+    a.K = D.qdim;
+    a.rows_per_block = rows_per_block(a.rows);
+    a.in_kind = lf::kInF32;
+    a.x = m->at<float>(W.o);
+    a.y = resid;
+    launch_gemv<lf::kEpiResid>(a, st);
+
+    // RMSNorm + gate/up + SwiGLU
+    a = base;
+    a.W = m->at<half_t>(W.wgu[l]);
+    a.rows = 2 * D.ffn;
+    a.K = D.d;
+    a.rows_per_block = rows_per_block(a.rows);
+    a.in_kind = lf::kInNormF32;
+    a.x = resid;
+    a.gain = m->at<half_t>(W.g2[l]);
+    a.y = m->at<float>(W.act);
+    launch_gemv<lf::kEpiSwiGLU>(a, st);
+
+    // down projection + residual (the last layer ends the step in hidden mode)
+    a = base;
+    a.W = m->at<half_t>(W.wd[l]);
+    a.rows = D.d;
+    a.K = D.ffn;
+    a.rows_per_block = rows_per_block(a.rows);
+    a.in_kind = lf::kInF32;
+    a.x = m->at<float>(W.act);
+    a.y = resid;
+    if (hidden && l == D.L - 1) a.counter = counters + D.lanes;
+    launch_gemv<lf::kEpiResid>(a, st);
+  }
+  if (!hidden) {
+    // final RMSNorm + LM head + greedy argmax; ends the step
+    lf::GemvArgs a = base;
+    a.W = m->at<half_t>(W.lm);
+    a.rows = D.V;
+    a.K = D.d;
+    a.rows_per_block = rows_per_block(a.rows);
+    a.in_kind = lf::kInNormF32;
+    a.x = resid;
+    a.gain = m->at<half_t>(W.gf);
+    a.y = kv->logits();
+    a.counter = counters + D.lanes;
+    a.lm_part = m->at<float2>(W.lm_part);
+    launch_gemv<lf::kEpiLogits>(a, st);
+  }
+  LF_HIP(hipPeekAtLastError());
+  return LF_OK;
+}
+
+int run_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
+  if (!m->use_graph) return enqueue_step(m, kv, xin, xout, st);
+  hipGraphExec_t exec = nullptr;
+  for (const GraphEntry& g : m->graphs)
+    if (g.kv == kv && g.xin == xin && g.xout == xout) exec = g.exec;
+  if (!exec) {
+    // Record on the library's own stream (the caller's may be the legacy
+    // default stream, which cannot be captured); nothing executes here.
+    hipStream_t cs = m->capture_stream;
+    LF_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    const int rc = enqueue_step(m, kv, xin, xout, cs);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(cs, &graph);
+    if (rc != LF_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(LF_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+    const hipError_t ei = hipGraphInstantiateWithFlags(&exec, graph, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return fail(LF_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(ei));
+    m->graphs.push_back({kv, xin, xout, exec});
+  }
+  LF_HIP(hipGraphLaunch(exec, st));
+  return LF_OK;
+}
+
+void drop_graphs(lf_model* m, lf_kv* kv) {
+  std::vector<GraphEntry> keep;
+  for (const GraphEntry& g : m->graphs) {
+    if (kv == nullptr || g.kv == kv)
+      (void)hipGraphExecDestroy(g.exec);
+    else
+      keep.push_back(g);
+  }
+  m->graphs.swap(keep);
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+
+extern "C" {
+
+const char* lf_last_error(void) { return g_err.c_str(); }
+
+size_t lf_workspace_bytes(const lf_config* cfg) {
+  if (validate(cfg) != LF_OK) return 0;
+  return ws_layout(*cfg).total;
+}
+
+size_t lf_kv_bytes(const lf_config* cfg) {
+  if (validate(cfg) != LF_OK) return 0;
+  return kv_layout(*cfg).total;
+}
+
+int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspace, size_t ws_bytes,
+                  void* stream, lf_model** out) {
+  if (!out) return fail(LF_EINVAL, "out is null");
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!w || !d_workspace) return fail(LF_EINVAL, "weights or workspace is null");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign) return fail(LF_EINVAL, "workspace not 256-byte aligned");
+  const Dims D = dims(*cfg);
+  const WsLayout W = ws_layout(*cfg);
+  if (ws_bytes < W.total) return fail(LF_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, W.total);
+  if (!w->attn_norm || !w->wqkv || !w->wo || !w->ffn_norm || !w->wgate_up || !w->wdown)
+    return fail(LF_EINVAL, "per-layer weight arrays must not be null");
+  for (int l = 0; l < D.L; ++l)
+    if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->wgate_up[l] || !w->wdown[l])
+      return fail(LF_EINVAL, "layer %d has a null weight pointer", l);
+  if (D.V && (!w->embed || !w->lm_head || !w->final_norm)) return fail(LF_EINVAL, "embed, lm_head and final_norm required when vocab > 0");
+  if ((rc = set_lds_limits())) return rc;
+
+  lf_model* m = new (std::nothrow) lf_model();
+  if (!m) return fail(LF_EINVAL, "out of host memory");
+  m->cfg = *cfg;
+  m->D = D;
+  m->W = W;
+  m->ws = static_cast<char*>(d_workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto bail = [&](int code) {
+    if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
+    delete m;
+    return code;
+  };
+  if (hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking) != hipSuccess)
+    return bail(fail(LF_EHIP, "capture stream: %s", hipGetErrorString(hipGetLastError())));
+  const size_t h = sizeof(half_t);
+
+  for (int l = 0; l < D.L; ++l) {
+    lf::RepackArgs r{};
+    r.K = D.d; r.hd = D.hd; r.n_q = D.hq; r.n_kv = D.hkv; r.qpl = D.qpl; r.kpl = D.kpl; r.ffn = D.ffn;
+    r.dst = m->at<half_t>(W.wqkv[l]);
+    r.src = static_cast<const half_t*>(w->wqkv[l]);
+    r.rows = D.qkv_rows;
+    r.mode = 0;
+    hipLaunchKernelGGL(lf::k_repack, dim3(r.rows), dim3(lf::kBlock), 0, st, r);
+    r.dst = m->at<half_t>(W.wgu[l]);
+    r.src = static_cast<const half_t*>(w->wgate_up[l]);
+    r.rows = 2 * D.ffn;
+    r.mode = 1;
+    hipLaunchKernelGGL(lf::k_repack, dim3(r.rows), dim3(lf::kBlock), 0, st, r);
+    if (hipMemcpyAsync(m->at<half_t>(W.wo[l]), w->wo[l], static_cast<size_t>(D.d) * D.qdim * h, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(m->at<half_t>(W.wd[l]), w->wdown[l], static_cast<size_t>(D.d) * D.ffn * h, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(m->at<half_t>(W.g1[l]), w->attn_norm[l], D.d * h, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(m->at<half_t>(W.g2[l]), w->ffn_norm[l], D.d * h, hipMemcpyDeviceToDevice, st))
+      return bail(fail(LF_EHIP, "weight copy failed: %s", hipGetErrorString(hipGetLastError())));
+  }
+  if (D.V) {
+    if (hipMemcpyAsync(m->at<half_t>(W.embed), w->embed, static_cast<size_t>(D.V) * D.d * h, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(m->at<half_t>(W.lm), w->lm_head, static_cast<size_t>(D.V) * D.d * h, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(m->at<half_t>(W.gf), w->final_norm, D.d * h, hipMemcpyDeviceToDevice, st))
+      return bail(fail(LF_EHIP, "embedding/head copy failed: %s", hipGetErrorString(hipGetLastError())));
+  }
+  // Rotary table: angle p * theta^(-2c/hd) evaluated in double, stored as fp32 (cos, sin).
+  std::vector<float2> rope(static_cast<size_t>(D.ctx) * (D.hd / 2));
+  for (int p = 0; p < D.ctx; ++p)
+    for (int c = 0; c < D.hd / 2; ++c) {
+      const double inv = std::pow(static_cast<double>(cfg->rope_theta), -2.0 * c / D.hd);
+      const double ang = p * inv;
+      rope[static_cast<size_t>(p) * (D.hd / 2) + c] = make_float2(static_cast<float>(std::cos(ang)), static_cast<float>(std::sin(ang)));
+    }
+  if (hipMemcpyAsync(m->at<float2>(W.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st))
+    return bail(fail(LF_EHIP, "rope upload failed: %s", hipGetErrorString(hipGetLastError())));
+  const int nctr = D.lanes + 4;
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, nctr);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
+  *out = m;
+  return LF_OK;
+}
+
+void lf_model_free(lf_model* m) {
+  if (!m) return;
+  drop_graphs(m, nullptr);
+  if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
+  delete m;
+}
+
+int lf_model_set_graph(lf_model* m, int enabled) {
+  if (!m) return fail(LF_EINVAL, "model is null");
+  m->use_graph = enabled != 0;
+  return LF_OK;
+}
+
+int lf_kv_alloc(lf_model* m, void* d_buf, size_t bytes, lf_kv** out) {
+  if (!m || !d_buf || !out) return fail(LF_EINVAL, "null argument");
+  *out = nullptr;
+  if (reinterpret_cast<uintptr_t>(d_buf) % kAlign) return fail(LF_EINVAL, "sequence buffer not 256-byte aligned");
+  const KvLayout K = kv_layout(m->cfg);
+  if (bytes < K.total) return fail(LF_EINVAL, "sequence buffer %zu bytes < %zu needed", bytes, K.total);
+  LF_HIP(hipMemset(static_cast<char*>(d_buf) + K.state, 0, K.tokens - K.state + (m->D.ctx + 1) * sizeof(int32_t)));
+  LF_HIP(hipDeviceSynchronize());
+  lf_kv* kv = new (std::nothrow) lf_kv();
+  if (!kv) return fail(LF_EINVAL, "out of host memory");
+  kv->m = m;
+  kv->buf = static_cast<char*>(d_buf);
+  kv->K = K;
+  kv->len = 0;
+  *out = kv;
+  return LF_OK;
+}
+
+void lf_kv_free(lf_kv* kv) {
+  if (!kv) return;
+  drop_graphs(kv->m, kv);
+  delete kv;
+}
+
+int lf_kv_cache_ptrs(const lf_kv* kv, void** d_k, void** d_v) {
+  if (!kv || !d_k || !d_v) return fail(LF_EINVAL, "null argument");
+  *d_k = kv->kc();
+  *d_v = kv->vc();
+  return LF_OK;
+}
+
+int32_t lf_kv_len(const lf_kv* kv) { return kv ? kv->len : -1; }
+
+int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream) {
+  if (!kv) return fail(LF_EINVAL, "kv is null");
+  if (len < 0 || len > kv->m->D.ctx) return fail(LF_ERANGE, "length %d out of [0, %d]", len, kv->m->D.ctx);
+  hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->state(), kv->tokens(), len,
+                     static_cast<const int32_t*>(nullptr));
+  LF_HIP(hipPeekAtLastError());
+  kv->len = len;
+  return LF_OK;
+}
+
+int lf_prefill(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, void* stream) {
+  if (!m || !kv || !d_tokens) return fail(LF_EINVAL, "null argument");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  if (m->D.V == 0) return fail(LF_EINVAL, "lf_prefill needs vocab > 0");
+  if (n < 1) return fail(LF_EINVAL, "n = %d < 1", n);
+  if (static_cast<long>(kv->len) + n > m->D.ctx) return fail(LF_ERANGE, "len %d + n %d > max_ctx %d", kv->len, n, m->D.ctx);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(lf::k_put_tokens, dim3((n + 255) / 256), dim3(256), 0, st, kv->state(), kv->tokens(), kv->len, d_tokens, n);
+  LF_HIP(hipPeekAtLastError());
+  for (int i = 0; i < n; ++i) {
+    const int rc = run_step(m, kv, nullptr, nullptr, st);
+    if (rc) return rc;
+    kv->len += 1;
+  }
+  return LF_OK;
+}
+
+int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream) {
+  if (!m || !kv) return fail(LF_EINVAL, "null argument");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  if (m->D.V == 0) return fail(LF_EINVAL, "lf_decode_step needs vocab > 0; use lf_decode_step_hidden");
+  if (kv->len >= m->D.ctx) return fail(LF_ERANGE, "sequence is full (%d positions)", m->D.ctx);
+  if (!d_token && kv->len == 0) return fail(LF_EINVAL, "no previous position to take a greedy token from");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d_token) {
+    hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, st, kv->state(), kv->tokens(), kv->len, d_token);
+    LF_HIP(hipPeekAtLastError());
+  }
+  const int rc = run_step(m, kv, nullptr, nullptr, st);
+  if (rc) return rc;
+  kv->len += 1;
+  return LF_OK;
+}
+
+int lf_decode_steps(lf_model* m, lf_kv* kv, int32_t n, void* stream) {
+  if (!m || !kv) return fail(LF_EINVAL, "null argument");
+  if (n < 0) return fail(LF_EINVAL, "n = %d < 0", n);
+  if (static_cast<long>(kv->len) + n > m->D.ctx) return fail(LF_ERANGE, "len %d + n %d > max_ctx %d", kv->len, n, m->D.ctx);
+  for (int i = 0; i < n; ++i) {
+    const int rc = lf_decode_step(m, kv, nullptr, stream);
+    if (rc) return rc;
+  }
+  return LF_OK;
+}
+
+int lf_decode_step_hidden(lf_model* m, lf_kv* kv, const float* d_x_in, float* d_x_out, void* stream) {
+  if (!m || !kv || !d_x_in || !d_x_out) return fail(LF_EINVAL, "null argument");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  if (m->D.V != 0) return fail(LF_EINVAL, "lf_decode_step_hidden needs vocab == 0");
+  if (kv->len >= m->D.ctx) return fail(LF_ERANGE, "sequence is full (%d positions)", m->D.ctx);
+  const int rc = run_step(m, kv, d_x_in, d_x_out, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  kv->len += 1;
+  return LF_OK;
+}
+
+int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_argmax, void* stream) {
+  if (!m || !kv || !d_logits) return fail(LF_EINVAL, "null argument");
+  if (m->D.V == 0) return fail(LF_EINVAL, "no logits when vocab == 0");
+  if (kv->len == 0) return fail(LF_EINVAL, "no position decoded yet");
+  const int n = m->D.V;
+  hipLaunchKernelGGL(lf::k_copy_out, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), d_logits,
+                     kv->logits(), n, d_argmax, kv->state());
+  LF_HIP(hipPeekAtLastError());
+  return LF_OK;
+}
+
+int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream) {
+  if (!kv || !out) return fail(LF_EINVAL, "null argument");
+  int32_t s[4];
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LF_HIP(hipMemcpyAsync(s, kv->state(), sizeof s, hipMemcpyDeviceToHost, st));
+  LF_HIP(hipStreamSynchronize(st));
+  out[0] = s[lf::kLen];
+  out[1] = s[lf::kArgmax];
+  out[2] = s[lf::kBadToken];
+  return LF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+/*
+ * lfdecode — batch-1 decode step of a Laneformer-2B-shaped decoder on MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * What one step computes (Kog Laneformer 2B blog, "Designing the
+ * architecture"): a pre-norm decoder transformer with causal grouped-query
+ * attention (query head i reads key/value head floor(i*Hkv/Hq)), heads spread
+ * evenly over lanes, sliding-window attention on some layers, a KV cache that
+ * every new token reads, and a greedy next token. The blog's "The idea" and
+ * "Designing the architecture" sections state that at batch 1 the step is
+ * bound by the bytes it streams from HBM: every weight once plus the visible
+ * cache. Inference is FP16 at batch 1 (asector.ru summary, "Performance and
+ * infrastructure"); the context is at most 4,096 tokens (same summary,
+ * "Operational risks").
+ *
+ * Numerics: fp16 weights and KV cache; fp32 accumulation, residual stream,
+ * softmax and logits.
+ *
+ * Memory ownership: the caller allocates every device buffer (weights,
+ * workspace, KV/sequence buffer, token and logits buffers) and keeps it alive
+ * while the library uses it. The library never allocates or frees device
+ * memory after lf_model_init returns, and never frees caller memory. Handles
+ * (lf_model, lf_kv) are small host objects owned by the library.
+ *
+ * Streams: every call that takes `stream` (a hipStream_t passed as void*)
+ * enqueues its device work on that stream and returns without waiting, except
+ * lf_model_init, which waits for its own setup work. Calls on one model must
+ * be serialised on one stream: all sequences of a model share its workspace.
+ *
+ * Errors: functions return 0 on success or a negative LF_E* code; no C++
+ * exception crosses the ABI. lf_last_error() returns a thread-local text for
+ * the last failure of the calling thread.
+ */
+#ifndef LFDECODE_H
+#define LFDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LF_OK 0
+#define LF_EINVAL (-1)   /* null pointer, invalid configuration, undersized buffer, wrong mode */
+#define LF_ERANGE (-2)   /* the sequence would pass max_ctx positions */
+#define LF_EHIP (-3)     /* a HIP runtime call failed; see lf_last_error() */
+
+#define LF_MAX_LAYERS 64
+
+/*
+ * Decoder shape. All sizes in elements.
+ *   n_q_heads % n_kv_heads == 0; n_q_heads, n_kv_heads and ffn divisible by n_lanes;
+ *   head_dim in {32, 64, 128}; (512 / head_dim) divisible by n_kv_heads / n_lanes;
+ *   d_model, ffn multiples of 8 and at most 16384; n_q_heads * head_dim at most 16384;
+ *   1 <= max_ctx <= 4096; 1 <= n_layers <= LF_MAX_LAYERS.
+ * vocab == 0 selects hidden-in / hidden-out mode: no embedding, no LM head,
+ * lf_decode_step_hidden is the step call.
+ * window[l] == 0: layer l is full causal; window[l] == W > 0: position p sees
+ * keys j with p - W < j <= p (the current key counts toward W).
+ * Rotary embedding: pairs (c, c + head_dim/2), angle p * rope_theta^(-2c/head_dim).
+ */
+typedef struct lf_config {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_lanes, max_ctx;
+  int32_t window[LF_MAX_LAYERS];
+  float rope_theta, rms_eps;
+} lf_config;
+
+/*
+ * Caller-owned device pointers to fp16 weights, matrices row-major [out, in].
+ * The per-layer members are HOST arrays of n_layers DEVICE pointers.
+ *   embed, lm_head  [vocab, d_model]   (unused when vocab == 0)
+ *   final_norm      [d_model]          (unused when vocab == 0)
+ *   attn_norm, ffn_norm [d_model] RMSNorm gains
+ *   wqkv     [(n_q_heads + 2 n_kv_heads) head_dim, d_model]: all q rows, then k rows, then v rows
+ *   wo       [d_model, n_q_heads head_dim]
+ *   wgate_up [2 ffn, d_model]: gate rows, then up rows
+ *   wdown    [d_model, ffn]
+ * lf_model_init copies (and repacks) everything it needs into the workspace;
+ * after it returns the caller may release these buffers.
+ */
+typedef struct lf_weight_ptrs {
+  const void* embed;
+  const void* lm_head;
+  const void* final_norm;
+  const void* const* attn_norm;
+  const void* const* wqkv;
+  const void* const* wo;
+  const void* const* ffn_norm;
+  const void* const* wgate_up;
+  const void* const* wdown;
+} lf_weight_ptrs;
+
+typedef struct lf_model lf_model;
+typedef struct lf_kv lf_kv;
+
+/* Bytes of device workspace a model of this shape needs (0 if the config is invalid). */
+size_t lf_workspace_bytes(const lf_config* cfg);
+
+/* Bytes of the per-sequence device buffer (state, token history, logits, K and V caches). */
+size_t lf_kv_bytes(const lf_config* cfg);
+
+/*
+ * Validate cfg, bind the caller's workspace (d_workspace, >= lf_workspace_bytes,
+ * 256-byte aligned), copy and repack the weights into it, build the rotary
+ * table, and wait for that setup on `stream`. *out receives the handle.
+ */
+int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspace, size_t ws_bytes,
+                  void* stream, lf_model** out);
+void lf_model_free(lf_model* m);
+
+/*
+ * Launch mode of the decode step: 1 (default) replays a hipGraph captured on
+ * first use per (sequence, in/out pointers); 0 launches the kernels one by one.
+ * Both run the same kernels with the same arguments.
+ */
+int lf_model_set_graph(lf_model* m, int enabled);
+
+/*
+ * Bind a caller buffer (>= lf_kv_bytes, 256-byte aligned) as one sequence with
+ * length 0. Layout of the caches, so a caller can fill them (K holds keys
+ * after the rotary embedding):
+ *   K[layer][lane][pos][kv_head_in_lane][head_dim] fp16, V likewise,
+ * kv head h lives in lane h / (n_kv_heads / n_lanes). lf_kv_cache_ptrs gives
+ * the two device addresses.
+ */
+int lf_kv_alloc(lf_model* m, void* d_buf, size_t bytes, lf_kv** out);
+void lf_kv_free(lf_kv* kv);
+int lf_kv_cache_ptrs(const lf_kv* kv, void** d_k, void** d_v);
+
+/*
+ * Set the sequence length to len (0 <= len <= max_ctx): rewinds, or adopts
+ * cache content the caller wrote for positions [0, len). Enqueued on stream.
+ */
+int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream);
+int32_t lf_kv_len(const lf_kv* kv);
+
+/*
+ * Append n positions whose token ids are d_tokens[0..n) (device int32, each in
+ * [0, vocab); ids outside are clamped and flagged, see lf_kv_status). Leaves
+ * the logits and greedy argmax of the last of them. LF_ERANGE if
+ * len + n > max_ctx. Token mode only (vocab > 0).
+ */
+int lf_prefill(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, void* stream);
+
+/*
+ * Append one position. d_token (device int32) gives its token id; NULL feeds
+ * the greedy argmax of the previous position, which stays on the device.
+ * Leaves the logits and argmax of the new position. LF_ERANGE if len == max_ctx.
+ */
+int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream);
+
+/* n chained greedy steps (lf_decode_step with d_token == NULL, n times). */
+int lf_decode_steps(lf_model* m, lf_kv* kv, int32_t n, void* stream);
+
+/*
+ * Hidden mode (vocab == 0): append one position whose input hidden vector is
+ * d_x_in (fp32 [d_model]) and write the last layer's output residual to
+ * d_x_out (fp32 [d_model]; may equal d_x_in).
+ */
+int lf_decode_step_hidden(lf_model* m, lf_kv* kv, const float* d_x_in, float* d_x_out, void* stream);
+
+/*
+ * Copy the logits of the most recent position (fp32 [vocab]) to d_logits and,
+ * if d_argmax is not NULL, its greedy token (lowest index among maximal
+ * logits) to d_argmax (device int32). Token mode only.
+ */
+int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_argmax, void* stream);
+
+/*
+ * Read back (synchronously on stream) the device-side sequence state:
+ * out[0] = length, out[1] = last argmax, out[2] = nonzero if a token id
+ * outside [0, vocab) was clamped since lf_kv_alloc.
+ */
+int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
+
+/* Text of the calling thread's last error ("" if none). */
+const char* lf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LFDECODE_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/lfdecode.h declares, and rejects invalid arguments before any
+HIP call. No compute runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_step_05_amd import lfdecode as C
+from synth import FULL, LANE, LAYER_FULL, TINY
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "lfdecode.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lf_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.load()
+    declared = header_functions()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in lfdecode.h but not exported"
+    assert sorted(C.EXPORTS) == declared
+
+
+def test_sizes_of_the_workloads():
+    # workspace = weights (+ small activations); sequence buffer = caches + state
+    for cfg in (TINY, LAYER_FULL, FULL, LANE):
+        c = C.make_config(cfg)
+        ws, kv = C.lf_workspace_bytes(c), C.lf_kv_bytes(c)
+        assert ws > 0 and kv > 0, C.lf_last_error()
+    c = C.make_config(FULL)
+    cache = 2 * 15 * 4096 * 16 * 128 * 2
+    assert cache <= C.lf_kv_bytes(c) < cache + 4096 * 4 + 32000 * 4 + 4096
+    weights = 2338451456 * 2
+    assert weights <= C.lf_workspace_bytes(c) < weights + 8 * 2 ** 20
+
+
+@pytest.mark.parametrize("field,value,msg", [
+    ("head_dim", 48, "head_dim"),
+    ("n_kv_heads", 5, "multiple of n_kv_heads"),
+    ("n_lanes", 3, "n_lanes"),
+    ("max_ctx", 4097, "max_ctx"),
+    ("max_ctx", 0, "max_ctx"),
+    ("d_model", 260, "d_model"),
+    ("ffn", 0, "ffn"),
+    ("n_layers", 0, "n_layers"),
+    ("vocab", -1, "vocab"),
+])
+def test_invalid_configs_rejected(field, value, msg):
+    c = C.make_config(TINY)
+    setattr(c, field, value)
+    assert C.lf_workspace_bytes(c) == 0
+    assert msg in C.lf_last_error()
+    assert C.lf_kv_bytes(c) == 0
+
+
+def test_group_and_lane_limits():
+    c = C.make_config(FULL)
+    c.n_kv_heads = 4          # 8 query heads per kv head
+    c.n_lanes = 4
+    assert C.lf_workspace_bytes(c) == 0 and "query heads per kv head" in C.lf_last_error()
+    c = C.make_config(FULL)
+    c.n_lanes = 1             # 16 kv heads in one lane: more than 512/128 = 4
+    assert C.lf_workspace_bytes(c) == 0 and "kv heads per lane" in C.lf_last_error()
+    c = C.make_config(TINY)
+    c.window[0] = -3
+    assert C.lf_workspace_bytes(c) == 0 and "window" in C.lf_last_error()
+
+
+def test_init_argument_errors_before_any_device_call():
+    lib = C.load()
+    c = C.make_config(TINY)
+    out = ctypes.c_void_p()
+    w = C.lf_weight_ptrs()
+    # null weights / workspace
+    assert lib.lf_model_init(ctypes.byref(c), None, None, 0, None, ctypes.byref(out)) == C.LF_EINVAL
+    # misaligned workspace
+    rc = lib.lf_model_init(ctypes.byref(c), ctypes.byref(w), 0x1001, 1 << 30, None, ctypes.byref(out))
+    assert rc == C.LF_EINVAL and "aligned" in C.lf_last_error()
+    # undersized workspace
+    rc = lib.lf_model_init(ctypes.byref(c), ctypes.byref(w), 0x10000, 16, None, ctypes.byref(out))
+    assert rc == C.LF_EINVAL and "workspace" in C.lf_last_error()
+    # null per-layer arrays
+    rc = lib.lf_model_init(ctypes.byref(c), ctypes.byref(w), 0x10000, 1 << 40, None, ctypes.byref(out))
+    assert rc == C.LF_EINVAL and "per-layer" in C.lf_last_error()
+    assert out.value is None
+
+
+def test_null_handles_rejected():
+    lib = C.load()
+    assert lib.lf_prefill(None, None, None, 1, None) == C.LF_EINVAL
+    assert lib.lf_decode_step(None, None, None, None) == C.LF_EINVAL
+    assert lib.lf_decode_step_hidden(None, None, None, None, None) == C.LF_EINVAL
+    assert lib.lf_logits(None, None, None, None, None) == C.LF_EINVAL
+    assert lib.lf_kv_set_len(None, 0, None) == C.LF_EINVAL
+    assert lib.lf_kv_alloc(None, None, 0, ctypes.byref(ctypes.c_void_p())) == C.LF_EINVAL
+    assert lib.lf_kv_len(None) == -1
+    lib.lf_model_free(None)
+    lib.lf_kv_free(None)
