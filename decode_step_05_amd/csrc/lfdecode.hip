@@ -174,6 +174,8 @@ struct lf_model {
   char* ws;
   bool use_graph = true;
   hipStream_t capture_stream = nullptr;  // graphs are recorded here, replayed on the caller's stream
+  std::vector<hipEvent_t> events;        // per-kernel brackets for lf_step_kernel_times
+  std::vector<lf_kv*> kvs;               // live sequences; detached when the model is freed
   std::vector<GraphEntry> graphs;
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -222,8 +224,26 @@ int set_lds_limits() {
   return LF_OK;
 }
 
+// Optional per-kernel event brackets around each launch of enqueue_step.
+struct StepTimer {
+  hipEvent_t* ev;   // 2 per kernel
+  int32_t* kinds;
+  int cap, n;
+  hipError_t err = hipSuccess;
+  void before(hipStream_t st) {
+    if (n < cap && err == hipSuccess) err = hipEventRecord(ev[2 * n], st);
+  }
+  void after(hipStream_t st, int kind) {
+    if (n < cap && err == hipSuccess) {
+      err = hipEventRecord(ev[2 * n + 1], st);
+      kinds[n] = kind;
+    }
+    ++n;
+  }
+};
+
 // Enqueue every kernel of one step. xin/xout: hidden mode input/output (null in token mode).
-int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
+int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st, StepTimer* tm = nullptr) {
   const Dims& D = m->D;
   const WsLayout& W = m->W;
   const lf_config& c = m->cfg;
@@ -263,7 +283,9 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.q = m->at<float>(W.q);
     a.kc = kv->kc() + l * layer_cache;
     a.vc = kv->vc() + l * layer_cache;
+    if (tm) tm->before(st);
     launch_gemv<lf::kEpiQKV>(a, st);
+    if (tm) tm->after(st, LF_KERNEL_QKV);
 
     // attention over the visible keys, split over key ranges, merged in-kernel
     const AttnPlan P = attn_plan(c, l);
@@ -283,7 +305,9 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     t.qpl = D.qpl;
     t.kpl = D.kpl;
     t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
+    if (tm) tm->before(st);
     launch_attn(t, D.hd, D.G, D.lanes, st);
+    if (tm) tm->after(st, LF_KERNEL_ATTN);
 
     // O projection + residual
     a = base;
@@ -294,7 +318,9 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.in_kind = lf::kInF32;
     a.x = m->at<float>(W.o);
     a.y = resid;
+    if (tm) tm->before(st);
     launch_gemv<lf::kEpiResid>(a, st);
+    if (tm) tm->after(st, LF_KERNEL_O);
 
     // RMSNorm + gate/up + SwiGLU
     a = base;
@@ -306,7 +332,9 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.x = resid;
     a.gain = m->at<half_t>(W.g2[l]);
     a.y = m->at<float>(W.act);
+    if (tm) tm->before(st);
     launch_gemv<lf::kEpiSwiGLU>(a, st);
+    if (tm) tm->after(st, LF_KERNEL_GATE_UP);
 
     // down projection + residual (the last layer ends the step in hidden mode)
     a = base;
@@ -318,7 +346,9 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.x = m->at<float>(W.act);
     a.y = resid;
     if (hidden && l == D.L - 1) a.counter = counters + D.lanes;
+    if (tm) tm->before(st);
     launch_gemv<lf::kEpiResid>(a, st);
+    if (tm) tm->after(st, LF_KERNEL_DOWN);
   }
   if (!hidden) {
     // final RMSNorm + LM head + greedy argmax; ends the step
@@ -333,9 +363,12 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.y = kv->logits();
     a.counter = counters + D.lanes;
     a.lm_part = m->at<float2>(W.lm_part);
+    if (tm) tm->before(st);
     launch_gemv<lf::kEpiLogits>(a, st);
+    if (tm) tm->after(st, LF_KERNEL_LM_HEAD);
   }
   LF_HIP(hipPeekAtLastError());
+  if (tm && tm->err != hipSuccess) return fail(LF_EHIP, "hipEventRecord: %s", hipGetErrorString(tm->err));
   return LF_OK;
 }
 
@@ -476,8 +509,12 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
 
 void lf_model_free(lf_model* m) {
   if (!m) return;
+  // Sequences may outlive their model (lf_kv_free may come later): detach
+  // them so that they never touch the freed model.
+  for (lf_kv* kv : m->kvs) kv->m = nullptr;
   drop_graphs(m, nullptr);
   if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
+  for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
   delete m;
 }
 
@@ -501,13 +538,21 @@ int lf_kv_alloc(lf_model* m, void* d_buf, size_t bytes, lf_kv** out) {
   kv->buf = static_cast<char*>(d_buf);
   kv->K = K;
   kv->len = 0;
+  m->kvs.push_back(kv);
   *out = kv;
   return LF_OK;
 }
 
 void lf_kv_free(lf_kv* kv) {
   if (!kv) return;
-  drop_graphs(kv->m, kv);
+  if (lf_model* m = kv->m) {
+    drop_graphs(m, kv);
+    for (size_t i = 0; i < m->kvs.size(); ++i)
+      if (m->kvs[i] == kv) {
+        m->kvs.erase(m->kvs.begin() + i);
+        break;
+      }
+  }
   delete kv;
 }
 
@@ -522,6 +567,7 @@ int32_t lf_kv_len(const lf_kv* kv) { return kv ? kv->len : -1; }
 
 int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream) {
   if (!kv) return fail(LF_EINVAL, "kv is null");
+  if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");
   if (len < 0 || len > kv->m->D.ctx) return fail(LF_ERANGE, "length %d out of [0, %d]", len, kv->m->D.ctx);
   hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->state(), kv->tokens(), len,
                      static_cast<const int32_t*>(nullptr));
@@ -588,6 +634,7 @@ int lf_decode_step_hidden(lf_model* m, lf_kv* kv, const float* d_x_in, float* d_
 
 int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_argmax, void* stream) {
   if (!m || !kv || !d_logits) return fail(LF_EINVAL, "null argument");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
   if (m->D.V == 0) return fail(LF_EINVAL, "no logits when vocab == 0");
   if (kv->len == 0) return fail(LF_EINVAL, "no position decoded yet");
   const int n = m->D.V;
@@ -599,6 +646,7 @@ int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_ar
 
 int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream) {
   if (!kv || !out) return fail(LF_EINVAL, "null argument");
+  if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");
   int32_t s[4];
   hipStream_t st = static_cast<hipStream_t>(stream);
   LF_HIP(hipMemcpyAsync(s, kv->state(), sizeof s, hipMemcpyDeviceToHost, st));
@@ -606,6 +654,36 @@ int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream) {
   out[0] = s[lf::kLen];
   out[1] = s[lf::kArgmax];
   out[2] = s[lf::kBadToken];
+  return LF_OK;
+}
+
+int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const float* d_x_in, float* d_x_out,
+                         float* ms, int32_t* kinds, int32_t cap, int32_t* n_out, void* stream) {
+  if (!m || !kv || !ms || !kinds || !n_out || cap < 1) return fail(LF_EINVAL, "null argument or cap < 1");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  const bool hidden = m->D.V == 0;
+  if (hidden && (!d_x_in || !d_x_out)) return fail(LF_EINVAL, "hidden mode needs d_x_in and d_x_out");
+  if (!hidden && !d_token && kv->len == 0) return fail(LF_EINVAL, "no previous position to take a greedy token from");
+  if (kv->len >= m->D.ctx) return fail(LF_ERANGE, "sequence is full (%d positions)", m->D.ctx);
+  const int nk = 5 * m->D.L + (hidden ? 0 : 1);
+  if (cap < nk) return fail(LF_EINVAL, "cap %d < %d kernels per step", cap, nk);
+  while (static_cast<int>(m->events.size()) < 2 * nk) {
+    hipEvent_t e;
+    LF_HIP(hipEventCreate(&e));
+    m->events.push_back(e);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d_token) {
+    hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, st, kv->state(), kv->tokens(), kv->len, d_token);
+    LF_HIP(hipPeekAtLastError());
+  }
+  StepTimer tm{m->events.data(), kinds, cap, 0};
+  const int rc = enqueue_step(m, kv, hidden ? d_x_in : nullptr, hidden ? d_x_out : nullptr, st, &tm);
+  if (rc) return rc;
+  kv->len += 1;
+  LF_HIP(hipStreamSynchronize(st));
+  for (int i = 0; i < tm.n; ++i) LF_HIP(hipEventElapsedTime(&ms[i], m->events[2 * i], m->events[2 * i + 1]));
+  *n_out = tm.n;
   return LF_OK;
 }
 

@@ -21,8 +21,10 @@ EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_prefill",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
-    "lf_last_error",
+    "lf_step_kernel_times", "lf_last_error",
 )
+
+KERNEL_KINDS = ("qkv", "attn", "o", "gate_up", "down", "lm_head")
 
 
 class lf_config(ctypes.Structure):
@@ -72,6 +74,8 @@ def load():
         "lf_decode_step_hidden": (c_int, [P, P, P, P, P]),
         "lf_logits": (c_int, [P, P, P, P, P]),
         "lf_kv_status": (c_int, [P, POINTER(c_int32), P]),
+        "lf_step_kernel_times": (c_int, [P, P, P, P, P, POINTER(c_float), POINTER(c_int32), c_int32,
+                                         POINTER(c_int32), P]),
         "lf_last_error": (c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -217,3 +221,13 @@ def lf_kv_status(kv, stream=None):
     out = (c_int32 * 3)()
     _check(load().lf_kv_status(kv, out, _stream(stream)))
     return int(out[0]), int(out[1]), int(out[2])
+
+
+def lf_step_kernel_times(model, kv, token=None, x_in=None, x_out=None, cap=512, stream=None):
+    """[(kind name, milliseconds)] of one step's kernels in launch order."""
+    ms = (c_float * cap)()
+    kinds = (c_int32 * cap)()
+    n = c_int32()
+    _check(load().lf_step_kernel_times(model, kv, _ptr(token), _ptr(x_in), _ptr(x_out), ms, kinds, cap,
+                                       ctypes.byref(n), _stream(stream)))
+    return [(KERNEL_KINDS[kinds[i]], float(ms[i])) for i in range(n.value)]

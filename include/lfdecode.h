@@ -107,6 +107,9 @@ size_t lf_kv_bytes(const lf_config* cfg);
  */
 int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspace, size_t ws_bytes,
                   void* stream, lf_model** out);
+/* Free the handle. Sequences of the model become unusable (calls on them
+ * fail with LF_EINVAL) but must still be released with lf_kv_free, in any
+ * order relative to this call. The caller's buffers stay the caller's. */
 void lf_model_free(lf_model* m);
 
 /*
@@ -173,6 +176,24 @@ int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_ar
  * outside [0, vocab) was clamped since lf_kv_alloc.
  */
 int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
+
+/*
+ * Profiling aid (not needed to decode): run one step exactly as lf_decode_step
+ * (token mode; d_token may be NULL) or lf_decode_step_hidden (hidden mode)
+ * would, but with the kernels launched one by one, each bracketed by two HIP
+ * events on `stream`; wait for it and write, in launch order, each kernel's
+ * elapsed milliseconds to ms[] and its kind (LF_KERNEL_*) to kinds[].
+ * cap must be at least 5 * n_layers (+ 1 in token mode); *n_out receives the
+ * kernel count. Appends one position like the step calls.
+ */
+#define LF_KERNEL_QKV 0      /* RMSNorm + QKV GEMV + rotary + KV append */
+#define LF_KERNEL_ATTN 1     /* split-KV GQA attention + merge */
+#define LF_KERNEL_O 2        /* O GEMV + residual */
+#define LF_KERNEL_GATE_UP 3  /* RMSNorm + gate/up GEMV + SwiGLU */
+#define LF_KERNEL_DOWN 4     /* down GEMV + residual */
+#define LF_KERNEL_LM_HEAD 5  /* RMSNorm + LM head + greedy argmax */
+int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const float* d_x_in, float* d_x_out,
+                         float* ms, int32_t* kinds, int32_t cap, int32_t* n_out, void* stream);
 
 /* Text of the calling thread's last error ("" if none). */
 const char* lf_last_error(void);

@@ -141,6 +141,26 @@ def test_first_position_and_context_limit():
     assert seq.status()[0] == 70
 
 
+def test_model_freed_before_sequence():
+    # regression: a sequence released after its model (as a garbage collector
+    # may order it) must not touch the freed model
+    import gc
+    from decode_step_05_amd import lfdecode as C
+    cfg = TINY
+    say("[parity] model freed before sequence")
+    dec = _dec(cfg, make_weights(cfg, seed=0))
+    seq = dec.sequence()
+    seq.prefill(np.array([1, 2, 3], dtype=np.int32))
+    _torch().cuda.synchronize()
+    dec.close()
+    with pytest.raises(C.LfError) as e:
+        seq.set_len(0)
+    assert e.value.code == C.LF_EINVAL
+    seq.close()
+    del e
+    gc.collect()
+
+
 def test_bad_token_is_clamped_and_flagged():
     cfg = TINY
     say("[parity] bad token")
