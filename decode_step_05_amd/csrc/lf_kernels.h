@@ -1,18 +1,96 @@
 // Kernels of one decode step (batch 1) for gfx950.
 //
-// Every projection is a GEMV y = W x with fp16 W (row-major [out, in], rows
-// streamed from HBM once per step with 16-byte non-temporal loads, one wave
-// per group of rows, wave-shuffle reductions) and an fp32 input vector that
-// each workgroup stages in LDS. The input stage can apply RMSNorm (the
-// workgroup reduces sum(x^2) itself, so no separate norm kernel exists), and
-// the epilogue fuses what follows the product: rotary embedding and the KV
-// append (QKV), SwiGLU (gate/up), the residual add (O, down) or the logits
-// and greedy argmax (LM head). Attention is split over key ranges; the last
-// workgroup of a lane to finish merges the partial softmax states.
+// Every projection is a GEMV y = W x with fp16 W (row-major [out, in]) read
+// once per step with 16-byte non-temporal loads. Each wave owns row groups
+// g, g + TW, g + 2 TW, ... (TW = all waves of the launch) and keeps the next
+// group's loads in flight while it reduces the current one, so HBM stays busy
+// through the reductions; the first two groups are issued before the
+// workgroup stages its input vector in LDS. The input stage can apply RMSNorm
+// (each workgroup reduces sum(x^2) itself: no separate norm kernel), and the
+// epilogue fuses what follows the product: rotary embedding and the KV append
+// (QKV), SwiGLU (gate/up), the residual add (O, down), or the logits and the
+// greedy argmax (LM head). Attention splits each kv head's visible keys over
+// workgroups; the last workgroup of a kv head merges the partial softmax
+// states.
+//
+// Data that another workgroup of the same launch reads is written with
+// device-scope stores and read with device-scope loads (they bypass the
+// per-XCD L2 without flushing it); a workgroup announces completion with one
+// atomic after its stores have been acknowledged. No L2 writeback fences.
 #pragma once
 #include "lf_device.h"
 
 namespace lf {
+
+// ------------------------------------------------- device-scope data access
+
+__device__ __forceinline__ void put_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_f32(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_f32x2(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 get_f32x2(const float2* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void put_f16(half_t* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned short*>(p), __builtin_bit_cast(unsigned short, static_cast<half_t>(v)),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's stores are acknowledged, then count the workgroup in.
+// Returns true in every thread of the last of `expected` workgroups.
+__device__ __forceinline__ bool arrive(unsigned* counter, unsigned expected, int* flag_lds) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = (prev == expected - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
+// ------------------------------------------------------------ reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// Sum within aligned groups of W lanes (W = 4, 8 or 16) using DPP lane moves.
+template <int W>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(W == 4 || W == 8 || W == 16, "DPP row reductions cover 4, 8 or 16 lanes");
+  v += dpp<0xB1>(v);                   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);                   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp<0x141>(v);   // row_half_mirror
+  if constexpr (W >= 16) v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+// Wave total, uniform across lanes.
+__device__ __forceinline__ float wave_total(float v) {
+  v = row_sum<16>(v);
+  const int i = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(i, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(i, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(i, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(i, 48)));
+}
+
+// Greedy key: larger logit wins, then the lower index; 0 is below every key.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+  unsigned u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(u) << 32) | static_cast<unsigned>(0x7fffffff - i);
+}
+__device__ __forceinline__ int argmax_index(unsigned long long key) {
+  return 0x7fffffff - static_cast<int>(key & 0xffffffffu);
+}
 
 // ------------------------------------------------------------------ GEMV
 
@@ -20,8 +98,8 @@ enum InKind : int { kInF32 = 0, kInNormF32 = 1, kInNormEmbed = 2 };
 enum Epi : int { kEpiQKV = 0, kEpiSwiGLU = 1, kEpiResid = 2, kEpiLogits = 3 };
 
 struct GemvArgs {
-  const half_t* W;        // [rows, K]
-  int rows, K, rows_per_block;
+  const half_t* W;        // [rows, K] (QKV and gate/up repacked so that epilogue pairs are adjacent rows)
+  int rows, K;
   // input vector
   int in_kind;
   const float* x;         // fp32 source (kInF32, kInNormF32)
@@ -41,225 +119,316 @@ struct GemvArgs {
   half_t* vc;             //          and V cache
   const float2* rope;     // (cos, sin) [max_ctx][hd / 2]
   int hd, qpl, kpl;
-  // finishing work of the last workgroup (kEpiLogits: argmax and step end; kEpiResid: step end)
-  unsigned* counter;      // null: no finishing work
-  float2* lm_part;        // per-workgroup (max, index) of the logits
+  // finishing work of the last workgroup (kEpiLogits: argmax + step end; kEpiResid: step end)
+  unsigned* counter;      // null: none
+  unsigned long long* best;  // kEpiLogits: packed greedy key
 };
 
-// Stage the input vector of length K in LDS (fp32), applying RMSNorm if asked.
-__device__ __forceinline__ void stage_input(const GemvArgs& a, float* xs, float* red) {
+// Input staging in two halves so that its loads can be issued before the
+// weight loads: the vector memory counter retires loads in issue order, so
+// waiting for the input must not also wait for the weights.
+template <int THREADS, int KMAX>
+struct Stage {
+  static constexpr int NV = (KMAX + THREADS * 8 - 1) / (THREADS * 8);  // 8-element pieces per thread
+  float v[NV][8];
+  u32x4 gn[NV];
+};
+
+// Issue the loads of the input vector (length K <= KMAX) and of the RMSNorm
+// gains. COH: read the source with device-scope loads (written in this launch).
+template <int THREADS, int KMAX, bool COH>
+__device__ __forceinline__ void stage_load(Stage<THREADS, KMAX>& st, const GemvArgs& a, int p) {
+  constexpr int NV = Stage<THREADS, KMAX>::NV;
   const int tid = threadIdx.x, K = a.K;
-  const int per = (K + gridDim.x - 1) / gridDim.x;
-  const int s0 = blockIdx.x * per, s1 = min(s0 + per, K);
-  float ss = 0.f;
+  const bool norm = a.in_kind != kInF32;
   if (a.in_kind == kInNormEmbed) {
-    const int p = a.state[kLen];
     int tok = a.tokens[p];
     if (tok < 0 || tok >= a.vocab) {
       tok = tok < 0 ? 0 : a.vocab - 1;
       if (tid == 0 && blockIdx.x == 0) a.state[kBadToken] = 1;
     }
     const half_t* row = a.emb + static_cast<size_t>(tok) * K;
-    for (int i = tid * 8; i < K; i += kBlock * 8) {
-      float f[8];
-      unpack8(ld16(row + i), f);
+    u32x4 e[NV];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xs[i + j] = f[j];
-        ss = fmaf(f[j], f[j], ss);
-        if (a.resid_copy && i + j >= s0 && i + j < s1) a.resid_copy[i + j] = f[j];
-      }
+    for (int j = 0; j < NV; ++j) {
+      const int i = min((tid + j * THREADS) * 8, K - 8);
+      e[j] = ld16(row + i);
+      st.gn[j] = ld16(a.gain + i);
     }
-  } else {
-    for (int i = tid * 4; i < K; i += kBlock * 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.x + i);
-      *reinterpret_cast<f32x4*>(xs + i) = v;
-      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-      if (a.resid_copy) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (i + j >= s0 && i + j < s1) a.resid_copy[i + j] = v[j];
-      }
-    }
+    for (int j = 0; j < NV; ++j) unpack8(e[j], st.v[j]);
+    return;
   }
-  if (a.in_kind != kInF32) {
-    const float tot = block_sum(ss, red);  // its barrier also publishes xs
-    const float r = 1.0f / sqrtf(tot / static_cast<float>(K) + a.eps);
-    for (int i = tid; i < K; i += kBlock) xs[i] = xs[i] * r * static_cast<float>(a.gain[i]);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = min((tid + j * THREADS) * 8, K - 8);
+    if (COH) {
+      const float2* src = reinterpret_cast<const float2*>(a.x + i);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float2 f = get_f32x2(src + t);
+        st.v[j][2 * t] = f.x;
+        st.v[j][2 * t + 1] = f.y;
+      }
+    } else {
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(a.x + i);
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(a.x + i + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        st.v[j][t] = f0[t];
+        st.v[j][4 + t] = f1[t];
+      }
+    }
+    if (norm) st.gn[j] = ld16(a.gain + i);
+  }
+}
+
+// Finish the stage: RMSNorm (sum of squares over the workgroup, then
+// x * rsqrt(mean + eps) * gain) if asked, the layer-0 residual copy, and the
+// LDS store. LDS layout: two planes, plane h holding elements 8q+4h .. 8q+4h+3
+// of every 8-element chunk q in the 16-byte word xs[h*K/8 + q]; a wave reading
+// chunks q = lane + 64c touches consecutive 16-byte words: one ds_read_b128
+// per plane, free of bank conflicts.
+template <int THREADS, int KMAX>
+__device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, const GemvArgs& a, f32x4* xs, float* red) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int NV = Stage<THREADS, KMAX>::NV;
+  const int tid = threadIdx.x, K = a.K;
+  const int per = (K + gridDim.x - 1) / gridDim.x;
+  const int s0 = blockIdx.x * per, s1 = min(s0 + per, K);
+  const bool norm = a.in_kind != kInF32;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = (tid + j * THREADS) * 8;
+    if (i >= K) break;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ss = fmaf(st.v[j][t], st.v[j][t], ss);
+    if (a.resid_copy)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (i + t >= s0 && i + t < s1) put_f32(a.resid_copy + i + t, st.v[j][t]);
+  }
+  float r = 1.f;
+  if (norm) {
+    ss = wave_total(ss);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += red[w];
+    r = 1.0f / sqrtf(tot / static_cast<float>(K) + a.eps);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int q = tid + j * THREADS;
+    if (q * 8 >= K) break;
+    float g[8];
+    if (norm) unpack8(st.gn[j], g);
+    f32x4 o0, o1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o0[t] = norm ? st.v[j][t] * r * g[t] : st.v[j][t];
+      o1[t] = norm ? st.v[j][4 + t] * r * g[4 + t] : st.v[j][4 + t];
+    }
+    xs[q] = o0;
+    xs[(K >> 3) + q] = o1;
   }
   __syncthreads();
 }
 
-// Dot products of NR consecutive rows (row stride K) with xs; rows at or past
-// `nvalid` are not read and give 0. Each lane covers 16-byte chunks
-// lane, lane+64, ...; U chunks per row are in flight at once.
-template <int NR, int U>
-__device__ __forceinline__ void rows_dot(const half_t* __restrict__ W, int K, int nvalid,
-                                         const float* __restrict__ xs, float (&out)[NR]) {
-  const int lane = threadIdx.x & (kWave - 1);
+template <int NR, int KCH>
+struct Rows {
+  u32x4 w[NR][KCH];
+  float res[NR];  // current residual values (residual epilogue)
+};
+
+// Issue the loads of rows [r, r+NR): lane covers 16-byte chunks lane + 64c.
+// res_src (residual epilogue): also load the residual values of those rows.
+template <int NR, int KCH>
+__device__ __forceinline__ void issue_rows(Rows<NR, KCH>& b, const half_t* __restrict__ W, int r, int rows, int K,
+                                           int lane, const float* res_src = nullptr) {
+  // Out-of-range rows and chunks load from a clamped, in-bounds address and are
+  // ignored where the values are used: no branches around the loads, so all
+  // of them stay in flight together.
   const int K8 = K >> 3;
-  float acc[NR];
+  if (res_src)
 #pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-  for (int c0 = lane; c0 < K8; c0 += kWave * U) {
-    u32x4 w[NR][U];
+    for (int i = 0; i < NR; ++i) b.res[i] = get_f32(res_src + min(r + i, rows - 1));
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + kWave * u;
+  for (int i = 0; i < NR; ++i) {
+    const half_t* row = W + static_cast<size_t>(min(r + i, rows - 1)) * K;
 #pragma unroll
-      for (int r = 0; r < NR; ++r)
-        w[r][u] = (c < K8 && r < nvalid) ? ld_stream(W + static_cast<size_t>(r) * K + static_cast<size_t>(c) * 8)
-                                         : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + kWave * u;
-      if (c < K8) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + c * 8);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + c * 8 + 4);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r] = dot8(w[r][u], x0, x1, acc[r]);
-      }
-    }
+    for (int c = 0; c < KCH; ++c) b.w[i][c] = ld_stream(row + static_cast<size_t>(min(lane + kWave * c, K8 - 1)) * 8);
   }
-#pragma unroll
-  for (int r = 0; r < NR; ++r) out[r] = wave_sum(acc[r]);
 }
 
-template <int EPI, int NR, int U>
-__global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
-  extern __shared__ float xs[];
-  __shared__ float red[kWavesPerBlock];
-  __shared__ float2 wbest[kWavesPerBlock];
-  __shared__ int flag;
-  static_assert(NR % 2 == 0, "rows are processed in pairs");
-
-  const int p = a.state[kLen];
-  if (p >= a.max_ctx) return;  // the host never launches a step on a full cache
-  stage_input(a, xs, red);
-
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int rb = blockIdx.x * a.rows_per_block;
-  const int re = min(rb + a.rows_per_block, a.rows);
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-
-  for (int r0 = rb + wave * NR; r0 < re; r0 += kWavesPerBlock * NR) {
-    const int nvalid = min(NR, re - r0);
-    float out[NR];
-    rows_dot<NR, U>(a.W + static_cast<size_t>(r0) * a.K, a.K, nvalid, xs, out);
-    if (lane != 0) continue;
-    if constexpr (EPI == kEpiQKV) {
-      const int half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl;
+// Reduce rows [r, r+NR) against xs and run the epilogue (lane 0 stores).
+// FULL: K is exactly 512*KCH, so every chunk of every lane is in range.
+template <int EPI, int NR, int KCH, bool FULL>
+__device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KCH>& b, const f32x4* xs, int r, int lane,
+                                            int p, float& bv, int& bi) {
+  const int K8 = a.K >> 3;
+  const f32x4* xs_hi = xs + K8;
+  float acc[NR][2];
 #pragma unroll
-      for (int k = 0; k < NR; k += 2) {
-        if (k >= nvalid) break;
-        const int r = r0 + k;
-        const int u = r / a.hd, c = (r % a.hd) >> 1;
-        const int ln = u / upl, j = u % upl;
-        float y0 = out[k], y1 = out[k + 1];
-        if (j < a.qpl + a.kpl) {  // rotary embedding on q and k
-          const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
-          const float t0 = y0 * cs.x - y1 * cs.y;
-          const float t1 = y0 * cs.y + y1 * cs.x;
-          y0 = t0;
-          y1 = t1;
-        }
-        if (j < a.qpl) {
-          float* qh = a.q + static_cast<size_t>(ln * a.qpl + j) * a.hd;
-          qh[c] = y0;
-          qh[c + half_hd] = y1;
-        } else {
-          const bool is_k = j < a.qpl + a.kpl;
-          const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
-          half_t* dst = (is_k ? a.kc : a.vc) +
-                        ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
-          dst[c] = static_cast<half_t>(y0);
-          dst[c + half_hd] = static_cast<half_t>(y1);
-        }
-      }
-    } else if constexpr (EPI == kEpiSwiGLU) {
+  for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = 0.f;
 #pragma unroll
-      for (int k = 0; k < NR; k += 2) {
-        if (k >= nvalid) break;
-        const float g = out[k], u = out[k + 1];
-        a.y[(r0 + k) >> 1] = g / (1.0f + expf(-g)) * u;
-      }
-    } else if constexpr (EPI == kEpiResid) {
+  for (int c = 0; c < KCH; ++c) {
+    const int ch = lane + kWave * c;
+    if (FULL || ch < K8) {
+      const f32x4 x0 = xs[ch];
+      const f32x4 x1 = xs_hi[ch];
 #pragma unroll
-      for (int k = 0; k < NR; ++k)
-        if (k < nvalid) a.y[r0 + k] += out[k];
-    } else {  // kEpiLogits
+      for (int i = 0; i < NR; ++i) {
+        const h8 h = __builtin_bit_cast(h8, b.w[i][c]);
+        // two independent chains (elements 0-3 and 4-7) keep the FMA pipe full
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        if (k < nvalid) {
-          a.y[r0 + k] = out[k];
-          if (better(out[k], r0 + k, bv, bi)) {
-            bv = out[k];
-            bi = r0 + k;
-          }
+        for (int t = 0; t < 4; ++t) {
+          acc[i][0] = fmaf(static_cast<float>(h[t]), x0[t], acc[i][0]);
+          acc[i][1] = fmaf(static_cast<float>(h[4 + t]), x1[t], acc[i][1]);
         }
       }
     }
   }
+  float out[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) out[i] = wave_total(acc[i][0] + acc[i][1]);
+  if (lane != 0) return;
+  if constexpr (EPI == kEpiQKV) {
+    static_assert(NR == 2, "QKV rows come in rotary pairs");
+    if (r >= a.rows) return;
+    const int half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl;
+    const int u = r / a.hd, c = (r % a.hd) >> 1;
+    const int ln = u / upl, j = u % upl;
+    float y0 = out[0], y1 = out[1];
+    if (j < a.qpl + a.kpl) {  // rotary embedding on q and k
+      const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
+      const float t0 = y0 * cs.x - y1 * cs.y;
+      const float t1 = y0 * cs.y + y1 * cs.x;
+      y0 = t0;
+      y1 = t1;
+    }
+    if (j < a.qpl) {
+      float* qh = a.q + static_cast<size_t>(ln * a.qpl + j) * a.hd;
+      put_f32(qh + c, y0);
+      put_f32(qh + c + half_hd, y1);
+    } else {
+      const bool is_k = j < a.qpl + a.kpl;
+      const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
+      half_t* dst = (is_k ? a.kc : a.vc) + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
+      put_f16(dst + c, y0);
+      put_f16(dst + c + half_hd, y1);
+    }
+  } else if constexpr (EPI == kEpiSwiGLU) {
+    static_assert(NR == 2, "gate/up rows come in pairs");
+    if (r >= a.rows) return;
+    const float g = out[0], up = out[1];
+    put_f32(a.y + (r >> 1), g / (1.0f + expf(-g)) * up);
+  } else if constexpr (EPI == kEpiResid) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (r + i < a.rows) put_f32(a.y + r + i, b.res[i] + out[i]);
+  } else {  // kEpiLogits
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (r + i < a.rows) {
+        put_f32(a.y + r + i, out[i]);
+        if (better(out[i], r + i, bv, bi)) {
+          bv = out[i];
+          bi = r + i;
+        }
+      }
+  }
+}
+
+// The GEMV work of one workgroup: wave gw of TW handles row groups gw + k*TW
+// for k < GPW (the launch covers the matrix: GPW * TW >= groups). The loop is
+// unrolled at compile time so that each group's loads are waited for exactly
+// (the next group's loads stay in flight while this one is reduced).
+// Must be called by every thread of the workgroup (the input stage has barriers).
+// Returns false (in every thread) if the sequence is full and nothing was done.
+template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH>
+__device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* red, int gw, int TW, int& p, float& bv,
+                                         int& bi) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ng = (a.rows + NR - 1) / NR;
+  const float* res = EPI == kEpiResid ? a.y : nullptr;
+  const bool full = a.K == KCH * kWave * 8;
+  constexpr int KMAX = KCH * kWave * 8;
+  Rows<NR, KCH> buf[2];
+  Stage<THREADS, KMAX> st;
+  // Issue order: input vector, then weights (loads retire in issue order).
+  // The embedding row needs the position first; that is one kernel per step.
+  const bool embed = a.in_kind == kInNormEmbed;
+  if (!embed) stage_load<THREADS, KMAX, COH>(st, a, 0);
+  issue_rows<NR, KCH>(buf[0], a.W, min(gw, ng - 1) * NR, a.rows, a.K, lane, res);
+  if (GPW > 1) issue_rows<NR, KCH>(buf[1], a.W, min(gw + TW, ng - 1) * NR, a.rows, a.K, lane, res);
+  p = a.state[kLen];
+  if (p >= a.max_ctx) return false;  // the host never launches a step on a full cache
+  if (embed) stage_load<THREADS, KMAX, COH>(st, a, p);
+  stage_store<THREADS, KMAX>(st, a, xs, red);
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) {
+    const int g = gw + k * TW;
+    if (g < ng) {
+      if (full)
+        finish_rows<EPI, NR, KCH, true>(a, buf[k & 1], xs, g * NR, lane, p, bv, bi);
+      else
+        finish_rows<EPI, NR, KCH, false>(a, buf[k & 1], xs, g * NR, lane, p, bv, bi);
+    }
+    if (k + 2 < GPW) issue_rows<NR, KCH>(buf[k & 1], a.W, min(gw + (k + 2) * TW, ng - 1) * NR, a.rows, a.K, lane, res);
+  }
+  return true;
+}
+
+template <int EPI, int NR, int KCH, int GPW, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void k_gemv(GemvArgs a) {
+  constexpr int THREADS = WAVES * kWave;
+  extern __shared__ f32x4 xs[];  // the input vector, 16-byte words (see stage_store)
+  __shared__ float red[WAVES];
+  __shared__ float2 wbest[WAVES];
+  __shared__ int flag;
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  int p;
+  if (!gemv_run<EPI, NR, KCH, GPW, THREADS, false>(a, xs, red, blockIdx.x * WAVES + wave, gridDim.x * WAVES, p, bv, bi))
+    return;
 
   if (a.counter == nullptr) return;
   if constexpr (EPI == kEpiLogits) {
     if (lane == 0) wbest[wave] = make_float2(bv, __int_as_float(bi));
     __syncthreads();
     if (threadIdx.x == 0) {
-      float v = wbest[0].x;
-      int i = __float_as_int(wbest[0].y);
-      for (int w = 1; w < kWavesPerBlock; ++w) {
+      for (int w = 1; w < WAVES; ++w) {
         const int wi = __float_as_int(wbest[w].y);
-        if (better(wbest[w].x, wi, v, i)) {
-          v = wbest[w].x;
-          i = wi;
+        if (better(wbest[w].x, wi, bv, bi)) {
+          bv = wbest[w].x;
+          bi = wi;
         }
       }
-      a.lm_part[blockIdx.x] = make_float2(v, __int_as_float(i));
+      if (bi != 0x7fffffff)
+        __hip_atomic_fetch_max(a.best, argmax_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!arrive_last(a.counter, gridDim.x, &flag)) return;
-    // Greedy choice over all workgroups' bests.
-    float v = -INFINITY;
-    int i = 0x7fffffff;
-    for (int b = threadIdx.x; b < static_cast<int>(gridDim.x); b += kBlock) {
-      const float2 e = a.lm_part[b];
-      const int ei = __float_as_int(e.y);
-      if (better(e.x, ei, v, i)) {
-        v = e.x;
-        i = ei;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o);
-      const int oi = __shfl_xor(i, o);
-      if (better(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-      }
-    }
-    if (lane == 0) wbest[wave] = make_float2(v, __int_as_float(i));
-    __syncthreads();
+    if (!arrive(a.counter, gridDim.x, &flag)) return;
     if (threadIdx.x == 0) {
-      for (int w = 1; w < kWavesPerBlock; ++w) {
-        const int wi = __float_as_int(wbest[w].y);
-        if (better(wbest[w].x, wi, v, i)) {
-          v = wbest[w].x;
-          i = wi;
-        }
-      }
-      if (i < 0 || i >= a.rows) i = 0;  // only if every logit is NaN
+      const unsigned long long key = __hip_atomic_load(a.best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int i = key ? argmax_index(key) : 0;  // key == 0 only if every logit is NaN
+      if (i < 0 || i >= a.rows) i = 0;
       a.state[kArgmax] = i;
       if (p + 1 >= a.state[kFedEnd]) a.tokens[p + 1] = i;
       a.state[kLen] = p + 1;
+      __hip_atomic_store(a.best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    reset_counter(a.counter);
   } else {
-    if (!arrive_last(a.counter, gridDim.x, &flag)) return;
-    if (threadIdx.x == 0) a.state[kLen] = p + 1;
-    reset_counter(a.counter);
+    if (!arrive(a.counter, gridDim.x, &flag)) return;
+    if (threadIdx.x == 0) {
+      a.state[kLen] = p + 1;
+      __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -273,46 +442,41 @@ struct AttnArgs {
   float2* part_ml;          // [Hq][S] (running max in log2 units, denominator)
   float* part_acc;          // [Hq][S][hd] unnormalised outputs
   float* o;                 // attention output [Hq * hd]
-  unsigned* counters;       // [lanes]
-  int max_ctx, window, S, chunk, qpl, kpl;
+  unsigned* counters;       // [Hkv]
+  int max_ctx, window, S, chunk, kpl;
   float scale_log2;         // log2(e) / sqrt(hd)
 };
 
-// Workgroup (split s, lane ln) reads the lane's key range
-// [lo + s*chunk, lo + (s+1)*chunk) of all its kv heads as one contiguous tile
-// (keys are lane-major: [pos][kv head in lane][hd]) and keeps an online
-// softmax per (row group, query head) in registers. HD/8 lanes hold one
-// 16-byte piece of a key row each; G query heads share each kv head.
+// Workgroup (split s, kv head h) reads keys [lo + s*chunk, lo + (s+1)*chunk)
+// of kv head h (lane h / kpl) for its G query heads. HD/8 lanes hold one
+// 16-byte piece of a key row; a wave load covers 512/HD keys; U loads of K and
+// of V per lane are in flight per iteration. Each row group keeps an online
+// softmax; the workgroup combines them in LDS and stores one partial state
+// per query head. The last workgroup of the kv head merges the S partials.
 template <int HD, int G, int U>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
-  constexpr int LPR = HD / 8;       // lanes per key row
-  constexpr int RPW = kWave / LPR;  // key rows per wave load
-  __shared__ float2 sm_ml[kWavesPerBlock][RPW][G];
-  __shared__ float sm_acc[kWavesPerBlock][RPW][G][HD];
+  constexpr int LPR = HD / 8;        // lanes per key row
+  constexpr int KPW = kWave / LPR;   // keys per wave load
+  __shared__ float2 sm_ml[kWavesPerBlock][KPW][G];
+  __shared__ float sm_acc[kWavesPerBlock][KPW][G][HD];
   __shared__ int flag;
 
-  const int s = blockIdx.x, ln = blockIdx.y;
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  const int ln = kvh / a.kpl, kvl = kvh % a.kpl;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int p = a.state[kLen];
   if (p >= a.max_ctx) return;
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const int k0 = lo + s * a.chunk;
-  const int k1 = min(k0 + a.chunk, p + 1);
-  const int nrows = k1 > k0 ? (k1 - k0) * a.kpl : 0;
+  const int nk = max(0, min(k0 + a.chunk, p + 1) - k0);
 
-  const int rin = lane / LPR, ch = lane % LPR, kvh = rin % a.kpl;
-  const int head0 = ln * a.qpl + kvh * G;
+  const int kin = lane / LPR, ch = lane % LPR;
   float qr[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float* qp = a.q + static_cast<size_t>(head0 + g) * HD + ch * 8;
-    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qp);
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qp + 4);
+    const float* qp = a.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qr[g][i] = q0[i] * a.scale_log2;
-      qr[g][4 + i] = q1[i] * a.scale_log2;
-    }
+    for (int i = 0; i < 8; ++i) qr[g][i] = qp[i] * a.scale_log2;
   }
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -323,18 +487,22 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
   }
 
-  const size_t base = (static_cast<size_t>(ln) * a.max_ctx + min(k0, a.max_ctx - 1)) * a.kpl * HD;
-  const half_t* Kb = a.kc + base + ch * 8;
-  const half_t* Vb = a.vc + base + ch * 8;
-  for (int b0 = wave; b0 * RPW < nrows; b0 += kWavesPerBlock * U) {
+  // key j of this kv head: ((ln * max_ctx + j) * kpl + kvl) * HD
+  const size_t key_stride = static_cast<size_t>(a.kpl) * HD;
+  const size_t base = ((static_cast<size_t>(ln) * a.max_ctx + min(k0, a.max_ctx - 1)) * a.kpl + kvl) * HD + ch * 8;
+  const half_t* Kb = a.kc + base;
+  const half_t* Vb = a.vc + base;
+  for (int b0 = wave; b0 * KPW < nk; b0 += kWavesPerBlock * U) {
     u32x4 kk[U], vv[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = (b0 + u * kWavesPerBlock) * RPW + rin;
-      ok[u] = t < nrows;
-      kk[u] = ok[u] ? ld_stream(Kb + static_cast<size_t>(t) * HD) : u32x4{0u, 0u, 0u, 0u};
-      vv[u] = ok[u] ? ld_stream(Vb + static_cast<size_t>(t) * HD) : u32x4{0u, 0u, 0u, 0u};
+      // keys past the range load the last key of the range and are masked below
+      const int t = (b0 + u * kWavesPerBlock) * KPW + kin;
+      ok[u] = t < nk;
+      const size_t off = static_cast<size_t>(min(t, nk - 1)) * key_stride;
+      kk[u] = ld_stream(Kb + off);
+      vv[u] = ld_stream(Vb + off);
     }
     float sc[U][G];
 #pragma unroll
@@ -346,7 +514,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) d = fmaf(qr[g][i], kf[i], d);
-        d = group_sum<LPR>(d);
+        d = row_sum<LPR>(d);
         sc[u][g] = ok[u] ? d : -INFINITY;
       }
     }
@@ -373,53 +541,61 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     }
   }
 
-  // Combine the row groups of all waves that served the same kv head.
+  // Combine the row groups of all waves.
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm_acc[wave][rin][g][ch * 8 + i] = acc[g][i];
-    if (ch == 0) sm_ml[wave][rin][g] = make_float2(m[g], l[g]);
+    for (int i = 0; i < 8; ++i) sm_acc[wave][kin][g][ch * 8 + i] = acc[g][i];
+    if (ch == 0) sm_ml[wave][kin][g] = make_float2(m[g], l[g]);
   }
   __syncthreads();
-  for (int idx = tid; idx < a.kpl * G * HD; idx += kBlock) {
-    const int d = idx % HD, g = (idx / HD) % G, kh = idx / (HD * G);
+  for (int idx = tid; idx < G * HD; idx += kBlock) {
+    const int d = idx % HD, g = idx / HD;
     float M = -INFINITY;
+#pragma unroll
     for (int w = 0; w < kWavesPerBlock; ++w)
-      for (int r = kh; r < RPW; r += a.kpl) M = fmaxf(M, sm_ml[w][r][g].x);
+#pragma unroll
+      for (int r = 0; r < KPW; ++r) M = fmaxf(M, sm_ml[w][r][g].x);
     float L = 0.f, A = 0.f;
     if (M != -INFINITY) {
+#pragma unroll
       for (int w = 0; w < kWavesPerBlock; ++w)
-        for (int r = kh; r < RPW; r += a.kpl) {
+#pragma unroll
+        for (int r = 0; r < KPW; ++r) {
           const float2 ml = sm_ml[w][r][g];
           const float f = exp2f(ml.x - M);
           L = fmaf(ml.y, f, L);
           A = fmaf(sm_acc[w][r][g][d], f, A);
         }
     }
-    const int head = ln * a.qpl + kh * G + g;
-    a.part_acc[(static_cast<size_t>(head) * a.S + s) * HD + d] = A;
-    if (d == 0) a.part_ml[head * a.S + s] = make_float2(M, L);
+    const int head = kvh * G + g;
+    put_f32(a.part_acc + (static_cast<size_t>(head) * a.S + s) * HD + d, A);
+    if (d == 0) put_f32x2(a.part_ml + head * a.S + s, make_float2(M, L));
   }
 
-  // The last workgroup of this lane merges the splits.
-  if (!arrive_last(&a.counters[ln], a.S, &flag)) return;
+  // The last workgroup of this kv head merges its splits.
+  if (!arrive(&a.counters[kvh], a.S, &flag)) return;
   const int n = p + 1 - lo;
   const int n_active = min(a.S, (n + a.chunk - 1) / a.chunk);
-  for (int idx = tid; idx < a.qpl * HD; idx += kBlock) {
-    const int d = idx % HD, head = ln * a.qpl + idx / HD;
+  for (int idx = tid; idx < G * HD; idx += kBlock) {
+    const int d = idx % HD, head = kvh * G + idx / HD;
     const float2* ml = a.part_ml + head * a.S;
     const float* pa = a.part_acc + static_cast<size_t>(head) * a.S * HD + d;
-    float M = -INFINITY;
-    for (int t = 0; t < n_active; ++t) M = fmaxf(M, ml[t].x);
-    float L = 0.f, A = 0.f;
+    float M = -INFINITY, L = 0.f, A = 0.f;
+#pragma unroll 8
     for (int t = 0; t < n_active; ++t) {
-      const float f = exp2f(ml[t].x - M);
-      L = fmaf(ml[t].y, f, L);
-      A = fmaf(pa[static_cast<size_t>(t) * HD], f, A);
+      const float2 e = get_f32x2(ml + t);
+      const float v = get_f32(pa + static_cast<size_t>(t) * HD);
+      if (e.x == -INFINITY) continue;
+      const float Mn = fmaxf(M, e.x);
+      const float fo = exp2f(M - Mn), fn = exp2f(e.x - Mn);
+      L = L * fo + e.y * fn;
+      A = A * fo + v * fn;
+      M = Mn;
     }
-    a.o[static_cast<size_t>(head) * HD + d] = A / L;
+    put_f32(a.o + static_cast<size_t>(head) * HD + d, A / L);
   }
-  reset_counter(&a.counters[ln]);
+  if (tid == 0) __hip_atomic_store(&a.counters[kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------- utilities
@@ -427,7 +603,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 // Weight repack. Mode 0 (QKV): packed unit u (lane-major: per lane, its q
 // heads, then k heads, then v heads) holds rows (dim c, dim c + hd/2) at
 // packed rows (2c, 2c+1), so a rotary pair lands in one wave. Mode 1
-// (gate/up): packed row 2j = gate j, 2j+1 = up j. Mode 2: identity.
+// (gate/up): packed row 2j = gate j, 2j+1 = up j.
 struct RepackArgs {
   half_t* dst;
   const half_t* src;
@@ -437,7 +613,6 @@ struct RepackArgs {
 
 __device__ __forceinline__ int repack_src_row(const RepackArgs& a, int r) {
   if (a.mode == 1) return (r & 1) ? a.ffn + (r >> 1) : (r >> 1);
-  if (a.mode == 2) return r;
   const int u = r / a.hd, i = r % a.hd;
   const int dim = (i & 1) ? (a.hd >> 1) + (i >> 1) : (i >> 1);
   const int upl = a.qpl + 2 * a.kpl;

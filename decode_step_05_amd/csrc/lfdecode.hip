@@ -44,28 +44,44 @@ struct AttnPlan {
 
 AttnPlan attn_plan(const lf_config& c, int layer) {
   const int visible = c.window[layer] > 0 ? std::min(c.window[layer], c.max_ctx) : c.max_ctx;
-  int S = std::max(1, 256 / c.n_lanes);
-  S = std::min(S, 64);
+  int S = std::max(1, 256 / c.n_kv_heads);  // about one workgroup per CU over all kv heads
+  S = std::min(S, 32);
   S = std::min(S, visible);
   const int chunk = (visible + S - 1) / S;
   S = (visible + chunk - 1) / chunk;
   return {S, chunk};
 }
 
-// Rows per workgroup of a GEMV with `rows` outputs: a multiple of 8 (4 waves x
-// a row pair) chosen so that about 1024 workgroups cover the matrix.
-int rows_per_block(int rows) {
-  const int target_blocks = 1024;
-  int rpb = (rows + target_blocks - 1) / target_blocks;
-  rpb = (rpb + 7) / 8 * 8;
-  return std::max(rpb, 8);
+// Launch shape of a GEMV: (waves per workgroup, row groups per wave). Each
+// candidate is a compiled variant; the first that gives a balanced grid of at
+// least 256 workgroups (one per CU) wins, else the one with the most
+// workgroups. Chosen from measurements of the decode shapes on MI355X.
+struct GemvShape {
+  int waves, gpw, blocks;
+};
+
+GemvShape gemv_shape(int epi, int rows) {
+  static const int qkv[][2] = {{8, 2}, {8, 1}}, glu[][2] = {{4, 7}, {8, 2}, {8, 1}},
+                   res[][2] = {{8, 2}, {8, 1}}, lgt[][2] = {{8, 8}, {8, 2}, {8, 1}};
+  const int(*cand)[2] = epi == lf::kEpiQKV ? qkv : epi == lf::kEpiSwiGLU ? glu : epi == lf::kEpiResid ? res : lgt;
+  const int n = epi == lf::kEpiQKV ? 2 : epi == lf::kEpiSwiGLU ? 3 : epi == lf::kEpiResid ? 2 : 3;
+  const int nr = (epi == lf::kEpiQKV || epi == lf::kEpiSwiGLU) ? 2 : 1;
+  const int ng = (rows + nr - 1) / nr;
+  GemvShape best{0, 0, 0};
+  for (int i = 0; i < n; ++i) {
+    const int w = cand[i][0], g = cand[i][1];
+    const int b = (ng + w * g - 1) / (w * g);
+    if (b >= 256 && (b % 256 == 0 || b > 480)) return {w, g, b};
+    if (b > best.blocks) best = {w, g, b};
+  }
+  return best;
 }
 
 int validate(const lf_config* c) {
   if (!c) return fail(LF_EINVAL, "config is null");
   if (c->n_layers < 1 || c->n_layers > LF_MAX_LAYERS) return fail(LF_EINVAL, "n_layers %d out of [1, %d]", c->n_layers, LF_MAX_LAYERS);
-  if (c->d_model < 8 || c->d_model % 8 || c->d_model > 16384) return fail(LF_EINVAL, "d_model %d: need a multiple of 8 in [8, 16384]", c->d_model);
-  if (c->ffn < 8 || c->ffn % 8 || c->ffn > 16384) return fail(LF_EINVAL, "ffn %d: need a multiple of 8 in [8, 16384]", c->ffn);
+  if (c->d_model < 8 || c->d_model % 8 || c->d_model > 8192) return fail(LF_EINVAL, "d_model %d: need a multiple of 8 in [8, 8192]", c->d_model);
+  if (c->ffn < 8 || c->ffn % 8 || c->ffn > 8192) return fail(LF_EINVAL, "ffn %d: need a multiple of 8 in [8, 8192]", c->ffn);
   if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return fail(LF_EINVAL, "head_dim %d: need 32, 64 or 128", c->head_dim);
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads) return fail(LF_EINVAL, "n_q_heads %d must be a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
   const int G = c->n_q_heads / c->n_kv_heads;
@@ -74,7 +90,7 @@ int validate(const lf_config* c) {
     return fail(LF_EINVAL, "n_lanes %d must divide n_q_heads, n_kv_heads and ffn", c->n_lanes);
   const int kpl = c->n_kv_heads / c->n_lanes;
   if ((512 / c->head_dim) % kpl) return fail(LF_EINVAL, "kv heads per lane %d must divide %d", kpl, 512 / c->head_dim);
-  if (static_cast<long>(c->n_q_heads) * c->head_dim > 16384) return fail(LF_EINVAL, "n_q_heads * head_dim exceeds 16384");
+  if (static_cast<long>(c->n_q_heads) * c->head_dim > 8192) return fail(LF_EINVAL, "n_q_heads * head_dim exceeds 8192");
   if (c->vocab < 0) return fail(LF_EINVAL, "vocab %d < 0", c->vocab);
   if (c->max_ctx < 1 || c->max_ctx > 4096) return fail(LF_EINVAL, "max_ctx %d out of [1, 4096]", c->max_ctx);
   for (int l = 0; l < c->n_layers; ++l)
@@ -99,8 +115,8 @@ Dims dims(const lf_config& c) {
 // Byte offsets of everything in the model workspace.
 struct WsLayout {
   std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
-  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, lm_part, counters, total;
-  int S_max, lm_blocks;
+  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, total;
+  int S_max;
 };
 
 WsLayout ws_layout(const lf_config& c) {
@@ -131,9 +147,8 @@ WsLayout ws_layout(const lf_config& c) {
   for (int l = 0; l < D.L; ++l) W.S_max = std::max(W.S_max, attn_plan(c, l).S);
   W.part_ml = take(static_cast<size_t>(D.hq) * W.S_max * sizeof(float2));
   W.part_acc = take(static_cast<size_t>(D.hq) * W.S_max * D.hd * sizeof(float));
-  W.lm_blocks = D.V ? (D.V + rows_per_block(D.V) - 1) / rows_per_block(D.V) : 1;
-  W.lm_part = take(static_cast<size_t>(W.lm_blocks) * sizeof(float2));
-  W.counters = take((D.lanes + 4) * sizeof(unsigned));
+  W.best = take(sizeof(unsigned long long));
+  W.counters = take((D.hkv + 4) * sizeof(unsigned));
   W.total = off;
   return W;
 }
@@ -195,20 +210,66 @@ struct lf_kv {
 
 namespace {
 
+template <int EPI> constexpr int gemv_nr() { return (EPI == lf::kEpiQKV || EPI == lf::kEpiSwiGLU) ? 2 : 1; }
+
+// 16-byte chunks per lane per row: the smallest instantiated count covering K.
+int gemv_kch(int K) {
+  const int need = ((K >> 3) + lf::kWave - 1) / lf::kWave;
+  for (int k : {1, 2, 4, 8, 14, 16})
+    if (need <= k) return k;
+  return 0;
+}
+
+template <int EPI, int KCH, int GPW, int WAVES>
+const void* gemv_fn() {
+  return reinterpret_cast<const void*>(&lf::k_gemv<EPI, gemv_nr<EPI>(), KCH, GPW, WAVES>);
+}
+
+template <int EPI, int KCH>
+const void* gemv_fn_k(int waves, int gpw) {
+  if (waves == 4 && gpw == 7) return gemv_fn<EPI, KCH, 7, 4>();
+  if (waves == 8 && gpw == 8) return gemv_fn<EPI, KCH, 8, 8>();
+  if (waves == 8 && gpw == 2) return gemv_fn<EPI, KCH, 2, 8>();
+  return gemv_fn<EPI, KCH, 1, 8>();
+}
+
+template <int EPI>
+const void* gemv_kernel(int K, int waves, int gpw) {
+  switch (gemv_kch(K)) {
+    case 1: return gemv_fn_k<EPI, 1>(waves, gpw);
+    case 2: return gemv_fn_k<EPI, 2>(waves, gpw);
+    case 4: return gemv_fn_k<EPI, 4>(waves, gpw);
+    case 8: return gemv_fn_k<EPI, 8>(waves, gpw);
+    case 14: return gemv_fn_k<EPI, 14>(waves, gpw);
+    default: return gemv_fn_k<EPI, 16>(waves, gpw);
+  }
+}
+
 template <int EPI>
 void launch_gemv(const lf::GemvArgs& a, hipStream_t st) {
-  const int nblk = (a.rows + a.rows_per_block - 1) / a.rows_per_block;
-  const size_t lds = static_cast<size_t>(a.K) * sizeof(float);
-  hipLaunchKernelGGL((lf::k_gemv<EPI, 2, 8>), dim3(nblk), dim3(lf::kBlock), lds, st, a);
+  const GemvShape sh = gemv_shape(EPI, a.rows);
+  const void* fn = gemv_kernel<EPI>(a.K, sh.waves, sh.gpw);
+  void* args[] = {const_cast<lf::GemvArgs*>(&a)};
+  (void)hipLaunchKernel(fn, dim3(sh.blocks), dim3(sh.waves * lf::kWave), args, static_cast<size_t>(a.K) * sizeof(float),
+                        st);
+}
+
+template <int EPI>
+int set_lds_limit_epi() {
+  const int bytes = 8192 * sizeof(float);
+  for (int K : {512, 1024, 2048, 4096, 7168, 8192})
+    for (const int* wg : {(const int[]){4, 7}, (const int[]){8, 8}, (const int[]){8, 2}, (const int[]){8, 1}})
+      LF_HIP(hipFuncSetAttribute(gemv_kernel<EPI>(K, wg[0], wg[1]), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  return LF_OK;
 }
 
 template <int HD, int G>
-void launch_attn_t(const lf::AttnArgs& a, int lanes, hipStream_t st) {
-  hipLaunchKernelGGL((lf::k_attn<HD, G, 4>), dim3(a.S, lanes), dim3(lf::kBlock), 0, st, a);
+void launch_attn_t(const lf::AttnArgs& a, int n_kv, hipStream_t st) {
+  hipLaunchKernelGGL((lf::k_attn<HD, G, 8>), dim3(a.S, n_kv), dim3(lf::kBlock), 0, st, a);
 }
 
-void launch_attn(const lf::AttnArgs& a, int hd, int G, int lanes, hipStream_t st) {
-#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, lanes, st);
+void launch_attn(const lf::AttnArgs& a, int hd, int G, int n_kv, hipStream_t st) {
+#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, n_kv, st);
   LF_ATTN_CASE(32, 1) LF_ATTN_CASE(32, 2) LF_ATTN_CASE(32, 4)
   LF_ATTN_CASE(64, 1) LF_ATTN_CASE(64, 2) LF_ATTN_CASE(64, 4)
   LF_ATTN_CASE(128, 1) LF_ATTN_CASE(128, 2) LF_ATTN_CASE(128, 4)
@@ -216,11 +277,10 @@ void launch_attn(const lf::AttnArgs& a, int hd, int G, int lanes, hipStream_t st
 }
 
 int set_lds_limits() {
-  const int bytes = 16384 * sizeof(float);
-  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiQKV, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
-  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiSwiGLU, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
-  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiResid, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
-  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_gemv<lf::kEpiLogits, 2, 8>), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  int rc;
+  if ((rc = set_lds_limit_epi<lf::kEpiQKV>()) || (rc = set_lds_limit_epi<lf::kEpiSwiGLU>()) ||
+      (rc = set_lds_limit_epi<lf::kEpiResid>()) || (rc = set_lds_limit_epi<lf::kEpiLogits>()))
+    return rc;
   return LF_OK;
 }
 
@@ -269,7 +329,6 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.W = m->at<half_t>(W.wqkv[l]);
     a.rows = D.qkv_rows;
     a.K = D.d;
-    a.rows_per_block = rows_per_block(a.rows);
     a.gain = m->at<half_t>(W.g1[l]);
     if (l == 0) {
       a.in_kind = hidden ? lf::kInNormF32 : lf::kInNormEmbed;
@@ -302,11 +361,10 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     t.window = c.window[l];
     t.S = P.S;
     t.chunk = P.chunk;
-    t.qpl = D.qpl;
     t.kpl = D.kpl;
     t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
     if (tm) tm->before(st);
-    launch_attn(t, D.hd, D.G, D.lanes, st);
+    launch_attn(t, D.hd, D.G, D.hkv, st);
     if (tm) tm->after(st, LF_KERNEL_ATTN);
 
     // O projection + residual
@@ -314,7 +372,6 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.W = m->at<half_t>(W.wo[l]);
     a.rows = D.d;
     a.K = D.qdim;
-    a.rows_per_block = rows_per_block(a.rows);
     a.in_kind = lf::kInF32;
     a.x = m->at<float>(W.o);
     a.y = resid;
@@ -327,7 +384,6 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.W = m->at<half_t>(W.wgu[l]);
     a.rows = 2 * D.ffn;
     a.K = D.d;
-    a.rows_per_block = rows_per_block(a.rows);
     a.in_kind = lf::kInNormF32;
     a.x = resid;
     a.gain = m->at<half_t>(W.g2[l]);
@@ -341,11 +397,10 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.W = m->at<half_t>(W.wd[l]);
     a.rows = D.d;
     a.K = D.ffn;
-    a.rows_per_block = rows_per_block(a.rows);
     a.in_kind = lf::kInF32;
     a.x = m->at<float>(W.act);
     a.y = resid;
-    if (hidden && l == D.L - 1) a.counter = counters + D.lanes;
+    if (hidden && l == D.L - 1) a.counter = counters + D.hkv;
     if (tm) tm->before(st);
     launch_gemv<lf::kEpiResid>(a, st);
     if (tm) tm->after(st, LF_KERNEL_DOWN);
@@ -356,13 +411,12 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.W = m->at<half_t>(W.lm);
     a.rows = D.V;
     a.K = D.d;
-    a.rows_per_block = rows_per_block(a.rows);
     a.in_kind = lf::kInNormF32;
     a.x = resid;
     a.gain = m->at<half_t>(W.gf);
     a.y = kv->logits();
-    a.counter = counters + D.lanes;
-    a.lm_part = m->at<float2>(W.lm_part);
+    a.counter = counters + D.hkv;
+    a.best = m->at<unsigned long long>(W.best);
     if (tm) tm->before(st);
     launch_gemv<lf::kEpiLogits>(a, st);
     if (tm) tm->after(st, LF_KERNEL_LM_HEAD);
@@ -498,8 +552,9 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
     }
   if (hipMemcpyAsync(m->at<float2>(W.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st))
     return bail(fail(LF_EHIP, "rope upload failed: %s", hipGetErrorString(hipGetLastError())));
-  const int nctr = D.lanes + 4;
+  const int nctr = D.hkv + 4;
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, nctr);
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.best), 0u, 2);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
