@@ -464,20 +464,28 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
   const int s = blockIdx.x, kvh = blockIdx.y;
   const int ln = kvh / a.kpl, kvl = kvh % a.kpl;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int kin = lane / LPR, ch = lane % LPR;
+  // the queries do not depend on the position: load them first
+  f32x4 qv[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const f32x4* qp = reinterpret_cast<const f32x4*>(a.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8);
+    qv[g][0] = qp[0];
+    qv[g][1] = qp[1];
+  }
   const int p = a.state[kLen];
   if (p >= a.max_ctx) return;
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const int k0 = lo + s * a.chunk;
   const int nk = max(0, min(k0 + a.chunk, p + 1) - k0);
-
-  const int kin = lane / LPR, ch = lane % LPR;
   float qr[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float* qp = a.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8;
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qr[g][i] = qp[i] * a.scale_log2;
-  }
+    for (int i = 0; i < 4; ++i) {
+      qr[g][i] = qv[g][0][i] * a.scale_log2;
+      qr[g][4 + i] = qv[g][1][i] * a.scale_log2;
+    }
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -573,25 +581,35 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     if (d == 0) put_f32x2(a.part_ml + head * a.S + s, make_float2(M, L));
   }
 
-  // The last workgroup of this kv head merges its splits.
+  // The last workgroup of this kv head merges its splits, loading the
+  // partial states 16 splits at a time (one memory round trip per batch).
   if (!arrive(&a.counters[kvh], a.S, &flag)) return;
   const int n = p + 1 - lo;
   const int n_active = min(a.S, (n + a.chunk - 1) / a.chunk);
+  constexpr int MB = 16;
   for (int idx = tid; idx < G * HD; idx += kBlock) {
     const int d = idx % HD, head = kvh * G + idx / HD;
     const float2* ml = a.part_ml + head * a.S;
     const float* pa = a.part_acc + static_cast<size_t>(head) * a.S * HD + d;
     float M = -INFINITY, L = 0.f, A = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < n_active; ++t) {
-      const float2 e = get_f32x2(ml + t);
-      const float v = get_f32(pa + static_cast<size_t>(t) * HD);
-      if (e.x == -INFINITY) continue;
-      const float Mn = fmaxf(M, e.x);
-      const float fo = exp2f(M - Mn), fn = exp2f(e.x - Mn);
-      L = L * fo + e.y * fn;
-      A = A * fo + v * fn;
-      M = Mn;
+    for (int t0 = 0; t0 < n_active; t0 += MB) {
+      float2 e[MB];
+      float v[MB];
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const int t = min(t0 + u, n_active - 1);
+        e[u] = get_f32x2(ml + t);
+        v[u] = get_f32(pa + static_cast<size_t>(t) * HD);
+      }
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        if (t0 + u >= n_active || e[u].x == -INFINITY) continue;
+        const float Mn = fmaxf(M, e[u].x);
+        const float fo = exp2f(M - Mn), fn = exp2f(e[u].x - Mn);
+        L = L * fo + e[u].y * fn;
+        A = A * fo + v[u] * fn;
+        M = Mn;
+      }
     }
     put_f32(a.o + static_cast<size_t>(head) * HD + d, A / L);
   }

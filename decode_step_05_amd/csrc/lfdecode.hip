@@ -42,11 +42,13 @@ struct AttnPlan {
   int S, chunk;
 };
 
+// A workgroup reads its keys in one round of loads: 8 loads of K and of V per
+// lane, 4 waves, 512/head_dim keys per wave load -> 16384/head_dim keys.
+constexpr int kAttnU = 8;
 AttnPlan attn_plan(const lf_config& c, int layer) {
   const int visible = c.window[layer] > 0 ? std::min(c.window[layer], c.max_ctx) : c.max_ctx;
-  int S = std::max(1, 256 / c.n_kv_heads);  // about one workgroup per CU over all kv heads
-  S = std::min(S, 32);
-  S = std::min(S, visible);
+  const int per_wg = kAttnU * lf::kWavesPerBlock * (512 / c.head_dim);
+  int S = std::min((visible + per_wg - 1) / per_wg, 64);
   const int chunk = (visible + S - 1) / S;
   S = (visible + chunk - 1) / chunk;
   return {S, chunk};
@@ -265,7 +267,7 @@ int set_lds_limit_epi() {
 
 template <int HD, int G>
 void launch_attn_t(const lf::AttnArgs& a, int n_kv, hipStream_t st) {
-  hipLaunchKernelGGL((lf::k_attn<HD, G, 8>), dim3(a.S, n_kv), dim3(lf::kBlock), 0, st, a);
+  hipLaunchKernelGGL((lf::k_attn<HD, G, kAttnU>), dim3(a.S, n_kv), dim3(lf::kBlock), 0, st, a);
 }
 
 void launch_attn(const lf::AttnArgs& a, int hd, int G, int n_kv, hipStream_t st) {
