@@ -655,12 +655,16 @@ __global__ void k_fill_u32(unsigned* p, unsigned v, int n) {
 }
 
 // Start a step with an explicit token, or set the length (d_token == null).
+// After a length change the greedy token of position len may be recorded as
+// token len+1 again (positions past len are discarded).
 __global__ void k_set_pos(int32_t* state, int32_t* tokens, int32_t len, const int32_t* d_token) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   state[kLen] = len;
   if (d_token) {
     tokens[len] = *d_token;
     state[kFedEnd] = len + 1;
+  } else {
+    state[kFedEnd] = min(state[kFedEnd], len + 1);
   }
 }
 

@@ -622,6 +622,17 @@ int lf_kv_cache_ptrs(const lf_kv* kv, void** d_k, void** d_v) {
 
 int32_t lf_kv_len(const lf_kv* kv) { return kv ? kv->len : -1; }
 
+int lf_kv_tokens(const lf_kv* kv, int32_t* d_out, int32_t start, int32_t n, void* stream) {
+  if (!kv || !d_out) return fail(LF_EINVAL, "null argument");
+  if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");
+  if (start < 0 || n < 0 || static_cast<long>(start) + n > kv->m->D.ctx + 1)
+    return fail(LF_ERANGE, "tokens [%d, %d) outside [0, %d]", start, start + n, kv->m->D.ctx + 1);
+  if (n == 0) return LF_OK;
+  LF_HIP(hipMemcpyAsync(d_out, kv->tokens() + start, static_cast<size_t>(n) * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                        static_cast<hipStream_t>(stream)));
+  return LF_OK;
+}
+
 int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream) {
   if (!kv) return fail(LF_EINVAL, "kv is null");
   if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");

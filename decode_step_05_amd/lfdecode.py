@@ -19,7 +19,7 @@ LF_OK, LF_EINVAL, LF_ERANGE, LF_EHIP = 0, -1, -2, -3
 # Every symbol include/lfdecode.h declares.
 EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
-    "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_prefill",
+    "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
     "lf_step_kernel_times", "lf_last_error",
 )
@@ -68,6 +68,7 @@ def load():
         "lf_kv_cache_ptrs": (c_int, [P, POINTER(P), POINTER(P)]),
         "lf_kv_set_len": (c_int, [P, c_int32, P]),
         "lf_kv_len": (c_int32, [P]),
+        "lf_kv_tokens": (c_int, [P, P, c_int32, c_int32, P]),
         "lf_prefill": (c_int, [P, P, P, c_int32, P]),
         "lf_decode_step": (c_int, [P, P, P, P]),
         "lf_decode_steps": (c_int, [P, P, c_int32, P]),
@@ -194,6 +195,10 @@ def lf_kv_set_len(kv, length: int, stream=None) -> None:
 
 def lf_kv_len(kv) -> int:
     return load().lf_kv_len(kv)
+
+
+def lf_kv_tokens(kv, out, start: int, n: int, stream=None) -> None:
+    _check(load().lf_kv_tokens(kv, _ptr(out), int(start), int(n), _stream(stream)))
 
 
 def lf_prefill(model, kv, tokens, n=None, stream=None) -> None:

@@ -110,6 +110,13 @@ class Sequence:
     def step_hidden(self, x_in, x_out, stream=None):
         C.lf_decode_step_hidden(self.dec.handle, self.handle, x_in, x_out, stream)
 
+    def tokens(self, start, n, stream=None):
+        """Token ids [start, start + n) of the history, as an int32 device tensor."""
+        torch = _torch()
+        out = torch.empty(n, dtype=torch.int32, device=self.dec.device)
+        C.lf_kv_tokens(self.handle, out, start, n, stream)
+        return out
+
     def logits(self, stream=None):
         torch = _torch()
         z = torch.empty(self.dec.c.vocab, dtype=torch.float32, device=self.dec.device)

@@ -133,10 +133,21 @@ int lf_kv_cache_ptrs(const lf_kv* kv, void** d_k, void** d_v);
 
 /*
  * Set the sequence length to len (0 <= len <= max_ctx): rewinds, or adopts
- * cache content the caller wrote for positions [0, len). Enqueued on stream.
+ * cache content the caller wrote for positions [0, len). Token len of the
+ * history is kept as the input of the next step; greedy tokens of the
+ * following steps are recorded from token len+1 on. Enqueued on stream.
  */
 int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream);
 int32_t lf_kv_len(const lf_kv* kv);
+
+/*
+ * Copy token ids [start, start + n) of the sequence's history to d_out (device
+ * int32, caller-owned): prompt tokens, tokens given to lf_decode_step, and the
+ * greedy token of every decoded position p (stored as token p+1 once p+1 is
+ * past the tokens given by the caller). 0 <= start, start + n <= max_ctx + 1,
+ * else LF_ERANGE. Enqueued on stream.
+ */
+int lf_kv_tokens(const lf_kv* kv, int32_t* d_out, int32_t start, int32_t n, void* stream);
 
 /*
  * Append n positions whose token ids are d_tokens[0..n) (device int32, each in
