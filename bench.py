@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event timing pass")
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps of the CPU baseline (0 = skip)")
+    ap.add_argument("--mode", choices=["default", "persistent", "graph", "eager"], default="default",
+                    help="step launch mode (default: the library's choice)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this decode path runs on one GPU; --gpus must be 1 "
@@ -132,7 +134,10 @@ def main():
     t = time.perf_counter()
     weights = make_weights(cfg, seed=wl.weight_seed, threads=16)
     log(f"[bench] weights generated in {time.perf_counter() - t:.1f}s")
-    dec = Decoder(cfg, weights)
+    modes = {"persistent": C.LF_MODE_PERSISTENT, "graph": C.LF_MODE_GRAPH, "eager": C.LF_MODE_EAGER}
+    dec = Decoder(cfg, weights, mode=None if args.mode == "default" else modes[args.mode])
+    mode_name = {v: k for k, v in modes.items()}[dec.mode]
+    log(f"[bench] step launch mode: {mode_name}")
     seq = dec.sequence()
     prompt = make_prompt(cfg, P, seed=wl.prompt_seed)
     torch.cuda.synchronize()

@@ -447,45 +447,60 @@ struct AttnArgs {
   float scale_log2;         // log2(e) / sqrt(hd)
 };
 
-// Workgroup (split s, kv head h) reads keys [lo + s*chunk, lo + (s+1)*chunk)
+// LDS of one attention work item run by NW waves (also used by the step kernel).
+template <int HD, int G, int NW>
+struct AttnSmem {
+  static constexpr int KPW = kWave / (HD / 8);
+  float2 ml[NW][KPW][G];
+  float acc[NW][KPW][G][HD];
+  int flag;
+};
+
+// Work item (split s, kv head h): read keys [lo + s*chunk, lo + (s+1)*chunk)
 // of kv head h (lane h / kpl) for its G query heads. HD/8 lanes hold one
 // 16-byte piece of a key row; a wave load covers 512/HD keys; U loads of K and
 // of V per lane are in flight per iteration. Each row group keeps an online
-// softmax; the workgroup combines them in LDS and stores one partial state
-// per query head. The last workgroup of the kv head merges the S partials.
-template <int HD, int G, int U>
-__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
+// softmax; the workgroup combines them in LDS and stores one partial state per
+// query head. The last workgroup of the kv head merges the S partials, 16 at a
+// time. All NW waves of the workgroup take part (barriers inside). COH: read
+// the queries and the key written in this launch with device-scope loads.
+template <int HD, int G, int U, int NW, bool COH>
+__device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>& sm, int s, int kvh, int p) {
   constexpr int LPR = HD / 8;        // lanes per key row
   constexpr int KPW = kWave / LPR;   // keys per wave load
-  __shared__ float2 sm_ml[kWavesPerBlock][KPW][G];
-  __shared__ float sm_acc[kWavesPerBlock][KPW][G][HD];
-  __shared__ int flag;
-
-  const int s = blockIdx.x, kvh = blockIdx.y;
+  constexpr int NT = NW * kWave;
   const int ln = kvh / a.kpl, kvl = kvh % a.kpl;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int kin = lane / LPR, ch = lane % LPR;
-  // the queries do not depend on the position: load them first
-  f32x4 qv[G][2];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const f32x4* qp = reinterpret_cast<const f32x4*>(a.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8);
-    qv[g][0] = qp[0];
-    qv[g][1] = qp[1];
-  }
-  const int p = a.state[kLen];
-  if (p >= a.max_ctx) return;
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const int k0 = lo + s * a.chunk;
   const int nk = max(0, min(k0 + a.chunk, p + 1) - k0);
+
+  // key j of this kv head: ((ln * max_ctx + j) * kpl + kvl) * HD
+  const size_t key_stride = static_cast<size_t>(a.kpl) * HD;
+  const size_t base = ((static_cast<size_t>(ln) * a.max_ctx + min(k0, a.max_ctx - 1)) * a.kpl + kvl) * HD + ch * 8;
+  const half_t* Kb = a.kc + base;
+  const half_t* Vb = a.vc + base;
   float qr[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
+    const float* qp = a.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8;
+    if (COH) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qr[g][i] = qv[g][0][i] * a.scale_log2;
-      qr[g][4 + i] = qv[g][1][i] * a.scale_log2;
+      for (int i = 0; i < 4; ++i) {
+        const float2 f = get_f32x2(reinterpret_cast<const float2*>(qp) + i);
+        qr[g][2 * i] = f.x * a.scale_log2;
+        qr[g][2 * i + 1] = f.y * a.scale_log2;
+      }
+    } else {
+      const f32x4 q0 = reinterpret_cast<const f32x4*>(qp)[0], q1 = reinterpret_cast<const f32x4*>(qp)[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qr[g][i] = q0[i] * a.scale_log2;
+        qr[g][4 + i] = q1[i] * a.scale_log2;
+      }
     }
+  }
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -494,23 +509,30 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
   }
-
-  // key j of this kv head: ((ln * max_ctx + j) * kpl + kvl) * HD
-  const size_t key_stride = static_cast<size_t>(a.kpl) * HD;
-  const size_t base = ((static_cast<size_t>(ln) * a.max_ctx + min(k0, a.max_ctx - 1)) * a.kpl + kvl) * HD + ch * 8;
-  const half_t* Kb = a.kc + base;
-  const half_t* Vb = a.vc + base;
-  for (int b0 = wave; b0 * KPW < nk; b0 += kWavesPerBlock * U) {
+  for (int b0 = wave; b0 * KPW < nk; b0 += NW * U) {
     u32x4 kk[U], vv[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // keys past the range load the last key of the range and are masked below
-      const int t = (b0 + u * kWavesPerBlock) * KPW + kin;
+      const int t = (b0 + u * NW) * KPW + kin;
       ok[u] = t < nk;
       const size_t off = static_cast<size_t>(min(t, nk - 1)) * key_stride;
-      kk[u] = ld_stream(Kb + off);
-      vv[u] = ld_stream(Vb + off);
+      if (COH && k0 + min(t, nk - 1) == p) {  // the key written in this launch
+        const unsigned long long* kp = reinterpret_cast<const unsigned long long*>(Kb + off);
+        const unsigned long long* vp = reinterpret_cast<const unsigned long long*>(Vb + off);
+        const unsigned long long k_lo = __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long k_hi = __hip_atomic_load(kp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long v_lo = __hip_atomic_load(vp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long v_hi = __hip_atomic_load(vp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        kk[u] = u32x4{static_cast<unsigned>(k_lo), static_cast<unsigned>(k_lo >> 32), static_cast<unsigned>(k_hi),
+                      static_cast<unsigned>(k_hi >> 32)};
+        vv[u] = u32x4{static_cast<unsigned>(v_lo), static_cast<unsigned>(v_lo >> 32), static_cast<unsigned>(v_hi),
+                      static_cast<unsigned>(v_hi >> 32)};
+      } else {
+        kk[u] = ld_stream(Kb + off);
+        vv[u] = ld_stream(Vb + off);
+      }
     }
     float sc[U][G];
 #pragma unroll
@@ -553,27 +575,27 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm_acc[wave][kin][g][ch * 8 + i] = acc[g][i];
-    if (ch == 0) sm_ml[wave][kin][g] = make_float2(m[g], l[g]);
+    for (int i = 0; i < 8; ++i) sm.acc[wave][kin][g][ch * 8 + i] = acc[g][i];
+    if (ch == 0) sm.ml[wave][kin][g] = make_float2(m[g], l[g]);
   }
   __syncthreads();
-  for (int idx = tid; idx < G * HD; idx += kBlock) {
+  for (int idx = tid; idx < G * HD; idx += NT) {
     const int d = idx % HD, g = idx / HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w)
+    for (int w = 0; w < NW; ++w)
 #pragma unroll
-      for (int r = 0; r < KPW; ++r) M = fmaxf(M, sm_ml[w][r][g].x);
+      for (int r = 0; r < KPW; ++r) M = fmaxf(M, sm.ml[w][r][g].x);
     float L = 0.f, A = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w)
+      for (int w = 0; w < NW; ++w)
 #pragma unroll
         for (int r = 0; r < KPW; ++r) {
-          const float2 ml = sm_ml[w][r][g];
+          const float2 ml = sm.ml[w][r][g];
           const float f = exp2f(ml.x - M);
           L = fmaf(ml.y, f, L);
-          A = fmaf(sm_acc[w][r][g][d], f, A);
+          A = fmaf(sm.acc[w][r][g][d], f, A);
         }
     }
     const int head = kvh * G + g;
@@ -583,11 +605,11 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 
   // The last workgroup of this kv head merges its splits, loading the
   // partial states 16 splits at a time (one memory round trip per batch).
-  if (!arrive(&a.counters[kvh], a.S, &flag)) return;
+  if (!arrive(&a.counters[kvh], a.S, &sm.flag)) return;
   const int n = p + 1 - lo;
   const int n_active = min(a.S, (n + a.chunk - 1) / a.chunk);
   constexpr int MB = 16;
-  for (int idx = tid; idx < G * HD; idx += kBlock) {
+  for (int idx = tid; idx < G * HD; idx += NT) {
     const int d = idx % HD, head = kvh * G + idx / HD;
     const float2* ml = a.part_ml + head * a.S;
     const float* pa = a.part_acc + static_cast<size_t>(head) * a.S * HD + d;
@@ -614,6 +636,15 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     put_f32(a.o + static_cast<size_t>(head) * HD + d, A / L);
   }
   if (tid == 0) __hip_atomic_store(&a.counters[kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+}
+
+template <int HD, int G, int U>
+__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
+  __shared__ AttnSmem<HD, G, kWavesPerBlock> sm;
+  const int p = a.state[kLen];
+  if (p >= a.max_ctx) return;
+  attn_item<HD, G, U, kWavesPerBlock, false>(a, sm, blockIdx.x, blockIdx.y, p);
 }
 
 // ------------------------------------------------------------- utilities

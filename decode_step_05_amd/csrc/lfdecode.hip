@@ -3,6 +3,7 @@
 // declared in include/lfdecode.h.
 #include "lfdecode.h"
 #include "lf_kernels.h"
+#include "lf_step.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -117,7 +118,7 @@ Dims dims(const lf_config& c) {
 // Byte offsets of everything in the model workspace.
 struct WsLayout {
   std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
-  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, total;
+  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, bar, layers, total;
   int S_max;
 };
 
@@ -151,6 +152,8 @@ WsLayout ws_layout(const lf_config& c) {
   W.part_acc = take(static_cast<size_t>(D.hq) * W.S_max * D.hd * sizeof(float));
   W.best = take(sizeof(unsigned long long));
   W.counters = take((D.hkv + 4) * sizeof(unsigned));
+  W.bar = take(4 * sizeof(unsigned));
+  W.layers = take(static_cast<size_t>(D.L) * sizeof(lf::LayerW));
   W.total = off;
   return W;
 }
@@ -189,10 +192,12 @@ struct lf_model {
   Dims D;
   WsLayout W;
   char* ws;
-  bool use_graph = true;
   hipStream_t capture_stream = nullptr;  // graphs are recorded here, replayed on the caller's stream
   std::vector<hipEvent_t> events;        // per-kernel brackets for lf_step_kernel_times
   std::vector<lf_kv*> kvs;               // live sequences; detached when the model is freed
+  int mode = LF_MODE_GRAPH;
+  const void* step_fn = nullptr;         // persistent step kernel for this shape (null: unavailable)
+  int step_grid = 0;
   std::vector<GraphEntry> graphs;
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -283,6 +288,61 @@ int set_lds_limits() {
   if ((rc = set_lds_limit_epi<lf::kEpiQKV>()) || (rc = set_lds_limit_epi<lf::kEpiSwiGLU>()) ||
       (rc = set_lds_limit_epi<lf::kEpiResid>()) || (rc = set_lds_limit_epi<lf::kEpiLogits>()))
     return rc;
+  return LF_OK;
+}
+
+// Persistent step kernels compiled for the shapes in use: (head_dim, query
+// heads per kv head, 16-byte chunks per lane covering d_model and the query
+// width, chunks covering ffn). Other shapes run the per-phase kernels.
+struct StepVariant {
+  int hd, G, kd, kf;
+  const void* fn;
+};
+#define LF_STEP(HD, G, KD, KF) {HD, G, KD, KF, reinterpret_cast<const void*>(&lf::k_step<HD, G, KD, KF>)}
+const StepVariant kStepVariants[] = {
+    LF_STEP(128, 2, 8, 14),  // the 2.3B-shaped decoder and its single layer
+    LF_STEP(128, 2, 8, 2),   // one lane's share
+    LF_STEP(32, 2, 1, 2),    // tiny decoder
+    LF_STEP(64, 2, 1, 1),
+    LF_STEP(128, 4, 2, 2),
+    LF_STEP(128, 2, 2, 1),
+};
+#undef LF_STEP
+
+int gemv_kch(int K);
+
+const void* find_step_kernel(const Dims& D) {
+  const int kd = std::max(gemv_kch(D.d), gemv_kch(D.qdim)), kf = gemv_kch(D.ffn);
+  for (const StepVariant& v : kStepVariants)
+    if (v.hd == D.hd && v.G == D.G && v.kd == kd && v.kf == kf) return v.fn;
+  return nullptr;
+}
+
+int launch_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
+  const Dims& D = m->D;
+  const WsLayout& W = m->W;
+  lf::StepArgs a{};
+  a.layers = m->at<lf::LayerW>(W.layers);
+  a.L = D.L; a.d = D.d; a.qkv_rows = D.qkv_rows; a.qdim = D.qdim; a.ffn = D.ffn; a.vocab = D.V; a.hd = D.hd;
+  a.qpl = D.qpl; a.kpl = D.kpl; a.n_kv = D.hkv; a.max_ctx = D.ctx;
+  a.eps = m->cfg.rms_eps;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
+  a.embed = D.V ? m->at<half_t>(W.embed) : nullptr;
+  a.lm = D.V ? m->at<half_t>(W.lm) : nullptr;
+  a.gf = D.V ? m->at<half_t>(W.gf) : nullptr;
+  a.rope = m->at<float2>(W.rope);
+  a.x = m->at<float>(W.x); a.q = m->at<float>(W.q); a.o = m->at<float>(W.o); a.act = m->at<float>(W.act);
+  a.part_ml = m->at<float2>(W.part_ml);
+  a.part_acc = m->at<float>(W.part_acc);
+  a.attn_counters = m->at<unsigned>(W.counters);
+  a.best = m->at<unsigned long long>(W.best);
+  a.bar = m->at<unsigned>(W.bar);
+  a.state = kv->state(); a.tokens = kv->tokens(); a.logits = kv->logits();
+  a.kc = kv->kc(); a.vc = kv->vc();
+  a.layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
+  a.x_in = xin; a.x_out = xout;
+  void* args[] = {&a};
+  LF_HIP(hipLaunchCooperativeKernel(m->step_fn, dim3(m->step_grid), dim3(lf::kStepThreads), args, 0, st));
   return LF_OK;
 }
 
@@ -429,7 +489,8 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
 }
 
 int run_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
-  if (!m->use_graph) return enqueue_step(m, kv, xin, xout, st);
+  if (m->mode == LF_MODE_PERSISTENT) return launch_step(m, kv, xin, xout, st);
+  if (m->mode == LF_MODE_EAGER) return enqueue_step(m, kv, xin, xout, st);
   hipGraphExec_t exec = nullptr;
   for (const GraphEntry& g : m->graphs)
     if (g.kv == kv && g.xin == xin && g.xout == xout) exec = g.exec;
@@ -557,6 +618,32 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   const int nctr = D.hkv + 4;
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, nctr);
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.best), 0u, 2);
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar), 0u, 4);
+  // Per-layer pointer table of the persistent step kernel.
+  std::vector<lf::LayerW> table(D.L);
+  for (int l = 0; l < D.L; ++l) {
+    const AttnPlan P = attn_plan(*cfg, l);
+    table[l] = {m->at<half_t>(W.wqkv[l]), m->at<half_t>(W.wo[l]), m->at<half_t>(W.wgu[l]), m->at<half_t>(W.wd[l]),
+                m->at<half_t>(W.g1[l]), m->at<half_t>(W.g2[l]), cfg->window[l], P.S, P.chunk};
+  }
+  if (hipMemcpyAsync(m->at<lf::LayerW>(W.layers), table.data(), table.size() * sizeof(lf::LayerW),
+                     hipMemcpyHostToDevice, st))
+    return bail(fail(LF_EHIP, "layer table upload failed: %s", hipGetErrorString(hipGetLastError())));
+  // The persistent step kernel needs cooperative launch and one 512-thread
+  // workgroup resident per compute unit. Graph replay stays the default: it
+  // is the faster mode on MI355X at the shapes measured so far.
+  {
+    int dev = 0, coop = 0, ncu = 0, per_cu = 0;
+    const void* fn = find_step_kernel(D);
+    if (fn && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, lf::kStepThreads, 0) == hipSuccess && per_cu >= 1) {
+      m->step_fn = fn;
+      m->step_grid = ncu;
+    }
+    (void)hipGetLastError();
+  }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
@@ -577,9 +664,21 @@ void lf_model_free(lf_model* m) {
 
 int lf_model_set_graph(lf_model* m, int enabled) {
   if (!m) return fail(LF_EINVAL, "model is null");
-  m->use_graph = enabled != 0;
+  m->mode = enabled ? LF_MODE_GRAPH : LF_MODE_EAGER;
   return LF_OK;
 }
+
+int lf_model_set_mode(lf_model* m, int mode) {
+  if (!m) return fail(LF_EINVAL, "model is null");
+  if (mode != LF_MODE_EAGER && mode != LF_MODE_GRAPH && mode != LF_MODE_PERSISTENT)
+    return fail(LF_EINVAL, "unknown mode %d", mode);
+  if (mode == LF_MODE_PERSISTENT && !m->step_fn)
+    return fail(LF_EINVAL, "no persistent step kernel for this shape or device");
+  m->mode = mode;
+  return LF_OK;
+}
+
+int lf_model_mode(const lf_model* m) { return m ? m->mode : -1; }
 
 int lf_kv_alloc(lf_model* m, void* d_buf, size_t bytes, lf_kv** out) {
   if (!m || !d_buf || !out) return fail(LF_EINVAL, "null argument");
@@ -716,12 +815,14 @@ int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream) {
   if (!kv || !out) return fail(LF_EINVAL, "null argument");
   if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");
   int32_t s[4];
+  unsigned bar[4];
   hipStream_t st = static_cast<hipStream_t>(stream);
   LF_HIP(hipMemcpyAsync(s, kv->state(), sizeof s, hipMemcpyDeviceToHost, st));
+  LF_HIP(hipMemcpyAsync(bar, kv->m->at<unsigned>(kv->m->W.bar), sizeof bar, hipMemcpyDeviceToHost, st));
   LF_HIP(hipStreamSynchronize(st));
   out[0] = s[lf::kLen];
   out[1] = s[lf::kArgmax];
-  out[2] = s[lf::kBadToken];
+  out[2] = (s[lf::kBadToken] ? 1 : 0) | (bar[2] ? 2 : 0);
   return LF_OK;
 }
 

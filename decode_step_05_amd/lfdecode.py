@@ -15,10 +15,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblfdecode
 MAX_LAYERS = 64
 
 LF_OK, LF_EINVAL, LF_ERANGE, LF_EHIP = 0, -1, -2, -3
+LF_MODE_EAGER, LF_MODE_GRAPH, LF_MODE_PERSISTENT = 0, 1, 2
 
 # Every symbol include/lfdecode.h declares.
 EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
+    "lf_model_set_mode", "lf_model_mode",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
     "lf_step_kernel_times", "lf_last_error",
@@ -63,6 +65,8 @@ def load():
         "lf_model_init": (c_int, [POINTER(lf_config), POINTER(lf_weight_ptrs), P, c_size_t, P, POINTER(P)]),
         "lf_model_free": (None, [P]),
         "lf_model_set_graph": (c_int, [P, c_int]),
+        "lf_model_set_mode": (c_int, [P, c_int]),
+        "lf_model_mode": (c_int, [P]),
         "lf_kv_alloc": (c_int, [P, P, c_size_t, POINTER(P)]),
         "lf_kv_free": (None, [P]),
         "lf_kv_cache_ptrs": (c_int, [P, POINTER(P), POINTER(P)]),
@@ -171,6 +175,14 @@ def lf_model_free(model) -> None:
 
 def lf_model_set_graph(model, enabled: bool) -> None:
     _check(load().lf_model_set_graph(model, int(bool(enabled))))
+
+
+def lf_model_set_mode(model, mode: int) -> None:
+    _check(load().lf_model_set_mode(model, int(mode)))
+
+
+def lf_model_mode(model) -> int:
+    return load().lf_model_mode(model)
 
 
 def lf_kv_alloc(model, buf):

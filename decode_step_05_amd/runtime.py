@@ -17,7 +17,7 @@ class Decoder:
     workspace with torch and calls lf_model_init. The library copies what it
     needs, so the uploaded weights are released afterwards."""
 
-    def __init__(self, cfg, weights: dict, device="cuda", stream=None, graph=True):
+    def __init__(self, cfg, weights: dict, device="cuda", stream=None, graph=True, mode=None):
         torch = _torch()
         self.cfg = cfg
         self.c = C.make_config(cfg)
@@ -35,6 +35,15 @@ class Decoder:
         del dev_w
         if not graph:
             C.lf_model_set_graph(self.handle, False)
+        if mode is not None:
+            C.lf_model_set_mode(self.handle, mode)
+
+    @property
+    def mode(self) -> int:
+        return C.lf_model_mode(self.handle)
+
+    def set_mode(self, mode: int):
+        C.lf_model_set_mode(self.handle, mode)
 
     def set_graph(self, enabled: bool):
         C.lf_model_set_graph(self.handle, enabled)

@@ -113,10 +113,23 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
 void lf_model_free(lf_model* m);
 
 /*
- * Launch mode of the decode step: 1 (default) replays a hipGraph captured on
- * first use per (sequence, in/out pointers); 0 launches the kernels one by one.
- * Both run the same kernels with the same arguments.
+ * How a step is launched. All modes compute the same function.
+ *   LF_MODE_PERSISTENT: one cooperative launch per step; the workgroups run
+ *     the phases (QKV, attention, O, gate/up, down, LM head) separated by
+ *     grid barriers and prefetch each phase's weights before its barrier.
+ *     Available when the shape has a compiled step kernel and the device
+ *     supports cooperative launch.
+ *   LF_MODE_GRAPH (default): one kernel per phase, captured per (sequence,
+ *     in/out pointers) into a hipGraph on first use and replayed.
+ *   LF_MODE_EAGER: one kernel per phase, launched one by one.
+ * lf_model_set_mode returns LF_EINVAL for a mode the model cannot run.
+ * lf_model_set_graph(m, 1/0) selects LF_MODE_GRAPH / LF_MODE_EAGER.
  */
+#define LF_MODE_EAGER 0
+#define LF_MODE_GRAPH 1
+#define LF_MODE_PERSISTENT 2
+int lf_model_set_mode(lf_model* m, int mode);
+int lf_model_mode(const lf_model* m);
 int lf_model_set_graph(lf_model* m, int enabled);
 
 /*
@@ -183,8 +196,10 @@ int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_ar
 
 /*
  * Read back (synchronously on stream) the device-side sequence state:
- * out[0] = length, out[1] = last argmax, out[2] = nonzero if a token id
- * outside [0, vocab) was clamped since lf_kv_alloc.
+ * out[0] = length, out[1] = last argmax, out[2] = flags: bit 0 set if a token
+ * id outside [0, vocab) was clamped since lf_kv_alloc; bit 1 set if a
+ * persistent step gave up waiting at a grid barrier (its results are invalid
+ * and later persistent steps of the model do nothing).
  */
 int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
 
