@@ -45,6 +45,17 @@ __device__ __forceinline__ void put_f16(half_t* p, float v) {
 
 // Wait until this wave's stores are acknowledged, then count the workgroup in.
 // Returns true in every thread of the last of `expected` workgroups.
+// Workgroup barrier for data exchanged through LDS only: each wave waits for
+// its own LDS operations, not for its global memory operations (loads may
+// stay in flight across it, where the barrier of __syncthreads would wait for
+// them). Whoever publishes global data waits for it explicitly.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ bool arrive(unsigned* counter, unsigned expected, int* flag_lds) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -53,6 +64,21 @@ __device__ __forceinline__ bool arrive(unsigned* counter, unsigned expected, int
     *flag_lds = (prev == expected - 1) ? 1 : 0;
   }
   __syncthreads();
+  return *flag_lds != 0;
+}
+
+// The same where only wave SW of the workgroup stored what must be visible:
+// only that wave waits for its memory operations (the other waves may keep
+// loads in flight), and its first lane counts the arrival.
+template <int SW>
+__device__ __forceinline__ bool arrive_wave(unsigned* counter, unsigned expected, int* flag_lds) {
+  if (threadIdx.x / kWave == SW) __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  if (threadIdx.x == SW * kWave) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = (prev == expected - 1) ? 1 : 0;
+  }
+  lds_barrier();
   return *flag_lds != 0;
 }
 
@@ -263,6 +289,42 @@ __device__ __forceinline__ void issue_rows(Rows<NR, KCH>& b, const half_t* __res
   }
 }
 
+// Where the QKV projection writes at position p.
+struct QkvOut {
+  float* q;
+  half_t *kc, *vc;
+  const float2* rope;
+  int hd, qpl, kpl, max_ctx;
+};
+
+// Store the rotary pair of QKV rows (r, r+1) (r even; lane-major order: per
+// lane its q heads, then k heads, then v heads, each head's rows as pairs
+// (c, c + hd/2) of the half-split rotary embedding): rotate q and k by the
+// angles of position p, then store q (fp32) or append k / v to the cache (fp16).
+__device__ __forceinline__ void qkv_put(const QkvOut& a, int r, float y0, float y1, int p) {
+  const int half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl;
+  const int u = r / a.hd, c = (r % a.hd) >> 1;
+  const int ln = u / upl, j = u % upl;
+  if (j < a.qpl + a.kpl) {  // rotary embedding on q and k
+    const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
+    const float t0 = y0 * cs.x - y1 * cs.y;
+    const float t1 = y0 * cs.y + y1 * cs.x;
+    y0 = t0;
+    y1 = t1;
+  }
+  if (j < a.qpl) {
+    float* qh = a.q + static_cast<size_t>(ln * a.qpl + j) * a.hd;
+    put_f32(qh + c, y0);
+    put_f32(qh + c + half_hd, y1);
+  } else {
+    const bool is_k = j < a.qpl + a.kpl;
+    const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
+    half_t* dst = (is_k ? a.kc : a.vc) + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
+    put_f16(dst + c, y0);
+    put_f16(dst + c + half_hd, y1);
+  }
+}
+
 // Reduce rows [r, r+NR) against xs and run the epilogue (lane 0 stores).
 // FULL: K is exactly 512*KCH, so every chunk of every lane is in range.
 template <int EPI, int NR, int KCH, bool FULL>
@@ -298,28 +360,7 @@ __device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KC
   if constexpr (EPI == kEpiQKV) {
     static_assert(NR == 2, "QKV rows come in rotary pairs");
     if (r >= a.rows) return;
-    const int half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl;
-    const int u = r / a.hd, c = (r % a.hd) >> 1;
-    const int ln = u / upl, j = u % upl;
-    float y0 = out[0], y1 = out[1];
-    if (j < a.qpl + a.kpl) {  // rotary embedding on q and k
-      const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
-      const float t0 = y0 * cs.x - y1 * cs.y;
-      const float t1 = y0 * cs.y + y1 * cs.x;
-      y0 = t0;
-      y1 = t1;
-    }
-    if (j < a.qpl) {
-      float* qh = a.q + static_cast<size_t>(ln * a.qpl + j) * a.hd;
-      put_f32(qh + c, y0);
-      put_f32(qh + c + half_hd, y1);
-    } else {
-      const bool is_k = j < a.qpl + a.kpl;
-      const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
-      half_t* dst = (is_k ? a.kc : a.vc) + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
-      put_f16(dst + c, y0);
-      put_f16(dst + c + half_hd, y1);
-    }
+    qkv_put(QkvOut{a.q, a.kc, a.vc, a.rope, a.hd, a.qpl, a.kpl, a.max_ctx}, r, out[0], out[1], p);
   } else if constexpr (EPI == kEpiSwiGLU) {
     static_assert(NR == 2, "gate/up rows come in pairs");
     if (r >= a.rows) return;
@@ -456,6 +497,77 @@ struct AttnSmem {
   int flag;
 };
 
+// K and V loads of one iteration of an attention work item: U 16-byte pieces
+// of K and of V per lane.
+template <int U>
+struct AttnLoads {
+  u32x4 kk[U], vv[U];
+};
+
+// Where work item (split s, kv head kvh) reads at position p.
+struct AttnSpan {
+  const half_t *Kb, *Vb;  // this lane's piece of the first key of the split
+  size_t key_stride;      // elements between consecutive keys
+  int k0, nk;             // first key and number of keys of the split
+};
+
+template <int HD>
+__device__ __forceinline__ AttnSpan attn_span(const AttnArgs& a, int s, int kvh, int p) {
+  constexpr int LPR = HD / 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ln = kvh / a.kpl, kvl = kvh % a.kpl;
+  const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+  AttnSpan sp;
+  sp.k0 = lo + s * a.chunk;
+  sp.nk = max(0, min(sp.k0 + a.chunk, p + 1) - sp.k0);
+  // key j of this kv head: ((ln * max_ctx + j) * kpl + kvl) * HD
+  sp.key_stride = static_cast<size_t>(a.kpl) * HD;
+  const size_t base =
+      ((static_cast<size_t>(ln) * a.max_ctx + min(sp.k0, a.max_ctx - 1)) * a.kpl + kvl) * HD + (lane % LPR) * 8;
+  sp.Kb = a.kc + base;
+  sp.Vb = a.vc + base;
+  return sp;
+}
+
+// Load 16 bytes of the key (or value) row written in this launch, with
+// device-scope loads.
+__device__ __forceinline__ u32x4 ld_coherent16(const half_t* ptr) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(ptr);
+  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{static_cast<unsigned>(lo), static_cast<unsigned>(lo >> 32), static_cast<unsigned>(hi),
+               static_cast<unsigned>(hi >> 32)};
+}
+
+// Issue the loads of the iteration whose first wave row block is b0. Keys
+// past the split load its last key (masked where used). COH: the key at p
+// (written in this launch) is read with device-scope loads. Requires nk > 0.
+template <int HD, int U, int NW, bool COH>
+__device__ __forceinline__ void attn_load(AttnLoads<U>& ld, const AttnSpan& sp, int b0, int p) {
+  constexpr int KPW = kWave / (HD / 8);
+  const int kin = (threadIdx.x & (kWave - 1)) / (HD / 8);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = min((b0 + u * NW) * KPW + kin, sp.nk - 1);
+    const size_t off = static_cast<size_t>(t) * sp.key_stride;
+    if (COH && sp.k0 + t == p) {
+      ld.kk[u] = ld_coherent16(sp.Kb + off);
+      ld.vv[u] = ld_coherent16(sp.Vb + off);
+    } else {
+      ld.kk[u] = ld_stream(sp.Kb + off);
+      ld.vv[u] = ld_stream(sp.Vb + off);
+    }
+  }
+}
+
+// Prefetch of the first iteration of a work item before the key at p exists:
+// every key is loaded plainly; attn_item(PRE) reloads the key at p.
+template <int HD, int U, int NW>
+__device__ __forceinline__ void attn_prefetch(AttnLoads<U>& ld, const AttnArgs& a, int s, int kvh, int p) {
+  const AttnSpan sp = attn_span<HD>(a, s, kvh, p);
+  if (sp.nk > 0) attn_load<HD, U, NW, false>(ld, sp, threadIdx.x / kWave, p);
+}
+
 // Work item (split s, kv head h): read keys [lo + s*chunk, lo + (s+1)*chunk)
 // of kv head h (lane h / kpl) for its G query heads. HD/8 lanes hold one
 // 16-byte piece of a key row; a wave load covers 512/HD keys; U loads of K and
@@ -464,23 +576,21 @@ struct AttnSmem {
 // query head. The last workgroup of the kv head merges the S partials, 16 at a
 // time. All NW waves of the workgroup take part (barriers inside). COH: read
 // the queries and the key written in this launch with device-scope loads.
-template <int HD, int G, int U, int NW, bool COH>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>& sm, int s, int kvh, int p) {
+// PRE: the first iteration's loads were issued by attn_prefetch (into *pre).
+// SW >= 0: only wave SW stores (partial states, merged outputs) and counts
+// the arrival; the other waves only load and compute.
+template <int HD, int G, int U, int NW, bool COH, bool PRE = false, int SW = -1>
+__device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>& sm, int s, int kvh, int p,
+                                          const AttnLoads<U>* pre = nullptr) {
   constexpr int LPR = HD / 8;        // lanes per key row
   constexpr int KPW = kWave / LPR;   // keys per wave load
   constexpr int NT = NW * kWave;
-  const int ln = kvh / a.kpl, kvl = kvh % a.kpl;
+  static_assert(!PRE || COH, "a prefetched item must reload the key written in this launch");
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int kin = lane / LPR, ch = lane % LPR;
+  const AttnSpan sp = attn_span<HD>(a, s, kvh, p);
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-  const int k0 = lo + s * a.chunk;
-  const int nk = max(0, min(k0 + a.chunk, p + 1) - k0);
-
-  // key j of this kv head: ((ln * max_ctx + j) * kpl + kvl) * HD
-  const size_t key_stride = static_cast<size_t>(a.kpl) * HD;
-  const size_t base = ((static_cast<size_t>(ln) * a.max_ctx + min(k0, a.max_ctx - 1)) * a.kpl + kvl) * HD + ch * 8;
-  const half_t* Kb = a.kc + base;
-  const half_t* Vb = a.vc + base;
+  const int nk = sp.nk;
   float qr[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -510,35 +620,29 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
   }
   for (int b0 = wave; b0 * KPW < nk; b0 += NW * U) {
-    u32x4 kk[U], vv[U];
+    AttnLoads<U> ld;
+    if (PRE && b0 == wave) {
+      ld = *pre;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = min((b0 + u * NW) * KPW + kin, nk - 1);
+        if (sp.k0 + t == p) {
+          const size_t off = static_cast<size_t>(t) * sp.key_stride;
+          ld.kk[u] = ld_coherent16(sp.Kb + off);
+          ld.vv[u] = ld_coherent16(sp.Vb + off);
+        }
+      }
+    } else {
+      attn_load<HD, U, NW, COH>(ld, sp, b0, p);
+    }
     bool ok[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // keys past the range load the last key of the range and are masked below
-      const int t = (b0 + u * NW) * KPW + kin;
-      ok[u] = t < nk;
-      const size_t off = static_cast<size_t>(min(t, nk - 1)) * key_stride;
-      if (COH && k0 + min(t, nk - 1) == p) {  // the key written in this launch
-        const unsigned long long* kp = reinterpret_cast<const unsigned long long*>(Kb + off);
-        const unsigned long long* vp = reinterpret_cast<const unsigned long long*>(Vb + off);
-        const unsigned long long k_lo = __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long k_hi = __hip_atomic_load(kp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long v_lo = __hip_atomic_load(vp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long v_hi = __hip_atomic_load(vp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        kk[u] = u32x4{static_cast<unsigned>(k_lo), static_cast<unsigned>(k_lo >> 32), static_cast<unsigned>(k_hi),
-                      static_cast<unsigned>(k_hi >> 32)};
-        vv[u] = u32x4{static_cast<unsigned>(v_lo), static_cast<unsigned>(v_lo >> 32), static_cast<unsigned>(v_hi),
-                      static_cast<unsigned>(v_hi >> 32)};
-      } else {
-        kk[u] = ld_stream(Kb + off);
-        vv[u] = ld_stream(Vb + off);
-      }
-    }
+    for (int u = 0; u < U; ++u) ok[u] = (b0 + u * NW) * KPW + kin < nk;
     float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[8];
-      unpack8(kk[u], kf);
+      unpack8(ld.kk[u], kf);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.f;
@@ -563,7 +667,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
         const float pu = exp2f(sc[u][g] - mx);
         l[g] += pu;
         float vf[8];
-        unpack8(vv[u], vf);
+        unpack8(ld.vv[u], vf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(pu, vf[i], acc[g][i]);
       }
@@ -578,8 +682,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
     for (int i = 0; i < 8; ++i) sm.acc[wave][kin][g][ch * 8 + i] = acc[g][i];
     if (ch == 0) sm.ml[wave][kin][g] = make_float2(m[g], l[g]);
   }
-  __syncthreads();
-  for (int idx = tid; idx < G * HD; idx += NT) {
+  lds_barrier();
+  // storing threads: all of them, or the lanes of wave SW
+  const bool storer = SW < 0 || wave == SW;
+  const int st0 = SW < 0 ? tid : lane, stn = SW < 0 ? NT : kWave;
+  for (int idx = storer ? st0 : G * HD; idx < G * HD; idx += stn) {
     const int d = idx % HD, g = idx / HD;
     float M = -INFINITY;
 #pragma unroll
@@ -605,11 +712,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
 
   // The last workgroup of this kv head merges its splits, loading the
   // partial states 16 splits at a time (one memory round trip per batch).
-  if (!arrive(&a.counters[kvh], a.S, &sm.flag)) return;
+  if (!(SW < 0 ? arrive(&a.counters[kvh], a.S, &sm.flag) : arrive_wave<SW < 0 ? 0 : SW>(&a.counters[kvh], a.S, &sm.flag)))
+    return;
   const int n = p + 1 - lo;
   const int n_active = min(a.S, (n + a.chunk - 1) / a.chunk);
   constexpr int MB = 16;
-  for (int idx = tid; idx < G * HD; idx += NT) {
+  for (int idx = storer ? st0 : G * HD; idx < G * HD; idx += stn) {
     const int d = idx % HD, head = kvh * G + idx / HD;
     const float2* ml = a.part_ml + head * a.S;
     const float* pa = a.part_acc + static_cast<size_t>(head) * a.S * HD + d;
@@ -635,8 +743,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
     }
     put_f32(a.o + static_cast<size_t>(head) * HD + d, A / L);
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  if (tid == (SW < 0 ? 0 : SW * kWave))
+    __hip_atomic_store(&a.counters[kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
 }
 
 template <int HD, int G, int U>

@@ -3,7 +3,7 @@
 // declared in include/lfdecode.h.
 #include "lfdecode.h"
 #include "lf_kernels.h"
-#include "lf_step.h"
+#include "lf_stream.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -46,13 +46,25 @@ struct AttnPlan {
 // A workgroup reads its keys in one round of loads: 8 loads of K and of V per
 // lane, 4 waves, 512/head_dim keys per wave load -> 16384/head_dim keys.
 constexpr int kAttnU = 8;
-AttnPlan attn_plan(const lf_config& c, int layer) {
-  const int visible = c.window[layer] > 0 ? std::min(c.window[layer], c.max_ctx) : c.max_ctx;
-  const int per_wg = kAttnU * lf::kWavesPerBlock * (512 / c.head_dim);
-  int S = std::min((visible + per_wg - 1) / per_wg, 64);
+constexpr int kMaxSplits = 64;  // partial-state buffers hold this many splits per head
+AttnPlan split_plan(int visible, int S) {
+  S = std::max(1, std::min(S, kMaxSplits));
   const int chunk = (visible + S - 1) / S;
-  S = (visible + chunk - 1) / chunk;
-  return {S, chunk};
+  return {(visible + chunk - 1) / chunk, chunk};
+}
+int visible_keys(const lf_config& c, int layer) {
+  return c.window[layer] > 0 ? std::min(c.window[layer], c.max_ctx) : c.max_ctx;
+}
+AttnPlan attn_plan(const lf_config& c, int layer) {
+  const int visible = visible_keys(c, layer);
+  const int per_wg = kAttnU * lf::kWavesPerBlock * (512 / c.head_dim);
+  return split_plan(visible, (visible + per_wg - 1) / per_wg);
+}
+// The persistent step kernel runs one work item per workgroup: at most
+// nb / n_kv splits per kv head, of at least 32 keys each.
+AttnPlan step_attn_plan(const lf_config& c, int layer, int nb) {
+  const int visible = visible_keys(c, layer);
+  return split_plan(visible, std::min(nb / c.n_kv_heads, (visible + 31) / 32));
 }
 
 // Launch shape of a GEMV: (waves per workgroup, row groups per wave). Each
@@ -118,9 +130,33 @@ Dims dims(const lf_config& c) {
 // Byte offsets of everything in the model workspace.
 struct WsLayout {
   std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
-  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, bar, layers, total;
+  std::vector<size_t> sw;  // stream-order copies of the GEMV weights, per stream phase
+  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, bar, sphases, slayers, total;
   int S_max;
 };
+
+// The GEMV phases of the stream step kernel: per layer QKV, O, gate/up,
+// down; then the LM head. Rows are dealt to the launch's compute waves, rpw
+// each (the last ones padded with zero rows); a row is kch 1-KB slots.
+struct StreamPhaseShape {
+  int rows, K, kch, rpw;
+  size_t bytes() const { return static_cast<size_t>(rpw) * kch * lf::kSTW * 1024; }
+};
+
+std::vector<StreamPhaseShape> stream_shapes(const Dims& D) {
+  auto shape = [](int rows, int K) {
+    return StreamPhaseShape{rows, K, (K + 511) / 512, (rows + lf::kSTW - 1) / lf::kSTW};
+  };
+  std::vector<StreamPhaseShape> v;
+  for (int l = 0; l < D.L; ++l) {
+    v.push_back(shape(D.qkv_rows, D.d));
+    v.push_back(shape(D.d, D.qdim));
+    v.push_back(shape(2 * D.ffn, D.d));
+    v.push_back(shape(D.d, D.ffn));
+  }
+  if (D.V) v.push_back(shape(D.V, D.d));
+  return v;
+}
 
 WsLayout ws_layout(const lf_config& c) {
   const Dims D = dims(c);
@@ -146,14 +182,16 @@ WsLayout ws_layout(const lf_config& c) {
   W.q = take(D.qdim * sizeof(float));
   W.o = take(D.qdim * sizeof(float));
   W.act = take(D.ffn * sizeof(float));
-  W.S_max = 1;
-  for (int l = 0; l < D.L; ++l) W.S_max = std::max(W.S_max, attn_plan(c, l).S);
+  W.S_max = kMaxSplits;
   W.part_ml = take(static_cast<size_t>(D.hq) * W.S_max * sizeof(float2));
   W.part_acc = take(static_cast<size_t>(D.hq) * W.S_max * D.hd * sizeof(float));
   W.best = take(sizeof(unsigned long long));
   W.counters = take((D.hkv + 4) * sizeof(unsigned));
   W.bar = take(4 * sizeof(unsigned));
-  W.layers = take(static_cast<size_t>(D.L) * sizeof(lf::LayerW));
+  const std::vector<StreamPhaseShape> sp = stream_shapes(D);
+  for (const StreamPhaseShape& e : sp) W.sw.push_back(take(e.bytes()));
+  W.sphases = take(sp.size() * sizeof(lf::SPhase));
+  W.slayers = take(static_cast<size_t>(D.L) * sizeof(lf::SLayer));
   W.total = off;
   return W;
 }
@@ -196,8 +234,8 @@ struct lf_model {
   std::vector<hipEvent_t> events;        // per-kernel brackets for lf_step_kernel_times
   std::vector<lf_kv*> kvs;               // live sequences; detached when the model is freed
   int mode = LF_MODE_GRAPH;
-  const void* step_fn = nullptr;         // persistent step kernel for this shape (null: unavailable)
-  int step_grid = 0;
+  const void* step_fn = nullptr;         // stream step kernel for this shape (null: unavailable)
+  int step_lds = 0;                      // its LDS bytes per workgroup
   std::vector<GraphEntry> graphs;
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -291,44 +329,34 @@ int set_lds_limits() {
   return LF_OK;
 }
 
-// Persistent step kernels compiled for the shapes in use: (head_dim, query
-// heads per kv head, 16-byte chunks per lane covering d_model and the query
-// width, chunks covering ffn). Other shapes run the per-phase kernels.
+// Stream step kernels compiled for the shapes in use: (head_dim, query heads
+// per kv head). Other shapes run the per-phase kernels.
 struct StepVariant {
-  int hd, G, kd, kf;
+  int hd, G, lds;
   const void* fn;
 };
-#define LF_STEP(HD, G, KD, KF) {HD, G, KD, KF, reinterpret_cast<const void*>(&lf::k_step<HD, G, KD, KF>)}
-const StepVariant kStepVariants[] = {
-    LF_STEP(128, 2, 8, 14),  // the 2.3B-shaped decoder and its single layer
-    LF_STEP(128, 2, 8, 2),   // one lane's share
-    LF_STEP(32, 2, 1, 2),    // tiny decoder
-    LF_STEP(64, 2, 1, 1),
-    LF_STEP(128, 4, 2, 2),
-    LF_STEP(128, 2, 2, 1),
-};
+#define LF_STEP(HD, G) {HD, G, lf::stream_lds_bytes<HD, G>(), reinterpret_cast<const void*>(&lf::k_stream<HD, G>)}
+const StepVariant kStepVariants[] = {LF_STEP(128, 2), LF_STEP(64, 2), LF_STEP(32, 2), LF_STEP(128, 4)};
 #undef LF_STEP
 
-int gemv_kch(int K);
-
-const void* find_step_kernel(const Dims& D) {
-  const int kd = std::max(gemv_kch(D.d), gemv_kch(D.qdim)), kf = gemv_kch(D.ffn);
+const StepVariant* find_step_kernel(const Dims& D) {
   for (const StepVariant& v : kStepVariants)
-    if (v.hd == D.hd && v.G == D.G && v.kd == kd && v.kf == kf) return v.fn;
+    if (v.hd == D.hd && v.G == D.G) return &v;
   return nullptr;
 }
 
 int launch_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
   const Dims& D = m->D;
   const WsLayout& W = m->W;
-  lf::StepArgs a{};
-  a.layers = m->at<lf::LayerW>(W.layers);
-  a.L = D.L; a.d = D.d; a.qkv_rows = D.qkv_rows; a.qdim = D.qdim; a.ffn = D.ffn; a.vocab = D.V; a.hd = D.hd;
+  lf::StreamArgs a{};
+  a.ph = m->at<lf::SPhase>(W.sphases);
+  a.layers = m->at<lf::SLayer>(W.slayers);
+  a.n_ph = static_cast<int>(W.sw.size());
+  a.L = D.L; a.d = D.d; a.qdim = D.qdim; a.ffn = D.ffn; a.vocab = D.V; a.hd = D.hd;
   a.qpl = D.qpl; a.kpl = D.kpl; a.n_kv = D.hkv; a.max_ctx = D.ctx;
   a.eps = m->cfg.rms_eps;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
   a.embed = D.V ? m->at<half_t>(W.embed) : nullptr;
-  a.lm = D.V ? m->at<half_t>(W.lm) : nullptr;
   a.gf = D.V ? m->at<half_t>(W.gf) : nullptr;
   a.rope = m->at<float2>(W.rope);
   a.x = m->at<float>(W.x); a.q = m->at<float>(W.q); a.o = m->at<float>(W.o); a.act = m->at<float>(W.act);
@@ -342,7 +370,7 @@ int launch_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream
   a.layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
   a.x_in = xin; a.x_out = xout;
   void* args[] = {&a};
-  LF_HIP(hipLaunchCooperativeKernel(m->step_fn, dim3(m->step_grid), dim3(lf::kStepThreads), args, 0, st));
+  LF_HIP(hipLaunchCooperativeKernel(m->step_fn, dim3(lf::kSGrid), dim3(lf::kSThreads), args, m->step_lds, st));
   return LF_OK;
 }
 
@@ -619,28 +647,48 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, nctr);
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.best), 0u, 2);
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar), 0u, 4);
-  // Per-layer pointer table of the persistent step kernel.
-  std::vector<lf::LayerW> table(D.L);
-  for (int l = 0; l < D.L; ++l) {
-    const AttnPlan P = attn_plan(*cfg, l);
-    table[l] = {m->at<half_t>(W.wqkv[l]), m->at<half_t>(W.wo[l]), m->at<half_t>(W.wgu[l]), m->at<half_t>(W.wd[l]),
-                m->at<half_t>(W.g1[l]), m->at<half_t>(W.g2[l]), cfg->window[l], P.S, P.chunk};
+  // Stream-order copies of the repacked GEMV weights, and the tables of the
+  // stream step kernel (the host copies live until the stream is
+  // synchronized below).
+  const std::vector<StreamPhaseShape> sp = stream_shapes(D);
+  std::vector<lf::SPhase> phases(sp.size());
+  for (size_t i = 0; i < sp.size(); ++i) {
+    const int l = static_cast<int>(i / 4), kind = static_cast<int>(i % 4);
+    const size_t src_off = static_cast<int>(i) == 4 * D.L ? W.lm
+                           : kind == 0                     ? W.wqkv[l]
+                           : kind == 1                     ? W.wo[l]
+                           : kind == 2                     ? W.wgu[l]
+                                                           : W.wd[l];
+    lf::u32x4* dst = m->at<lf::u32x4>(W.sw[i]);
+    hipLaunchKernelGGL(lf::k_stream_repack, dim3(4096), dim3(256), 0, st, m->at<half_t>(src_off), sp[i].rows, sp[i].K,
+                       sp[i].kch, sp[i].rpw, dst, sp[i].bytes() / 16);
+    phases[i] = {dst, sp[i].rows, sp[i].K, sp[i].kch, sp[i].rpw};
   }
-  if (hipMemcpyAsync(m->at<lf::LayerW>(W.layers), table.data(), table.size() * sizeof(lf::LayerW),
+  std::vector<lf::SLayer> slayers(D.L);
+  for (int l = 0; l < D.L; ++l) {
+    const AttnPlan P = step_attn_plan(*cfg, l, lf::kSGrid);
+    slayers[l] = {m->at<half_t>(W.g1[l]), m->at<half_t>(W.g2[l]), cfg->window[l], P.S, P.chunk};
+  }
+  if (hipMemcpyAsync(m->at<lf::SPhase>(W.sphases), phases.data(), phases.size() * sizeof(lf::SPhase),
+                     hipMemcpyHostToDevice, st) ||
+      hipMemcpyAsync(m->at<lf::SLayer>(W.slayers), slayers.data(), slayers.size() * sizeof(lf::SLayer),
                      hipMemcpyHostToDevice, st))
-    return bail(fail(LF_EHIP, "layer table upload failed: %s", hipGetErrorString(hipGetLastError())));
-  // The persistent step kernel needs cooperative launch and one 512-thread
-  // workgroup resident per compute unit. Graph replay stays the default: it
-  // is the faster mode on MI355X at the shapes measured so far.
+    return bail(fail(LF_EHIP, "stream table upload failed: %s", hipGetErrorString(hipGetLastError())));
+  // The stream step kernel needs cooperative launch and kSGrid co-resident
+  // workgroups. Graph replay stays the default until it is measured faster.
   {
+    const StepVariant* v = find_step_kernel(D);
+    bool fits = v != nullptr;
+    for (const StreamPhaseShape& e : sp) fits = fits && lf::kSW * e.rpw <= lf::kSResMax && e.K <= lf::kSKMax;
     int dev = 0, coop = 0, ncu = 0, per_cu = 0;
-    const void* fn = find_step_kernel(D);
-    if (fn && hipGetDevice(&dev) == hipSuccess &&
+    if (fits && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, lf::kStepThreads, 0) == hipSuccess && per_cu >= 1) {
-      m->step_fn = fn;
-      m->step_grid = ncu;
+        hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, v->lds) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, lf::kSThreads, v->lds) == hipSuccess &&
+        per_cu * ncu >= lf::kSGrid) {
+      m->step_fn = v->fn;
+      m->step_lds = v->lds;
     }
     (void)hipGetLastError();
   }

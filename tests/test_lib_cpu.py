@@ -28,8 +28,21 @@ def test_library_exports_every_declared_symbol():
     assert sorted(C.EXPORTS) == declared
 
 
+def _stream_copy_bytes(cfg):
+    # the stream step kernel's copy of every GEMV matrix: rows dealt to
+    # 256 workgroups x 8 compute waves (padded to whole rows per wave), each
+    # row a whole number of 1-KB (512-element) slots
+    waves = 256 * 8
+    d, q = cfg.d_model, cfg.n_q_heads * cfg.head_dim
+    mats = [(cfg.qkv_rows, d), (d, q), (2 * cfg.ffn, d), (d, cfg.ffn)] * cfg.n_layers
+    if cfg.vocab:
+        mats.append((cfg.vocab, d))
+    return sum(-(-rows // waves) * -(-k // 512) * waves * 1024 for rows, k in mats)
+
+
 def test_sizes_of_the_workloads():
-    # workspace = weights (+ small activations); sequence buffer = caches + state
+    # workspace = weights twice (row-major and stream order) + small
+    # activations; sequence buffer = caches + state
     for cfg in (TINY, LAYER_FULL, FULL, LANE):
         c = C.make_config(cfg)
         ws, kv = C.lf_workspace_bytes(c), C.lf_kv_bytes(c)
@@ -38,7 +51,11 @@ def test_sizes_of_the_workloads():
     cache = 2 * 15 * 4096 * 16 * 128 * 2
     assert cache <= C.lf_kv_bytes(c) < cache + 4096 * 4 + 32000 * 4 + 4096
     weights = 2338451456 * 2
-    assert weights <= C.lf_workspace_bytes(c) < weights + 8 * 2 ** 20
+    stream = _stream_copy_bytes(FULL)
+    # = the weights without the embedding table and the norm gains, with the
+    # LM head's 32000 rows padded to 32768 (16 per wave); everything else divides
+    assert stream == weights - 32000 * 4096 * 2 - (2 * 15 + 1) * 4096 * 2 + 768 * 4096 * 2
+    assert weights + stream <= C.lf_workspace_bytes(c) < weights + stream + 8 * 2 ** 20
 
 
 @pytest.mark.parametrize("field,value,msg", [
