@@ -789,9 +789,10 @@ __global__ __launch_bounds__(kBlock) void k_repack(RepackArgs a) {
   for (int c = threadIdx.x; c < (a.K >> 3); c += kBlock) d[c] = s[c];
 }
 
-__global__ void k_fill_u32(unsigned* p, unsigned v, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+__global__ void k_fill_u32(unsigned* p, unsigned v, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
 }
 
 // Start a step with an explicit token, or set the length (d_token == null).

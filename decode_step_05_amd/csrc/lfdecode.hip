@@ -132,6 +132,8 @@ struct WsLayout {
   std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
   std::vector<size_t> sw;  // stream-order copies of the GEMV weights, per stream phase
   size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, bar, sphases, slayers, total;
+  // tagged exchange buffers of the stream step kernel (one zeroed region)
+  size_t xt, qt, kvt, ot, actt, partt, tagged_begin, tagged_end;
   int S_max;
 };
 
@@ -187,7 +189,16 @@ WsLayout ws_layout(const lf_config& c) {
   W.part_acc = take(static_cast<size_t>(D.hq) * W.S_max * D.hd * sizeof(float));
   W.best = take(sizeof(unsigned long long));
   W.counters = take((D.hkv + 4) * sizeof(unsigned));
-  W.bar = take(4 * sizeof(unsigned));
+  W.bar = take(8 * sizeof(unsigned));
+  const size_t tw = sizeof(unsigned long long);
+  W.tagged_begin = off;
+  W.xt = take(D.d * tw);
+  W.qt = take(D.qdim * tw);
+  W.kvt = take(static_cast<size_t>(2) * D.hkv * D.hd * tw);
+  W.ot = take(D.qdim * tw);
+  W.actt = take(D.ffn * tw);
+  W.partt = take(static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2) * tw);
+  W.tagged_end = off;
   const std::vector<StreamPhaseShape> sp = stream_shapes(D);
   for (const StreamPhaseShape& e : sp) W.sw.push_back(take(e.bytes()));
   W.sphases = take(sp.size() * sizeof(lf::SPhase));
@@ -353,16 +364,14 @@ int launch_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream
   a.layers = m->at<lf::SLayer>(W.slayers);
   a.n_ph = static_cast<int>(W.sw.size());
   a.L = D.L; a.d = D.d; a.qdim = D.qdim; a.ffn = D.ffn; a.vocab = D.V; a.hd = D.hd;
-  a.qpl = D.qpl; a.kpl = D.kpl; a.n_kv = D.hkv; a.max_ctx = D.ctx;
+  a.qpl = D.qpl; a.kpl = D.kpl; a.n_kv = D.hkv; a.max_ctx = D.ctx; a.S_max = W.S_max;
   a.eps = m->cfg.rms_eps;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
   a.embed = D.V ? m->at<half_t>(W.embed) : nullptr;
   a.gf = D.V ? m->at<half_t>(W.gf) : nullptr;
   a.rope = m->at<float2>(W.rope);
-  a.x = m->at<float>(W.x); a.q = m->at<float>(W.q); a.o = m->at<float>(W.o); a.act = m->at<float>(W.act);
-  a.part_ml = m->at<float2>(W.part_ml);
-  a.part_acc = m->at<float>(W.part_acc);
-  a.attn_counters = m->at<unsigned>(W.counters);
+  a.xt = m->at<lf::u64>(W.xt); a.qt = m->at<lf::u64>(W.qt); a.kvt = m->at<lf::u64>(W.kvt);
+  a.ot = m->at<lf::u64>(W.ot); a.actt = m->at<lf::u64>(W.actt); a.partt = m->at<lf::u64>(W.partt);
   a.best = m->at<unsigned long long>(W.best);
   a.bar = m->at<unsigned>(W.bar);
   a.state = kv->state(); a.tokens = kv->tokens(); a.logits = kv->logits();
@@ -644,9 +653,13 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   if (hipMemcpyAsync(m->at<float2>(W.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st))
     return bail(fail(LF_EHIP, "rope upload failed: %s", hipGetErrorString(hipGetLastError())));
   const int nctr = D.hkv + 4;
-  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, nctr);
-  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.best), 0u, 2);
-  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar), 0u, 4);
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, size_t(nctr));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.best), 0u, size_t(2));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar), 0u, size_t(8));
+  // stream kernel: tags start at zero, the launch epoch at 1 (tags of epoch e are >= 512 e)
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(256), dim3(256), 0, st, m->at<unsigned>(W.tagged_begin), 0u,
+                     (W.tagged_end - W.tagged_begin) / sizeof(unsigned));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar) + 3, 1u, size_t(1));
   // Stream-order copies of the repacked GEMV weights, and the tables of the
   // stream step kernel (the host copies live until the stream is
   // synchronized below).
