@@ -24,6 +24,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+# HBM bytes per gate/up GEMV launch measured with rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (a 512 MiB device copy reads as 0.5x FETCH_SIZE, writes as 1.0x
+# WRITE_SIZE; both factors applied), for the GEMV kernel sources whose sha256
+# is given: reported only while the sources are unchanged.
+GATE_UP_TRAFFIC = {"bytes": 118265092,
+                   "sources": ("decode_step_05_amd/csrc/lf_device.h", "decode_step_05_amd/csrc/lf_kernels.h"),
+                   "sha256": "44513e22b0c636cc0b66e3f4f9c4d89e98515c2e86f646189732e39d68e93147"}
+
+
+def measured_traffic(entry):
+    import hashlib
+    h = hashlib.sha256()
+    for path in entry["sources"]:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return entry["bytes"] if h.hexdigest() == entry["sha256"] else None
 METRIC = "batch-1 decode tokens/s and achieved HBM GB/s (% of peak) at ctx 4096"
 
 
@@ -106,6 +123,12 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps of the CPU baseline (0 = skip)")
     ap.add_argument("--mode", choices=["default", "persistent", "graph", "eager"], default="default",
                     help="step launch mode (default: the library's choice)")
+    ap.add_argument("--synthetic-cache", action="store_true",
+                    help="load a seeded random KV cache of the prompt's length instead of prefilling it "
+                         "(same kernels and bytes per step; for hardware-counter runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only copy a MB-MiB device buffer three times and exit (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this decode path runs on one GPU; --gpus must be 1 "
@@ -114,9 +137,18 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     from decode_step_05_amd import Decoder
     from decode_step_05_amd import lfdecode as C
-    from synth import WORKLOADS, make_prompt, make_weights
+    from synth import WORKLOADS, make_kv, make_prompt, make_weights
 
     wl = WORKLOADS["ctx4096"]
     cfg = wl.cfg
@@ -142,10 +174,16 @@ def main():
     prompt = make_prompt(cfg, P, seed=wl.prompt_seed)
     torch.cuda.synchronize()
     t = time.perf_counter()
-    seq.prefill(prompt)
+    if args.synthetic_cache:
+        K_, V_ = make_kv(cfg, P, seed=wl.data_seed)
+        seq.load_cache(K_, V_)
+        seq.set_len(P)
+        del K_, V_
+    else:
+        seq.prefill(prompt)
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t
-    log(f"[bench] prefill {P} tokens in {prefill_s:.2f}s")
+    log(f"[bench] {'synthetic cache' if args.synthetic_cache else 'prefill'} {P} positions in {prefill_s:.2f}s")
 
     # warm-up, then rewind so the timed steps replay positions P .. P+K-1
     if args.warmup:
@@ -168,7 +206,9 @@ def main():
     last_bytes = step_bytes(cfg, cfg.max_ctx - 1)
     log(f"[bench] {K} steps: {ms:.2f} ms (wall {wall * 1e3:.2f} ms) -> {tok_s:.1f} tok/s, {gbs:.0f} GB/s")
 
-    # per-kernel event timing (kernels launched one by one) for the roofline
+    # per-kernel timing: eager launches of one step (launch gaps included), and
+    # for the roofline the gate/up GEMVs launched back to back in a graph, as
+    # the timed graph replays run them (the kernel duration rocprofv3 reports)
     seq.set_len(P)
     torch.cuda.synchronize()
     per_kind = {}
@@ -176,9 +216,13 @@ def main():
         for kind, kms in C.lf_step_kernel_times(dec.handle, seq.handle):
             per_kind.setdefault(kind, []).append(kms)
     avg = {k: float(np.mean(v)) for k, v in per_kind.items()}
-    gu_ms = avg["gate_up"]
+    log("[bench] eager kernel averages (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in avg.items()))
+    seq.set_len(P)
+    # all 15 layers' launches in turn: each streams its own 117 MB from HBM
+    # (one layer's weights repeated would stay in the 256 MB last-level cache)
+    gu_ms = C.lf_kernel_time(dec.handle, seq.handle, "gate_up", -1, reps=1, iters=16)
     gu_gbs = gate_up_bytes(cfg) / (gu_ms / 1e3) / 1e9
-    log("[bench] kernel averages (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in avg.items()))
+    log(f"[bench] gate_up back to back: {gu_ms * 1e3:.2f} us per launch, {gu_gbs:.0f} GB/s")
 
     # fixed context 4096: repeat the step at p = 4095
     n_fixed = 64
@@ -228,10 +272,10 @@ def main():
                           "roofline_tok_s": round(PEAK_HBM_GBS * 1e9 / last_bytes, 1),
                           "note": "each step preceded by a length reset; includes that launch"},
         "prefill_s": round(prefill_s, 2),
-        "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "roofline": {"bound": "hbm", "kernel": "gate_up GEMV (RMSNorm + SwiGLU fused), 14336x4096 fp16",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(GATE_UP_TRAFFIC),
                      "bytes_per_launch": gate_up_bytes(cfg), "avg_launch_us": round(gu_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }

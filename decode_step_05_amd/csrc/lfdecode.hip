@@ -385,21 +385,40 @@ int launch_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream
 
 // Optional per-kernel event brackets around each launch of enqueue_step.
 struct StepTimer {
-  hipEvent_t* ev;   // 2 per kernel
+  hipEvent_t* ev;   // 2 per kernel (null: no events)
   int32_t* kinds;
   int cap, n;
   hipError_t err = hipSuccess;
+  // only_kind >= 0: enqueue nothing but `reps` launches of that kernel of
+  // layer only_layer (of every layer, in order, if only_layer < 0)
+  int only_kind = -1, only_layer = -1, reps = 1;
   void before(hipStream_t st) {
-    if (n < cap && err == hipSuccess) err = hipEventRecord(ev[2 * n], st);
+    if (ev && n < cap && err == hipSuccess) err = hipEventRecord(ev[2 * n], st);
   }
   void after(hipStream_t st, int kind) {
-    if (n < cap && err == hipSuccess) {
+    if (ev && n < cap && err == hipSuccess) {
       err = hipEventRecord(ev[2 * n + 1], st);
       kinds[n] = kind;
     }
     ++n;
   }
 };
+
+// Launch one kernel of a step (kind, layer l) through `launch`, bracketed by
+// the timer's events, or as the timer's filter asks.
+template <class F>
+void emit_kernel(StepTimer* tm, hipStream_t st, int kind, int l, F&& launch) {
+  if (!tm) {
+    launch();
+  } else if (tm->only_kind >= 0) {
+    if (kind == tm->only_kind && (tm->only_layer < 0 || l == tm->only_layer))
+      for (int r = 0; r < tm->reps; ++r) launch();
+  } else {
+    tm->before(st);
+    launch();
+    tm->after(st, kind);
+  }
+}
 
 // Enqueue every kernel of one step. xin/xout: hidden mode input/output (null in token mode).
 int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st, StepTimer* tm = nullptr) {
@@ -441,9 +460,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.q = m->at<float>(W.q);
     a.kc = kv->kc() + l * layer_cache;
     a.vc = kv->vc() + l * layer_cache;
-    if (tm) tm->before(st);
-    launch_gemv<lf::kEpiQKV>(a, st);
-    if (tm) tm->after(st, LF_KERNEL_QKV);
+    emit_kernel(tm, st, LF_KERNEL_QKV, l, [&] { launch_gemv<lf::kEpiQKV>(a, st); });
 
     // attention over the visible keys, split over key ranges, merged in-kernel
     const AttnPlan P = attn_plan(c, l);
@@ -462,9 +479,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     t.chunk = P.chunk;
     t.kpl = D.kpl;
     t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
-    if (tm) tm->before(st);
-    launch_attn(t, D.hd, D.G, D.hkv, st);
-    if (tm) tm->after(st, LF_KERNEL_ATTN);
+    emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, st); });
 
     // O projection + residual
     a = base;
@@ -474,9 +489,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.in_kind = lf::kInF32;
     a.x = m->at<float>(W.o);
     a.y = resid;
-    if (tm) tm->before(st);
-    launch_gemv<lf::kEpiResid>(a, st);
-    if (tm) tm->after(st, LF_KERNEL_O);
+    emit_kernel(tm, st, LF_KERNEL_O, l, [&] { launch_gemv<lf::kEpiResid>(a, st); });
 
     // RMSNorm + gate/up + SwiGLU
     a = base;
@@ -487,9 +500,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.x = resid;
     a.gain = m->at<half_t>(W.g2[l]);
     a.y = m->at<float>(W.act);
-    if (tm) tm->before(st);
-    launch_gemv<lf::kEpiSwiGLU>(a, st);
-    if (tm) tm->after(st, LF_KERNEL_GATE_UP);
+    emit_kernel(tm, st, LF_KERNEL_GATE_UP, l, [&] { launch_gemv<lf::kEpiSwiGLU>(a, st); });
 
     // down projection + residual (the last layer ends the step in hidden mode)
     a = base;
@@ -500,9 +511,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.x = m->at<float>(W.act);
     a.y = resid;
     if (hidden && l == D.L - 1) a.counter = counters + D.hkv;
-    if (tm) tm->before(st);
-    launch_gemv<lf::kEpiResid>(a, st);
-    if (tm) tm->after(st, LF_KERNEL_DOWN);
+    emit_kernel(tm, st, LF_KERNEL_DOWN, l, [&] { launch_gemv<lf::kEpiResid>(a, st); });
   }
   if (!hidden) {
     // final RMSNorm + LM head + greedy argmax; ends the step
@@ -516,9 +525,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.y = kv->logits();
     a.counter = counters + D.hkv;
     a.best = m->at<unsigned long long>(W.best);
-    if (tm) tm->before(st);
-    launch_gemv<lf::kEpiLogits>(a, st);
-    if (tm) tm->after(st, LF_KERNEL_LM_HEAD);
+    emit_kernel(tm, st, LF_KERNEL_LM_HEAD, D.L, [&] { launch_gemv<lf::kEpiLogits>(a, st); });
   }
   LF_HIP(hipPeekAtLastError());
   if (tm && tm->err != hipSuccess) return fail(LF_EHIP, "hipEventRecord: %s", hipGetErrorString(tm->err));
@@ -910,10 +917,57 @@ int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const f
   StepTimer tm{m->events.data(), kinds, cap, 0};
   const int rc = enqueue_step(m, kv, hidden ? d_x_in : nullptr, hidden ? d_x_out : nullptr, st, &tm);
   if (rc) return rc;
-  kv->len += 1;
   LF_HIP(hipStreamSynchronize(st));
+  kv->len += 1;
   for (int i = 0; i < tm.n; ++i) LF_HIP(hipEventElapsedTime(&ms[i], m->events[2 * i], m->events[2 * i + 1]));
   *n_out = tm.n;
+  return LF_OK;
+}
+
+int lf_kernel_time(lf_model* m, lf_kv* kv, int32_t kind, int32_t layer, int32_t reps, int32_t iters,
+                   const float* d_x_in, float* d_x_out, float* avg_ms, void* stream) {
+  if (!m || !kv || !avg_ms) return fail(LF_EINVAL, "null argument");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  const bool hidden = m->D.V == 0;
+  if (kind < LF_KERNEL_QKV || kind > LF_KERNEL_DOWN) return fail(LF_EINVAL, "kind %d cannot be repeated", kind);
+  if (layer < -1 || layer >= m->D.L) return fail(LF_EINVAL, "layer %d out of range", layer);
+  if (hidden && kind == LF_KERNEL_DOWN && (layer == m->D.L - 1 || layer < 0))
+    return fail(LF_EINVAL, "the last down projection ends the step in hidden mode");
+  if (hidden && (!d_x_in || !d_x_out)) return fail(LF_EINVAL, "hidden mode needs d_x_in and d_x_out");
+  if (reps < 1 || reps > 256 || iters < 1) return fail(LF_EINVAL, "reps must be in [1, 256], iters >= 1");
+  if (kv->len >= m->D.ctx) return fail(LF_ERANGE, "sequence is full (%d positions)", m->D.ctx);
+  while (m->events.size() < 2) {
+    hipEvent_t e;
+    LF_HIP(hipEventCreate(&e));
+    m->events.push_back(e);
+  }
+  StepTimer tm{nullptr, nullptr, 0, 0};
+  tm.only_kind = kind;
+  tm.only_layer = layer;
+  tm.reps = reps;
+  hipStream_t cs = m->capture_stream, st = static_cast<hipStream_t>(stream);
+  LF_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+  const int rc = enqueue_step(m, kv, hidden ? d_x_in : nullptr, hidden ? d_x_out : nullptr, cs, &tm);
+  hipGraph_t graph = nullptr;
+  const hipError_t e = hipStreamEndCapture(cs, &graph);
+  if (rc != LF_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc != LF_OK ? rc : fail(LF_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiateWithFlags(&exec, graph, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) return fail(LF_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(ei));
+  hipError_t er = hipGraphLaunch(exec, st);  // warm-up
+  if (er == hipSuccess) er = hipEventRecord(m->events[0], st);
+  for (int i = 0; i < iters && er == hipSuccess; ++i) er = hipGraphLaunch(exec, st);
+  if (er == hipSuccess) er = hipEventRecord(m->events[1], st);
+  if (er == hipSuccess) er = hipStreamSynchronize(st);
+  float ms = 0.f;
+  if (er == hipSuccess) er = hipEventElapsedTime(&ms, m->events[0], m->events[1]);
+  (void)hipGraphExecDestroy(exec);
+  if (er != hipSuccess) return fail(LF_EHIP, "kernel timing: %s", hipGetErrorString(er));
+  *avg_ms = ms / (static_cast<float>(iters) * reps * (layer < 0 ? m->D.L : 1));
   return LF_OK;
 }
 

@@ -23,7 +23,7 @@ EXPORTS = (
     "lf_model_set_mode", "lf_model_mode",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
-    "lf_step_kernel_times", "lf_last_error",
+    "lf_step_kernel_times", "lf_kernel_time", "lf_last_error",
 )
 
 KERNEL_KINDS = ("qkv", "attn", "o", "gate_up", "down", "lm_head")
@@ -81,6 +81,7 @@ def load():
         "lf_kv_status": (c_int, [P, POINTER(c_int32), P]),
         "lf_step_kernel_times": (c_int, [P, P, P, P, P, POINTER(c_float), POINTER(c_int32), c_int32,
                                          POINTER(c_int32), P]),
+        "lf_kernel_time": (c_int, [P, P, c_int32, c_int32, c_int32, c_int32, P, P, POINTER(c_float), P]),
         "lf_last_error": (c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -248,3 +249,13 @@ def lf_step_kernel_times(model, kv, token=None, x_in=None, x_out=None, cap=512, 
     _check(load().lf_step_kernel_times(model, kv, _ptr(token), _ptr(x_in), _ptr(x_out), ms, kinds, cap,
                                        ctypes.byref(n), _stream(stream)))
     return [(KERNEL_KINDS[kinds[i]], float(ms[i])) for i in range(n.value)]
+
+
+def lf_kernel_time(model, kv, kind, layer, reps=16, iters=8, x_in=None, x_out=None, stream=None):
+    """Milliseconds per launch of one per-phase kernel (kind name or LF_KERNEL_*) of
+    layer `layer`, launched back to back in a graph."""
+    k = KERNEL_KINDS.index(kind) if isinstance(kind, str) else int(kind)
+    ms = c_float()
+    _check(load().lf_kernel_time(model, kv, k, layer, reps, iters, _ptr(x_in), _ptr(x_out), ctypes.byref(ms),
+                                 _stream(stream)))
+    return float(ms.value)

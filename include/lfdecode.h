@@ -94,7 +94,9 @@ typedef struct lf_weight_ptrs {
 typedef struct lf_model lf_model;
 typedef struct lf_kv lf_kv;
 
-/* Bytes of device workspace a model of this shape needs (0 if the config is invalid). */
+/* Bytes of device workspace a model of this shape needs (0 if the config is
+ * invalid): the weights twice (row-major for the per-phase kernels, stream
+ * order for the persistent kernel) plus activations and exchange buffers. */
 size_t lf_workspace_bytes(const lf_config* cfg);
 
 /* Bytes of the per-sequence device buffer (state, token history, logits, K and V caches). */
@@ -114,11 +116,13 @@ void lf_model_free(lf_model* m);
 
 /*
  * How a step is launched. All modes compute the same function.
- *   LF_MODE_PERSISTENT: one cooperative launch per step; the workgroups run
- *     the phases (QKV, attention, O, gate/up, down, LM head) separated by
- *     grid barriers and prefetch each phase's weights before its barrier.
- *     Available when the shape has a compiled step kernel and the device
- *     supports cooperative launch.
+ *   LF_MODE_PERSISTENT: one cooperative launch of 256 workgroups per step;
+ *     the workgroups run the phases (QKV, attention, O, gate/up, down, LM
+ *     head) streaming every weight through LDS, and pass data between phases
+ *     as tagged words instead of grid barriers. Available when the shape has
+ *     a compiled step kernel and the device can hold 256 such workgroups at
+ *     once (MI355X: one per compute unit). The workspace holds a second,
+ *     stream-ordered copy of the weights for it.
  *   LF_MODE_GRAPH (default): one kernel per phase, captured per (sequence,
  *     in/out pointers) into a hipGraph on first use and replayed.
  *   LF_MODE_EAGER: one kernel per phase, launched one by one.
@@ -198,17 +202,18 @@ int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_ar
  * Read back (synchronously on stream) the device-side sequence state:
  * out[0] = length, out[1] = last argmax, out[2] = flags: bit 0 set if a token
  * id outside [0, vocab) was clamped since lf_kv_alloc; bit 1 set if a
- * persistent step gave up waiting at a grid barrier (its results are invalid
- * and later persistent steps of the model do nothing).
+ * persistent step gave up waiting for another workgroup's data (its results
+ * are invalid and later persistent steps of the model do nothing).
  */
 int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
 
 /*
  * Profiling aid (not needed to decode): run one step exactly as lf_decode_step
  * (token mode; d_token may be NULL) or lf_decode_step_hidden (hidden mode)
- * would, but with the kernels launched one by one, each bracketed by two HIP
- * events on `stream`; wait for it and write, in launch order, each kernel's
- * elapsed milliseconds to ms[] and its kind (LF_KERNEL_*) to kinds[].
+ * would, but with the per-phase kernels launched one by one, each bracketed
+ * by two HIP events on `stream`; wait for it and write, in launch order, each
+ * kernel's elapsed milliseconds (launch gaps included) to ms[] and its kind
+ * (LF_KERNEL_*) to kinds[].
  * cap must be at least 5 * n_layers (+ 1 in token mode); *n_out receives the
  * kernel count. Appends one position like the step calls.
  */
@@ -220,6 +225,22 @@ int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
 #define LF_KERNEL_LM_HEAD 5  /* RMSNorm + LM head + greedy argmax */
 int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const float* d_x_in, float* d_x_out,
                          float* ms, int32_t* kinds, int32_t cap, int32_t* n_out, void* stream);
+
+/*
+ * Profiling aid: the average duration of one per-phase kernel of the step's
+ * graph, launched back to back as graph replays run it. Captures `reps`
+ * launches (1..256) of the kernel of kind `kind` (LF_KERNEL_QKV .. DOWN; not
+ * the LM head, nor in hidden mode the last layer's down projection, which end
+ * the step) of layer `layer` (layer -1: of every layer in order, so that each
+ * launch streams other weights, as in a step) with the arguments of the
+ * sequence's next step, replays that graph `iters` times between two events
+ * on `stream`, waits, and writes the time per launch in milliseconds to
+ * *avg_ms. The sequence's
+ * position does not change, but its activations and the KV entry at that
+ * position are left unspecified (the next step recomputes them).
+ */
+int lf_kernel_time(lf_model* m, lf_kv* kv, int32_t kind, int32_t layer, int32_t reps, int32_t iters,
+                   const float* d_x_in, float* d_x_out, float* avg_ms, void* stream);
 
 /* Text of the calling thread's last error ("" if none). */
 const char* lf_last_error(void);

@@ -132,6 +132,32 @@ def test_rewind_reproduces_logits():
     torch.cuda.synchronize()
 
 
+def test_kernel_timing_leaves_the_sequence_intact():
+    # lf_kernel_time repeats single kernels of the next step; the step that
+    # follows must still give the same logits, bit for bit
+    cfg = TINY
+    say(f"[parity] kernel timing cfg={cfg.name}")
+    from decode_step_05_amd import lfdecode as C
+    w = make_weights(cfg, seed=0)
+    dec = _dec(cfg, w)
+    seq = dec.sequence()
+    seq.prefill(make_prompt(cfg, 70, seed=1))
+    seq.step()
+    want = seq.logits()[0].cpu().numpy()
+    seq.set_len(70)
+    for kind in ("qkv", "attn", "o", "gate_up", "down"):
+        for l in range(cfg.n_layers):
+            ms = C.lf_kernel_time(dec.handle, seq.handle, kind, l, reps=4, iters=2)
+            assert 0.0 < ms < 10.0, (kind, l, ms)
+    for kind in ("qkv", "attn", "o", "gate_up", "down"):
+        assert 0.0 < C.lf_kernel_time(dec.handle, seq.handle, kind, -1, reps=2, iters=2) < 10.0
+    assert seq.status()[0] == 70
+    seq.step()
+    assert np.array_equal(seq.logits()[0].cpu().numpy(), want)
+    with pytest.raises(C.LfError):
+        C.lf_kernel_time(dec.handle, seq.handle, "lm_head", 0)
+
+
 def test_first_position_and_context_limit():
     # ctx = 1 (attention over a single key) and the exact max_ctx boundary
     cfg = TINY.replace(max_ctx=70, name="tiny70")
