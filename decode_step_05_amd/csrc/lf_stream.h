@@ -605,22 +605,25 @@ __device__ __forceinline__ void s_attn_combine(SSmem<HD, G>& sm, int tid) {
   if (d == 0) sm.comb_ml[g] = make_float2(M, L);
 }
 
-// Control wave of split si of kv head kvh: wait for the S partial states of
-// the kv head's G query heads and store this split's share of the merged
-// attention output (outputs [si*per, si*per + per) of the G*HD, per even).
-// In rounds of at most 64 output pairs: lane (pair pi, group sg) folds splits
-// sg, sg + NG, ... of pair pi into a running (max, denominator, outputs)
-// state, and the NG groups are folded through LDS. Returns false if the
-// launch was aborted.
+// One wave of split si of kv head kvh: wait for the S partial states of the
+// kv head's G query heads (part: [n_kv * G][S_max][HD + 2] tagged words:
+// outputs, running max in log2 units, denominator) and store this split's
+// share of the merged attention output to out ([n_kv * G * HD] tagged words;
+// outputs [si*per, si*per + per) of the G*HD, per even). In rounds of at most
+// 64 output pairs: lane (pair pi, group sg) folds splits sg, sg + NG, ... of
+// pair pi into a running (max, denominator, outputs) state, and the NG groups
+// are folded through mrg (64 words of LDS, this wave's own). Returns false if
+// the launch was aborted.
 template <int HD, int G>
-__device__ __forceinline__ bool s_attn_merge(const StreamArgs& s, SSmem<HD, G>& sm, int kvh, int si, int S,
-                                            unsigned tag_part, unsigned tag_att, SPoll& poll, int lane) {
+__device__ __forceinline__ bool attn_merge_share(const u64* part, u64* out, int n_kv, int S_max, f32x4* mrg, int kvh,
+                                                 int si, int S, unsigned tag_part, unsigned tag_att, SPoll& poll,
+                                                 int lane) {
   constexpr int ST = HD + 2;  // tagged words per (head, split)
   constexpr int NE = G * HD;  // outputs of the kv head's query heads
   const int per = ((NE + S - 1) / S + 1) & ~1;
   const int e_begin = si * per, e_end = min(NE, e_begin + per);
-  const rsrc_t r = rsrc_of(s.partt, s.n_kv * G * s.S_max * ST * 8);
-  const rsrc_t ro = rsrc_of(s.ot, s.n_kv * G * HD * 8);
+  const rsrc_t r = rsrc_of(part, n_kv * G * S_max * ST * 8);
+  const rsrc_t ro = rsrc_of(out, n_kv * G * HD * 8);
   constexpr int MAXS = 8;  // splits per lane per batch of loads
   for (int e0 = e_begin; e0 < e_end; e0 += 2 * kWave) {
     const int P = min(kWave, (e_end - e0) / 2);  // output pairs of this round
@@ -629,7 +632,7 @@ __device__ __forceinline__ bool s_attn_merge(const StreamArgs& s, SSmem<HD, G>& 
     const bool active = sg < NG;
     const int e = e0 + 2 * pi;
     const int head = kvh * G + e / HD, d = e % HD;
-    const int va_off = (head * s.S_max * ST + d) * 8, vm_off = (head * s.S_max * ST + HD) * 8;
+    const int va_off = (head * S_max * ST + d) * 8, vm_off = (head * S_max * ST + HD) * 8;
     float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
     for (int t0 = sg; t0 < S; t0 += NG * MAXS) {
       u32x4 va[MAXS], vm[MAXS];
@@ -637,9 +640,13 @@ __device__ __forceinline__ bool s_attn_merge(const StreamArgs& s, SSmem<HD, G>& 
 #pragma unroll
       for (int u = 0; u < MAXS; ++u) {
         const int t = t0 + u * NG;
-        va[u] = ld_t2(r, va_off, t * ST * 8);
-        vm[u] = ld_t2(r, vm_off, t * ST * 8);
-        if (active && t < S && (stale2(va[u], tag_part) || stale2(vm[u], tag_part))) stale |= 1u << u;
+        const bool want = active && t < S;
+        // per-lane offsets in the vector operand; splits past S read past the
+        // descriptor's range, which returns zero without a memory access
+        const int so = want ? t * ST * 8 : 0x40000000;
+        va[u] = ld_t2(r, va_off + so, 0);
+        vm[u] = ld_t2(r, vm_off + so, 0);
+        if (want && (stale2(va[u], tag_part) || stale2(vm[u], tag_part))) stale |= 1u << u;
       }
       while (__any(stale != 0)) {
         if (!poll.next(lane)) return false;
@@ -647,8 +654,8 @@ __device__ __forceinline__ bool s_attn_merge(const StreamArgs& s, SSmem<HD, G>& 
         for (int u = 0; u < MAXS; ++u)
           if (stale & (1u << u)) {
             const int t = t0 + u * NG;
-            va[u] = ld_t2(r, va_off, t * ST * 8);
-            vm[u] = ld_t2(r, vm_off, t * ST * 8);
+            va[u] = ld_t2(r, va_off + t * ST * 8, 0);
+            vm[u] = ld_t2(r, vm_off + t * ST * 8, 0);
             if (!stale2(va[u], tag_part) && !stale2(vm[u], tag_part)) stale &= ~(1u << u);
           }
       }
@@ -665,12 +672,12 @@ __device__ __forceinline__ bool s_attn_merge(const StreamArgs& s, SSmem<HD, G>& 
       }
     }
     // fold the lane groups (LDS written and read by this wave only)
-    sm.mrg[lane] = f32x4{M, L, A0, A1};
+    mrg[lane] = f32x4{M, L, A0, A1};
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     if (lane < P) {
       for (int g = 1; g < NG; ++g) {
-        const f32x4 o = sm.mrg[g * P + lane];
+        const f32x4 o = mrg[g * P + lane];
         if (o[0] == -INFINITY) continue;
         const float Mn = fmaxf(M, o[0]);
         const float fo = exp2f(M - Mn), fn = exp2f(o[0] - Mn);
@@ -917,7 +924,8 @@ __device__ __forceinline__ void s_ctrl_main(const SCtx<HD, G>& c) {
         put_t(rpart, ml + 1, sm.comb_ml[lane].y, tp);
       }
       // every split merges its share of the outputs (an abort shows up at the next wait)
-      s_attn_merge<HD, G>(s, sm, kvh, si, t.S, tp, stag(epoch, l, kTAtt), poll, lane);
+      attn_merge_share<HD, G>(s.partt, s.ot, s.n_kv, s.S_max, sm.mrg, kvh, si, t.S, tp, stag(epoch, l, kTAtt), poll,
+                              lane);
     }
     alive = stage(4 * l + 1, kSO, l);
     if (alive) epilogue(4 * l + 1, kSO, l);
