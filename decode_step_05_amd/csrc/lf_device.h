@@ -28,6 +28,15 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Read a value of a table that no one writes during the launch through the
+// constant address space: a wave-uniform address then gives scalar loads,
+// which (unlike vector loads, retired in issue order) do not wait behind the
+// wave's weight loads.
+template <class T>
+__device__ __forceinline__ T cload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 // acc + sum_i w[i] * x[i] over 8 fp16 weights and 8 fp32 inputs.
 __device__ __forceinline__ float dot8(u32x4 w, f32x4 x0, f32x4 x1, float acc) {
   const h8 h = __builtin_bit_cast(h8, w);

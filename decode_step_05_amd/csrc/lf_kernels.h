@@ -120,6 +120,11 @@ __device__ __forceinline__ int argmax_index(unsigned long long key) {
 
 // ------------------------------------------------------------------ GEMV
 
+// Input of a GEMV: an fp32 vector, the same with RMSNorm, or RMSNorm of an
+// embedding row. A compile-time parameter of the kernels: with one staging
+// path per kernel, the wait for the staged input counts only the loads
+// issued before it (a runtime choice between paths that issue it before and
+// after the weights makes the compiler wait for every load at their join).
 enum InKind : int { kInF32 = 0, kInNormF32 = 1, kInNormEmbed = 2 };
 enum Epi : int { kEpiQKV = 0, kEpiSwiGLU = 1, kEpiResid = 2, kEpiLogits = 3 };
 
@@ -127,7 +132,7 @@ struct GemvArgs {
   const half_t* W;        // [rows, K] (QKV and gate/up repacked so that epilogue pairs are adjacent rows)
   int rows, K;
   // input vector
-  int in_kind;
+  int in_kind;            // InKind; selects the kernel variant
   const float* x;         // fp32 source (kInF32, kInNormF32)
   const half_t* emb;      // embedding table [vocab, K] (kInNormEmbed)
   const half_t* gain;     // RMSNorm gain [K]
@@ -162,12 +167,12 @@ struct Stage {
 
 // Issue the loads of the input vector (length K <= KMAX) and of the RMSNorm
 // gains. COH: read the source with device-scope loads (written in this launch).
-template <int THREADS, int KMAX, bool COH>
+template <int THREADS, int KMAX, bool COH, int IN>
 __device__ __forceinline__ void stage_load(Stage<THREADS, KMAX>& st, const GemvArgs& a, int p) {
   constexpr int NV = Stage<THREADS, KMAX>::NV;
   const int tid = threadIdx.x, K = a.K;
-  const bool norm = a.in_kind != kInF32;
-  if (a.in_kind == kInNormEmbed) {
+  constexpr bool norm = IN != kInF32;
+  if constexpr (IN == kInNormEmbed) {
     int tok = a.tokens[p];
     if (tok < 0 || tok >= a.vocab) {
       tok = tok < 0 ? 0 : a.vocab - 1;
@@ -215,14 +220,14 @@ __device__ __forceinline__ void stage_load(Stage<THREADS, KMAX>& st, const GemvA
 // of every 8-element chunk q in the 16-byte word xs[h*K/8 + q]; a wave reading
 // chunks q = lane + 64c touches consecutive 16-byte words: one ds_read_b128
 // per plane, free of bank conflicts.
-template <int THREADS, int KMAX>
+template <int THREADS, int KMAX, int IN>
 __device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, const GemvArgs& a, f32x4* xs, float* red) {
   constexpr int NW = THREADS / kWave;
   constexpr int NV = Stage<THREADS, KMAX>::NV;
   const int tid = threadIdx.x, K = a.K;
   const int per = (K + gridDim.x - 1) / gridDim.x;
   const int s0 = blockIdx.x * per, s1 = min(s0 + per, K);
-  const bool norm = a.in_kind != kInF32;
+  constexpr bool norm = IN != kInF32;
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -239,7 +244,7 @@ __device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, cons
   if (norm) {
     ss = wave_total(ss);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
-    __syncthreads();
+    lds_barrier();  // not __syncthreads: its fence would wait for the weight loads in flight
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += red[w];
@@ -260,7 +265,7 @@ __device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, cons
     xs[q] = o0;
     xs[(K >> 3) + q] = o1;
   }
-  __syncthreads();
+  lds_barrier();  // the weight loads stay in flight; each group is waited for where it is reduced
 }
 
 template <int NR, int KCH>
@@ -306,7 +311,9 @@ __device__ __forceinline__ void qkv_put(const QkvOut& a, int r, float y0, float 
   const int u = r / a.hd, c = (r % a.hd) >> 1;
   const int ln = u / upl, j = u % upl;
   if (j < a.qpl + a.kpl) {  // rotary embedding on q and k
-    const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
+    // scalar load (one lane runs this; the row, hence the index, is the wave's)
+    const int ri = __builtin_amdgcn_readfirstlane(p * half_hd + c);
+    const float2 cs = __builtin_bit_cast(float2, cload(reinterpret_cast<const unsigned long long*>(a.rope + ri)));
     const float t0 = y0 * cs.x - y1 * cs.y;
     const float t1 = y0 * cs.y + y1 * cs.x;
     y0 = t0;
@@ -325,11 +332,20 @@ __device__ __forceinline__ void qkv_put(const QkvOut& a, int r, float y0, float 
   }
 }
 
-// Reduce rows [r, r+NR) against xs and run the epilogue (lane 0 stores).
-// FULL: K is exactly 512*KCH, so every chunk of every lane is in range.
+// This lane's chunks of the staged input in registers (zero past K): read
+// from LDS once per wave instead of once per row group, for K up to 4096.
+template <int KCH>
+struct XRegs {
+  static constexpr bool on = KCH <= 8;
+  f32x4 x[2][on ? KCH : 1];
+};
+
+// Reduce rows [r, r+NR) against the input (xr if XRegs<KCH>::on, else xs in
+// LDS) and run the epilogue (lane 0 stores). FULL: K is exactly 512*KCH, so
+// every chunk of every lane is in range.
 template <int EPI, int NR, int KCH, bool FULL>
-__device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KCH>& b, const f32x4* xs, int r, int lane,
-                                            int p, float& bv, int& bi) {
+__device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KCH>& b, const f32x4* xs,
+                                            const XRegs<KCH>& xr, int r, int lane, int p, float& bv, int& bi) {
   const int K8 = a.K >> 3;
   const f32x4* xs_hi = xs + K8;
   float acc[NR][2];
@@ -338,9 +354,15 @@ __device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KC
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
     const int ch = lane + kWave * c;
-    if (FULL || ch < K8) {
-      const f32x4 x0 = xs[ch];
-      const f32x4 x1 = xs_hi[ch];
+    if (XRegs<KCH>::on || FULL || ch < K8) {
+      f32x4 x0, x1;
+      if constexpr (XRegs<KCH>::on) {
+        x0 = xr.x[0][c];
+        x1 = xr.x[1][c];
+      } else {
+        x0 = xs[ch];
+        x1 = xs_hi[ch];
+      }
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const h8 h = __builtin_bit_cast(h8, b.w[i][c]);
@@ -389,7 +411,7 @@ __device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KC
 // (the next group's loads stay in flight while this one is reduced).
 // Must be called by every thread of the workgroup (the input stage has barriers).
 // Returns false (in every thread) if the sequence is full and nothing was done.
-template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH>
+template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH, int IN>
 __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* red, int gw, int TW, int& p, float& bv,
                                          int& bi) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -401,29 +423,42 @@ __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* re
   Stage<THREADS, KMAX> st;
   // Issue order: input vector, then weights (loads retire in issue order).
   // The embedding row needs the position first; that is one kernel per step.
-  const bool embed = a.in_kind == kInNormEmbed;
-  if (!embed) stage_load<THREADS, KMAX, COH>(st, a, 0);
+  // (Staging the input before requesting any weight was measured slower:
+  // HBM idles for the input's round trip at every launch.)
+  constexpr bool embed = IN == kInNormEmbed;
+  if constexpr (!embed) stage_load<THREADS, KMAX, COH, IN>(st, a, 0);
   issue_rows<NR, KCH>(buf[0], a.W, min(gw, ng - 1) * NR, a.rows, a.K, lane, res);
   if (GPW > 1) issue_rows<NR, KCH>(buf[1], a.W, min(gw + TW, ng - 1) * NR, a.rows, a.K, lane, res);
   p = a.state[kLen];
   if (p >= a.max_ctx) return false;  // the host never launches a step on a full cache
-  if (embed) stage_load<THREADS, KMAX, COH>(st, a, p);
-  stage_store<THREADS, KMAX>(st, a, xs, red);
+  if constexpr (embed) stage_load<THREADS, KMAX, COH, IN>(st, a, p);
+  stage_store<THREADS, KMAX, IN>(st, a, xs, red);
+  XRegs<KCH> xr;
+  if constexpr (XRegs<KCH>::on) {
+    const int K8 = a.K >> 3;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = lane + kWave * c;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      xr.x[0][c] = ch < K8 ? xs[ch] : z;
+      xr.x[1][c] = ch < K8 ? xs[K8 + ch] : z;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
     const int g = gw + k * TW;
     if (g < ng) {
       if (full)
-        finish_rows<EPI, NR, KCH, true>(a, buf[k & 1], xs, g * NR, lane, p, bv, bi);
+        finish_rows<EPI, NR, KCH, true>(a, buf[k & 1], xs, xr, g * NR, lane, p, bv, bi);
       else
-        finish_rows<EPI, NR, KCH, false>(a, buf[k & 1], xs, g * NR, lane, p, bv, bi);
+        finish_rows<EPI, NR, KCH, false>(a, buf[k & 1], xs, xr, g * NR, lane, p, bv, bi);
     }
     if (k + 2 < GPW) issue_rows<NR, KCH>(buf[k & 1], a.W, min(gw + (k + 2) * TW, ng - 1) * NR, a.rows, a.K, lane, res);
   }
   return true;
 }
 
-template <int EPI, int NR, int KCH, int GPW, int WAVES>
+template <int EPI, int NR, int KCH, int GPW, int WAVES, int IN>
 __global__ __launch_bounds__(WAVES * kWave) void k_gemv(GemvArgs a) {
   constexpr int THREADS = WAVES * kWave;
   extern __shared__ f32x4 xs[];  // the input vector, 16-byte words (see stage_store)
@@ -435,7 +470,8 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv(GemvArgs a) {
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   int p;
-  if (!gemv_run<EPI, NR, KCH, GPW, THREADS, false>(a, xs, red, blockIdx.x * WAVES + wave, gridDim.x * WAVES, p, bv, bi))
+  if (!gemv_run<EPI, NR, KCH, GPW, THREADS, false, IN>(a, xs, red, blockIdx.x * WAVES + wave, gridDim.x * WAVES, p, bv,
+                                                         bi))
     return;
 
   if (a.counter == nullptr) return;

@@ -148,13 +148,6 @@ __device__ __forceinline__ void dma_1k(const u32x4* src, u32x4* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
 }
 
-// Read a value of a table that no one writes during the launch through the
-// constant address space: a wave-uniform address then gives scalar loads,
-// which (unlike vector loads) do not wait behind the weight stream.
-template <class T>
-__device__ __forceinline__ T cload(const T* p) {
-  return *(const __attribute__((address_space(4))) T*)(p);
-}
 __device__ __forceinline__ SPhase const_load(const SPhase* p) {
   SPhase r;
   r.w = cload(&p->w);

@@ -276,35 +276,57 @@ int gemv_kch(int K) {
   return 0;
 }
 
-template <int EPI, int KCH, int GPW, int WAVES>
-const void* gemv_fn() {
-  return reinterpret_cast<const void*>(&lf::k_gemv<EPI, gemv_nr<EPI>(), KCH, GPW, WAVES>);
-}
-
-template <int EPI, int KCH>
-const void* gemv_fn_k(int waves, int gpw) {
-  if (waves == 4 && gpw == 7) return gemv_fn<EPI, KCH, 7, 4>();
-  if (waves == 8 && gpw == 8) return gemv_fn<EPI, KCH, 8, 8>();
-  if (waves == 8 && gpw == 2) return gemv_fn<EPI, KCH, 2, 8>();
-  return gemv_fn<EPI, KCH, 1, 8>();
-}
-
+// The input kinds each epilogue is launched with: QKV takes the normed
+// residual (or, at layer 0, an embedding row), gate/up and the LM head the
+// normed residual, O and down a plain vector.
 template <int EPI>
-const void* gemv_kernel(int K, int waves, int gpw) {
+constexpr bool gemv_takes(int in) {
+  return EPI == lf::kEpiQKV ? in != lf::kInF32 : EPI == lf::kEpiResid ? in == lf::kInF32 : in == lf::kInNormF32;
+}
+
+template <int EPI, int KCH, int GPW, int WAVES, int IN>
+const void* gemv_fn() {
+  if constexpr (gemv_takes<EPI>(IN))
+    return reinterpret_cast<const void*>(&lf::k_gemv<EPI, gemv_nr<EPI>(), KCH, GPW, WAVES, IN>);
+  else
+    return nullptr;
+}
+
+template <int EPI, int KCH, int IN>
+const void* gemv_fn_k(int waves, int gpw) {
+  if (waves == 4 && gpw == 7) return gemv_fn<EPI, KCH, 7, 4, IN>();
+  if (waves == 8 && gpw == 8) return gemv_fn<EPI, KCH, 8, 8, IN>();
+  if (waves == 8 && gpw == 2) return gemv_fn<EPI, KCH, 2, 8, IN>();
+  return gemv_fn<EPI, KCH, 1, 8, IN>();
+}
+
+template <int EPI, int IN>
+const void* gemv_kernel_in(int K, int waves, int gpw) {
   switch (gemv_kch(K)) {
-    case 1: return gemv_fn_k<EPI, 1>(waves, gpw);
-    case 2: return gemv_fn_k<EPI, 2>(waves, gpw);
-    case 4: return gemv_fn_k<EPI, 4>(waves, gpw);
-    case 8: return gemv_fn_k<EPI, 8>(waves, gpw);
-    case 14: return gemv_fn_k<EPI, 14>(waves, gpw);
-    default: return gemv_fn_k<EPI, 16>(waves, gpw);
+    case 1: return gemv_fn_k<EPI, 1, IN>(waves, gpw);
+    case 2: return gemv_fn_k<EPI, 2, IN>(waves, gpw);
+    case 4: return gemv_fn_k<EPI, 4, IN>(waves, gpw);
+    case 8: return gemv_fn_k<EPI, 8, IN>(waves, gpw);
+    case 14: return gemv_fn_k<EPI, 14, IN>(waves, gpw);
+    default: return gemv_fn_k<EPI, 16, IN>(waves, gpw);
+  }
+}
+
+// The kernel variant for (input kind, K, launch shape); null if EPI never
+// takes that input.
+template <int EPI>
+const void* gemv_kernel(int K, int waves, int gpw, int in) {
+  switch (in) {
+    case lf::kInF32: return gemv_kernel_in<EPI, lf::kInF32>(K, waves, gpw);
+    case lf::kInNormF32: return gemv_kernel_in<EPI, lf::kInNormF32>(K, waves, gpw);
+    default: return gemv_kernel_in<EPI, lf::kInNormEmbed>(K, waves, gpw);
   }
 }
 
 template <int EPI>
 void launch_gemv(const lf::GemvArgs& a, hipStream_t st) {
   const GemvShape sh = gemv_shape(EPI, a.rows);
-  const void* fn = gemv_kernel<EPI>(a.K, sh.waves, sh.gpw);
+  const void* fn = gemv_kernel<EPI>(a.K, sh.waves, sh.gpw, a.in_kind);
   void* args[] = {const_cast<lf::GemvArgs*>(&a)};
   (void)hipLaunchKernel(fn, dim3(sh.blocks), dim3(sh.waves * lf::kWave), args, static_cast<size_t>(a.K) * sizeof(float),
                         st);
@@ -313,9 +335,12 @@ void launch_gemv(const lf::GemvArgs& a, hipStream_t st) {
 template <int EPI>
 int set_lds_limit_epi() {
   const int bytes = 8192 * sizeof(float);
-  for (int K : {512, 1024, 2048, 4096, 7168, 8192})
-    for (const int* wg : {(const int[]){4, 7}, (const int[]){8, 8}, (const int[]){8, 2}, (const int[]){8, 1}})
-      LF_HIP(hipFuncSetAttribute(gemv_kernel<EPI>(K, wg[0], wg[1]), hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  static const int shapes[][2] = {{4, 7}, {8, 8}, {8, 2}, {8, 1}};  // (waves, row groups per wave)
+  for (int in : {lf::kInF32, lf::kInNormF32, lf::kInNormEmbed})
+    for (int K : {512, 1024, 2048, 4096, 7168, 8192})
+      for (const auto& wg : shapes)
+        if (const void* fn = gemv_kernel<EPI>(K, wg[0], wg[1], in))
+          LF_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
   return LF_OK;
 }
 
