@@ -1,0 +1,156 @@
+// Data exchange between workgroups of one launch through tagged words, and
+// the split merge of attention built on it.
+//
+// Every value another workgroup reads is stored as one 64-bit word (fp32
+// value, 32-bit tag) with a device-scope store; the tag names the producing
+// launch (and phase), and a reader polls with device-scope loads until the
+// words it needs carry the expected tag. Producers never wait for their
+// stores, so an exchange costs one memory round trip after the data lands.
+#pragma once
+#include "lf_device.h"
+
+namespace lf {
+
+typedef unsigned long long u64;
+
+constexpr unsigned kSSpin = 1u << 21;  // polls before a wait gives up (raises the abort flag)
+
+// Buffers are addressed through buffer descriptors (scalar registers) with a
+// per-lane byte offset and a wave-uniform one, so that few vector registers
+// hold addresses. Reads past a descriptor's range return zero (and are masked
+// out where used).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+
+__device__ __forceinline__ rsrc_t rsrc_of(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+// Store tagged element e: one 64-bit store with the device-scope coherence
+// bit (the form of a relaxed device-scope atomic store).
+__device__ __forceinline__ void put_t(rsrc_t r, int e, float v, unsigned tag) {
+  const u32x2 d = {__float_as_uint(v), tag};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, e * 8, 0, 16);
+}
+
+// Two tagged values (16 bytes at byte offset voff + soff) with a
+// device-coherent load (the cache bypass of a device-scope atomic load; each
+// 8-byte half is one tagged value, written by a single 64-bit store).
+__device__ __forceinline__ u32x4 ld_t2(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 16);
+}
+
+__device__ __forceinline__ bool stale2(const u32x4& v, unsigned tag) { return v[1] != tag || v[3] != tag; }
+
+// Poll budget shared by the waits of a wave: false once the launch is aborted
+// (by another wave, or by this one when its budget runs out).
+struct SPoll {
+  unsigned* abort;
+  unsigned spins;
+  __device__ __forceinline__ bool next(int lane) {
+    if (++spins >= kSSpin) {
+      if (lane == 0) __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    if ((spins & 31) == 0 && __hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+    __builtin_amdgcn_s_sleep(1);
+    return true;
+  }
+};
+
+// One wave of split si of kv head kvh: wait for the S partial states of the
+// kv head's G query heads (part: [n_kv * G][S_max][HD + 2] tagged words:
+// outputs, running max in log2 units, denominator) and store this split's
+// share of the merged attention output to out ([n_kv * G * HD]; tagged words
+// if TAGGED, else fp32 values for a later launch; outputs [si*per,
+// si*per + per) of the G*HD, per even). In rounds of at most
+// 64 output pairs: lane (pair pi, group sg) folds splits sg, sg + NG, ... of
+// pair pi into a running (max, denominator, outputs) state, and the NG groups
+// are folded through mrg (64 words of LDS, this wave's own). Returns false if
+// the launch was aborted.
+template <int HD, int G, bool TAGGED = true>
+__device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int n_kv, int S_max, f32x4* mrg, int kvh,
+                                                 int si, int S, unsigned tag_part, unsigned tag_att, SPoll& poll,
+                                                 int lane) {
+  constexpr int ST = HD + 2;  // tagged words per (head, split)
+  constexpr int NE = G * HD;  // outputs of the kv head's query heads
+  const int per = ((NE + S - 1) / S + 1) & ~1;
+  const int e_begin = si * per, e_end = min(NE, e_begin + per);
+  const rsrc_t r = rsrc_of(part, n_kv * G * S_max * ST * 8);
+  const rsrc_t ro = rsrc_of(out, n_kv * G * HD * 8);
+  constexpr int MAXS = 8;  // splits per lane per batch of loads
+  for (int e0 = e_begin; e0 < e_end; e0 += 2 * kWave) {
+    const int P = min(kWave, (e_end - e0) / 2);  // output pairs of this round
+    const int NG = kWave / P;                    // lane groups
+    const int pi = lane % P, sg = lane / P;
+    const bool active = sg < NG;
+    const int e = e0 + 2 * pi;
+    const int head = kvh * G + e / HD, d = e % HD;
+    const int va_off = (head * S_max * ST + d) * 8, vm_off = (head * S_max * ST + HD) * 8;
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int t0 = sg; t0 < S; t0 += NG * MAXS) {
+      u32x4 va[MAXS], vm[MAXS];
+      unsigned stale = 0;
+#pragma unroll
+      for (int u = 0; u < MAXS; ++u) {
+        const int t = t0 + u * NG;
+        const bool want = active && t < S;
+        // per-lane offsets in the vector operand; splits past S read past the
+        // descriptor's range, which returns zero without a memory access
+        const int so = want ? t * ST * 8 : 0x40000000;
+        va[u] = ld_t2(r, va_off + so, 0);
+        vm[u] = ld_t2(r, vm_off + so, 0);
+        if (want && (stale2(va[u], tag_part) || stale2(vm[u], tag_part))) stale |= 1u << u;
+      }
+      while (__any(stale != 0)) {
+        if (!poll.next(lane)) return false;
+#pragma unroll
+        for (int u = 0; u < MAXS; ++u)
+          if (stale & (1u << u)) {
+            const int t = t0 + u * NG;
+            va[u] = ld_t2(r, va_off + t * ST * 8, 0);
+            vm[u] = ld_t2(r, vm_off + t * ST * 8, 0);
+            if (!stale2(va[u], tag_part) && !stale2(vm[u], tag_part)) stale &= ~(1u << u);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < MAXS; ++u) {
+        const float mu = __uint_as_float(vm[u][0]), lu = __uint_as_float(vm[u][2]);
+        if (!active || t0 + u * NG >= S || mu == -INFINITY) continue;
+        const float Mn = fmaxf(M, mu);
+        const float fo = exp2f(M - Mn), fn = exp2f(mu - Mn);
+        L = L * fo + lu * fn;
+        A0 = A0 * fo + __uint_as_float(va[u][0]) * fn;
+        A1 = A1 * fo + __uint_as_float(va[u][2]) * fn;
+        M = Mn;
+      }
+    }
+    // fold the lane groups (LDS written and read by this wave only)
+    mrg[lane] = f32x4{M, L, A0, A1};
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    if (lane < P) {
+      for (int g = 1; g < NG; ++g) {
+        const f32x4 o = mrg[g * P + lane];
+        if (o[0] == -INFINITY) continue;
+        const float Mn = fmaxf(M, o[0]);
+        const float fo = exp2f(M - Mn), fn = exp2f(o[0] - Mn);
+        L = L * fo + o[1] * fn;
+        A0 = A0 * fo + o[2] * fn;
+        A1 = A1 * fo + o[3] * fn;
+        M = Mn;
+      }
+      if constexpr (TAGGED) {
+        put_t(ro, head * HD + d, A0 / L, tag_att);
+        put_t(ro, head * HD + d + 1, A1 / L, tag_att);
+      } else {
+        *reinterpret_cast<float2*>(static_cast<float*>(out) + head * HD + d) = make_float2(A0 / L, A1 / L);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // reads done before the next round's writes
+    asm volatile("" ::: "memory");
+  }
+  return true;
+}
+
+}  // namespace lf

@@ -18,7 +18,7 @@
 // per-XCD L2 without flushing it); a workgroup announces completion with one
 // atomic after its stores have been acknowledged. No L2 writeback fences.
 #pragma once
-#include "lf_device.h"
+#include "lf_exchange.h"
 
 namespace lf {
 
@@ -29,10 +29,6 @@ __device__ __forceinline__ void put_f32(float* p, float v) {
 }
 __device__ __forceinline__ float get_f32(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put_f32x2(float2* p, float2 v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float2 get_f32x2(const float2* p) {
   return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
@@ -67,20 +63,6 @@ __device__ __forceinline__ bool arrive(unsigned* counter, unsigned expected, int
   return *flag_lds != 0;
 }
 
-// The same where only wave SW of the workgroup stored what must be visible:
-// only that wave waits for its memory operations (the other waves may keep
-// loads in flight), and its first lane counts the arrival.
-template <int SW>
-__device__ __forceinline__ bool arrive_wave(unsigned* counter, unsigned expected, int* flag_lds) {
-  if (threadIdx.x / kWave == SW) __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
-  if (threadIdx.x == SW * kWave) {
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_lds = (prev == expected - 1) ? 1 : 0;
-  }
-  lds_barrier();
-  return *flag_lds != 0;
-}
 
 // ------------------------------------------------------------ reductions
 
@@ -511,26 +493,15 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv(GemvArgs a) {
 
 // ------------------------------------------------------------- attention
 
+// One layer's attention at position p: queries, the layer's cache, the
+// window and the split plan (S work items per kv head, `chunk` keys each).
 struct AttnArgs {
   const float* q;           // rotated queries [Hq * hd]
   const half_t* kc;         // this layer's K cache [lanes][max_ctx][kpl][hd]
   const half_t* vc;
   const int32_t* state;
-  float2* part_ml;          // [Hq][S] (running max in log2 units, denominator)
-  float* part_acc;          // [Hq][S][hd] unnormalised outputs
-  float* o;                 // attention output [Hq * hd]
-  unsigned* counters;       // [Hkv]
   int max_ctx, window, S, chunk, kpl;
   float scale_log2;         // log2(e) / sqrt(hd)
-};
-
-// LDS of one attention work item run by NW waves (also used by the step kernel).
-template <int HD, int G, int NW>
-struct AttnSmem {
-  static constexpr int KPW = kWave / (HD / 8);
-  float2 ml[NW][KPW][G];
-  float acc[NW][KPW][G][HD];
-  int flag;
 };
 
 // K and V loads of one iteration of an attention work item: U 16-byte pieces
@@ -565,88 +536,106 @@ __device__ __forceinline__ AttnSpan attn_span(const AttnArgs& a, int s, int kvh,
   return sp;
 }
 
-// Load 16 bytes of the key (or value) row written in this launch, with
-// device-scope loads.
-__device__ __forceinline__ u32x4 ld_coherent16(const half_t* ptr) {
-  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(ptr);
-  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return u32x4{static_cast<unsigned>(lo), static_cast<unsigned>(lo >> 32), static_cast<unsigned>(hi),
-               static_cast<unsigned>(hi >> 32)};
-}
-
-// Issue the loads of the iteration whose first wave row block is b0. Keys
-// past the split load its last key (masked where used). COH: the key at p
-// (written in this launch) is read with device-scope loads. Requires nk > 0.
-template <int HD, int U, int NW, bool COH>
-__device__ __forceinline__ void attn_load(AttnLoads<U>& ld, const AttnSpan& sp, int b0, int p) {
+// Issue the loads of the iteration whose first wave row block is b0 (NW
+// waves; a wave load covers KPW keys). Keys past the split load its last key
+// (masked where used). Requires nk > 0.
+template <int HD, int U, int NW>
+__device__ __forceinline__ void attn_load(AttnLoads<U>& ld, const AttnSpan& sp, int b0) {
   constexpr int KPW = kWave / (HD / 8);
   const int kin = (threadIdx.x & (kWave - 1)) / (HD / 8);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = min((b0 + u * NW) * KPW + kin, sp.nk - 1);
     const size_t off = static_cast<size_t>(t) * sp.key_stride;
-    if (COH && sp.k0 + t == p) {
-      ld.kk[u] = ld_coherent16(sp.Kb + off);
-      ld.vv[u] = ld_coherent16(sp.Vb + off);
-    } else {
-      ld.kk[u] = ld_stream(sp.Kb + off);
-      ld.vv[u] = ld_stream(sp.Vb + off);
-    }
+    ld.kk[u] = ld_stream(sp.Kb + off);
+    ld.vv[u] = ld_stream(sp.Vb + off);
   }
 }
 
-// Prefetch of the first iteration of a work item before the key at p exists:
-// every key is loaded plainly; attn_item(PRE) reloads the key at p.
+// Prefetch of the first iteration of a work item (all NW waves).
 template <int HD, int U, int NW>
 __device__ __forceinline__ void attn_prefetch(AttnLoads<U>& ld, const AttnArgs& a, int s, int kvh, int p) {
   const AttnSpan sp = attn_span<HD>(a, s, kvh, p);
-  if (sp.nk > 0) attn_load<HD, U, NW, false>(ld, sp, threadIdx.x / kWave, p);
+  if (sp.nk > 0) attn_load<HD, U, NW>(ld, sp, threadIdx.x / kWave);
 }
 
-// Work item (split s, kv head h): read keys [lo + s*chunk, lo + (s+1)*chunk)
-// of kv head h (lane h / kpl) for its G query heads. HD/8 lanes hold one
-// 16-byte piece of a key row; a wave load covers 512/HD keys; U loads of K and
-// of V per lane are in flight per iteration. Each row group keeps an online
-// softmax; the workgroup combines them in LDS and stores one partial state per
-// query head. The last workgroup of the kv head merges the S partials, 16 at a
-// time. All NW waves of the workgroup take part (barriers inside). COH: read
-// the queries and the key written in this launch with device-scope loads.
-// PRE: the first iteration's loads were issued by attn_prefetch (into *pre).
-// SW >= 0: only wave SW stores (partial states, merged outputs) and counts
-// the arrival; the other waves only load and compute.
-template <int HD, int G, int U, int NW, bool COH, bool PRE = false, int SW = -1>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>& sm, int s, int kvh, int p,
-                                          const AttnLoads<U>* pre = nullptr) {
-  constexpr int LPR = HD / 8;        // lanes per key row
-  constexpr int KPW = kWave / LPR;   // keys per wave load
-  constexpr int NT = NW * kWave;
-  static_assert(!PRE || COH, "a prefetched item must reload the key written in this launch");
+// Fold the online-softmax state (m, l, acc) of lane ^ off into this lane's.
+template <int G>
+__device__ __forceinline__ void fold_xor(float (&m)[G], float (&l)[G], float (&acc)[G][8], int off) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float m2 = __shfl_xor(m[g], off), l2 = __shfl_xor(l[g], off);
+    float a2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a2[i] = __shfl_xor(acc[g][i], off);
+    const float M = fmaxf(m[g], m2);
+    if (M == -INFINITY) continue;
+    const float f1 = exp2f(m[g] - M), f2 = exp2f(m2 - M);
+    l[g] = l[g] * f1 + l2 * f2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = acc[g][i] * f1 + a2[i] * f2;
+    m[g] = M;
+  }
+}
+
+struct AttnXArgs {
+  AttnArgs t;
+  u64* part;          // [Hq][S_max][hd + 2] tagged split states: outputs, running max (log2 units), denominator
+  float* o;           // attention output [Hq * hd]
+  unsigned* epochs;   // [Hkv] launch epoch per kv head (>= 1): the tag of its split states
+  unsigned* abort;    // raised when a wait gives up; later waits give up at once
+  int S_max, n_kv;
+};
+
+template <int HD, int G>
+struct AttnXSmem {
+  float acc[kWavesPerBlock][G][HD];  // per-wave softmax states
+  float2 ml[kWavesPerBlock][G];
+  f32x4 mrg[kWave];                  // merge scratch of wave 0
+  unsigned epoch;
+};
+
+// Attention of work item (split s = blockIdx.x, kv head kvh = blockIdx.y):
+// keys [lo + s*chunk, lo + (s+1)*chunk) of the visible ones (lo = p - W + 1
+// under a window W, else 0) for the kv head's G query heads (grouped-query
+// attention: query head i reads kv head i / G). Each of the kBlock/64 waves
+// loads U 16-byte pieces of K and of V per lane per iteration (HD/8 lanes per
+// key row), keeps an online softmax per key row in registers and folds its
+// rows with lane shuffles; the workgroup combines the waves in LDS and stores
+// the split's state as tagged words. Then wave 0 of every split merges its
+// share of the kv head's outputs from the S states (one memory round trip:
+// no counter, no last-workgroup pass) and stores them for the O projection.
+// The S splits of a kv head are consecutive workgroups and wait for each
+// other, so S must not exceed what the device holds at once (it holds many
+// more). The tag is the kv head's epoch, which split 0 advances once it has
+// read every split's state, hence after every split has read the epoch.
+template <int HD, int G, int U>
+__global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
+  constexpr int LPR = HD / 8, NW = kWavesPerBlock;
+  __shared__ AttnXSmem<HD, G> sm;
+  const int p = a.t.state[kLen];
+  if (p >= a.t.max_ctx) return;  // the host never launches a step on a full cache
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int si = blockIdx.x, kvh = blockIdx.y;
   const int kin = lane / LPR, ch = lane % LPR;
-  const AttnSpan sp = attn_span<HD>(a, s, kvh, p);
-  const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-  const int nk = sp.nk;
+  constexpr int KPW = kWave / LPR;
+
+  const AttnSpan sp = attn_span<HD>(a.t, si, kvh, p);
+  AttnLoads<U> ld;
+  if (sp.nk > 0) attn_load<HD, U, NW>(ld, sp, wave);
   float qr[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float* qp = a.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8;
-    if (COH) {
+    const float* qp = a.t.q + static_cast<size_t>(kvh * G + g) * HD + ch * 8;
+    const f32x4 q0 = reinterpret_cast<const f32x4*>(qp)[0], q1 = reinterpret_cast<const f32x4*>(qp)[1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float2 f = get_f32x2(reinterpret_cast<const float2*>(qp) + i);
-        qr[g][2 * i] = f.x * a.scale_log2;
-        qr[g][2 * i + 1] = f.y * a.scale_log2;
-      }
-    } else {
-      const f32x4 q0 = reinterpret_cast<const f32x4*>(qp)[0], q1 = reinterpret_cast<const f32x4*>(qp)[1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qr[g][i] = q0[i] * a.scale_log2;
-        qr[g][4 + i] = q1[i] * a.scale_log2;
-      }
+    for (int i = 0; i < 4; ++i) {
+      qr[g][i] = q0[i] * a.t.scale_log2;
+      qr[g][4 + i] = q1[i] * a.t.scale_log2;
     }
   }
+  if (tid == 0) sm.epoch = a.epochs[kvh];
+
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -655,37 +644,23 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
   }
-  for (int b0 = wave; b0 * KPW < nk; b0 += NW * U) {
-    AttnLoads<U> ld;
-    if (PRE && b0 == wave) {
-      ld = *pre;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = min((b0 + u * NW) * KPW + kin, nk - 1);
-        if (sp.k0 + t == p) {
-          const size_t off = static_cast<size_t>(t) * sp.key_stride;
-          ld.kk[u] = ld_coherent16(sp.Kb + off);
-          ld.vv[u] = ld_coherent16(sp.Vb + off);
-        }
-      }
-    } else {
-      attn_load<HD, U, NW, COH>(ld, sp, b0, p);
-    }
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) ok[u] = (b0 + u * NW) * KPW + kin < nk;
+  const int nk = sp.nk;
+  // one iteration: the scores of U key rows per lane group, then the online
+  // softmax update with their values
+  auto step = [&](const AttnLoads<U>& x, int b0) {
     float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int t = (b0 + u * NW) * KPW + kin;
       float kf[8];
-      unpack8(ld.kk[u], kf);
+      unpack8(x.kk[u], kf);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) d = fmaf(qr[g][i], kf[i], d);
         d = row_sum<LPR>(d);
-        sc[u][g] = ok[u] ? d : -INFINITY;
+        sc[u][g] = t < nk ? d : -INFINITY;
       }
     }
 #pragma unroll
@@ -703,93 +678,61 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, AttnSmem<HD, G, NW>
         const float pu = exp2f(sc[u][g] - mx);
         l[g] += pu;
         float vf[8];
-        unpack8(ld.vv[u], vf);
+        unpack8(x.vv[u], vf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(pu, vf[i], acc[g][i]);
       }
       m[g] = mx;
     }
+  };
+  if (nk > 0) {
+    step(ld, wave);
+    for (int b0 = wave + NW * U; b0 * KPW < nk; b0 += NW * U) {
+      attn_load<HD, U, NW>(ld, sp, b0);
+      step(ld, b0);
+    }
   }
-
-  // Combine the row groups of all waves.
+  // fold the wave's key rows (lanes ch, ch + LPR, ...), then the waves in LDS
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int off = LPR; off < kWave; off <<= 1) fold_xor<G>(m, l, acc, off);
+  if (lane < LPR) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm.acc[wave][kin][g][ch * 8 + i] = acc[g][i];
-    if (ch == 0) sm.ml[wave][kin][g] = make_float2(m[g], l[g]);
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.acc[wave][g][ch * 8 + i] = acc[g][i];
+      if (ch == 0) sm.ml[wave][g] = make_float2(m[g], l[g]);
+    }
   }
   lds_barrier();
-  // storing threads: all of them, or the lanes of wave SW
-  const bool storer = SW < 0 || wave == SW;
-  const int st0 = SW < 0 ? tid : lane, stn = SW < 0 ? NT : kWave;
-  for (int idx = storer ? st0 : G * HD; idx < G * HD; idx += stn) {
+  const unsigned epoch = __builtin_amdgcn_readfirstlane(sm.epoch);
+  const rsrc_t rp = rsrc_of(a.part, a.n_kv * G * a.S_max * (HD + 2) * 8);
+  for (int idx = tid; idx < G * HD; idx += kBlock) {
     const int d = idx % HD, g = idx / HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int r = 0; r < KPW; ++r) M = fmaxf(M, sm.ml[w][r][g].x);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[w][g].x);
     float L = 0.f, A = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int r = 0; r < KPW; ++r) {
-          const float2 ml = sm.ml[w][r][g];
-          const float f = exp2f(ml.x - M);
-          L = fmaf(ml.y, f, L);
-          A = fmaf(sm.acc[w][r][g][d], f, A);
-        }
-    }
-    const int head = kvh * G + g;
-    put_f32(a.part_acc + (static_cast<size_t>(head) * a.S + s) * HD + d, A);
-    if (d == 0) put_f32x2(a.part_ml + head * a.S + s, make_float2(M, L));
-  }
-
-  // The last workgroup of this kv head merges its splits, loading the
-  // partial states 16 splits at a time (one memory round trip per batch).
-  if (!(SW < 0 ? arrive(&a.counters[kvh], a.S, &sm.flag) : arrive_wave<SW < 0 ? 0 : SW>(&a.counters[kvh], a.S, &sm.flag)))
-    return;
-  const int n = p + 1 - lo;
-  const int n_active = min(a.S, (n + a.chunk - 1) / a.chunk);
-  constexpr int MB = 16;
-  for (int idx = storer ? st0 : G * HD; idx < G * HD; idx += stn) {
-    const int d = idx % HD, head = kvh * G + idx / HD;
-    const float2* ml = a.part_ml + head * a.S;
-    const float* pa = a.part_acc + static_cast<size_t>(head) * a.S * HD + d;
-    float M = -INFINITY, L = 0.f, A = 0.f;
-    for (int t0 = 0; t0 < n_active; t0 += MB) {
-      float2 e[MB];
-      float v[MB];
-#pragma unroll
-      for (int u = 0; u < MB; ++u) {
-        const int t = min(t0 + u, n_active - 1);
-        e[u] = get_f32x2(ml + t);
-        v[u] = get_f32(pa + static_cast<size_t>(t) * HD);
-      }
-#pragma unroll
-      for (int u = 0; u < MB; ++u) {
-        if (t0 + u >= n_active || e[u].x == -INFINITY) continue;
-        const float Mn = fmaxf(M, e[u].x);
-        const float fo = exp2f(M - Mn), fn = exp2f(e[u].x - Mn);
-        L = L * fo + e[u].y * fn;
-        A = A * fo + v[u] * fn;
-        M = Mn;
+      for (int w = 0; w < NW; ++w) {
+        const float2 ml = sm.ml[w][g];
+        const float f = exp2f(ml.x - M);
+        L = fmaf(ml.y, f, L);
+        A = fmaf(sm.acc[w][g][d], f, A);
       }
     }
-    put_f32(a.o + static_cast<size_t>(head) * HD + d, A / L);
+    const int base = ((kvh * G + g) * a.S_max + si) * (HD + 2);
+    put_t(rp, base + d, A, epoch);
+    if (d == 0) {
+      put_t(rp, base + HD, M, epoch);
+      put_t(rp, base + HD + 1, L, epoch);
+    }
   }
-  if (tid == (SW < 0 ? 0 : SW * kWave))
-    __hip_atomic_store(&a.counters[kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  lds_barrier();
-}
-
-template <int HD, int G, int U>
-__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
-  __shared__ AttnSmem<HD, G, kWavesPerBlock> sm;
-  const int p = a.state[kLen];
-  if (p >= a.max_ctx) return;
-  attn_item<HD, G, U, kWavesPerBlock, false>(a, sm, blockIdx.x, blockIdx.y, p);
+  if (wave == 0) {
+    SPoll poll{a.abort, 0u};
+    attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, sm.mrg, kvh, si, a.t.S, epoch, epoch, poll, lane);
+    if (si == 0 && lane == 0) a.epochs[kvh] = epoch + 1 == 0 ? 1u : epoch + 1;
+  }
 }
 
 // ------------------------------------------------------------- utilities

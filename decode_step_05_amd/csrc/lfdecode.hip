@@ -43,9 +43,13 @@ struct AttnPlan {
   int S, chunk;
 };
 
-// A workgroup reads its keys in one round of loads: 8 loads of K and of V per
-// lane, 4 waves, 512/head_dim keys per wave load -> 16384/head_dim keys.
-constexpr int kAttnU = 8;
+// Attention splits each kv head's visible keys over at most kAttnSplits work
+// items (16 kv heads x 16 = 256 workgroups: one per CU), at least 64 keys
+// each; every split's merge reads all S split states, so more splits cost
+// more than they gain. A work item reads its keys in rounds of U loads of K
+// and of V per lane (4 waves, 512/head_dim keys per wave load), U the
+// smallest of 4, 8, 16 that covers its chunk in one round.
+constexpr int kAttnSplits = 16;
 constexpr int kMaxSplits = 64;  // partial-state buffers hold this many splits per head
 AttnPlan split_plan(int visible, int S) {
   S = std::max(1, std::min(S, kMaxSplits));
@@ -57,8 +61,13 @@ int visible_keys(const lf_config& c, int layer) {
 }
 AttnPlan attn_plan(const lf_config& c, int layer) {
   const int visible = visible_keys(c, layer);
-  const int per_wg = kAttnU * lf::kWavesPerBlock * (512 / c.head_dim);
-  return split_plan(visible, (visible + per_wg - 1) / per_wg);
+  return split_plan(visible, std::min(kAttnSplits, (visible + 63) / 64));
+}
+int attn_loads_per_lane(int chunk, int head_dim) {
+  const int per_load = lf::kWavesPerBlock * (512 / head_dim);  // keys per load round of the workgroup
+  for (int u : {4, 8})
+    if (u * per_load >= chunk) return u;
+  return 16;
 }
 // The persistent step kernel runs one work item per workgroup: at most
 // nb / n_kv splits per kv head, of at least 32 keys each.
@@ -131,9 +140,10 @@ Dims dims(const lf_config& c) {
 struct WsLayout {
   std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
   std::vector<size_t> sw;  // stream-order copies of the GEMV weights, per stream phase
-  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, part_ml, part_acc, best, counters, bar, sphases, slayers, total;
-  // tagged exchange buffers of the stream step kernel (one zeroed region)
-  size_t xt, qt, kvt, ot, actt, partt, tagged_begin, tagged_end;
+  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, best, counters, bar, attn_epochs, sphases, slayers, total;
+  // tagged exchange buffers of the attention kernel and of the stream step
+  // kernel (one zeroed region)
+  size_t attn_part, xt, qt, kvt, ot, actt, partt, tagged_begin, tagged_end;
   int S_max;
 };
 
@@ -185,13 +195,13 @@ WsLayout ws_layout(const lf_config& c) {
   W.o = take(D.qdim * sizeof(float));
   W.act = take(D.ffn * sizeof(float));
   W.S_max = kMaxSplits;
-  W.part_ml = take(static_cast<size_t>(D.hq) * W.S_max * sizeof(float2));
-  W.part_acc = take(static_cast<size_t>(D.hq) * W.S_max * D.hd * sizeof(float));
   W.best = take(sizeof(unsigned long long));
   W.counters = take((D.hkv + 4) * sizeof(unsigned));
   W.bar = take(8 * sizeof(unsigned));
+  W.attn_epochs = take(D.hkv * sizeof(unsigned));
   const size_t tw = sizeof(unsigned long long);
   W.tagged_begin = off;
+  W.attn_part = take(static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2) * tw);
   W.xt = take(D.d * tw);
   W.qt = take(D.qdim * tw);
   W.kvt = take(static_cast<size_t>(2) * D.hkv * D.hd * tw);
@@ -345,11 +355,16 @@ int set_lds_limit_epi() {
 }
 
 template <int HD, int G>
-void launch_attn_t(const lf::AttnArgs& a, int n_kv, hipStream_t st) {
-  hipLaunchKernelGGL((lf::k_attn<HD, G, kAttnU>), dim3(a.S, n_kv), dim3(lf::kBlock), 0, st, a);
+void launch_attn_t(const lf::AttnXArgs& a, int n_kv, hipStream_t st) {
+  const dim3 grid(a.t.S, n_kv), block(lf::kBlock);
+  switch (attn_loads_per_lane(a.t.chunk, HD)) {
+    case 4: hipLaunchKernelGGL((lf::k_attn<HD, G, 4>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((lf::k_attn<HD, G, 8>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((lf::k_attn<HD, G, 16>), grid, block, 0, st, a); break;
+  }
 }
 
-void launch_attn(const lf::AttnArgs& a, int hd, int G, int n_kv, hipStream_t st) {
+void launch_attn(const lf::AttnXArgs& a, int hd, int G, int n_kv, hipStream_t st) {
 #define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, n_kv, st);
   LF_ATTN_CASE(32, 1) LF_ATTN_CASE(32, 2) LF_ATTN_CASE(32, 4)
   LF_ATTN_CASE(64, 1) LF_ATTN_CASE(64, 2) LF_ATTN_CASE(64, 4)
@@ -489,21 +504,23 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
 
     // attention over the visible keys, split over key ranges, merged in-kernel
     const AttnPlan P = attn_plan(c, l);
-    lf::AttnArgs t{};
-    t.q = m->at<float>(W.q);
-    t.kc = kv->kc() + l * layer_cache;
-    t.vc = kv->vc() + l * layer_cache;
-    t.state = kv->state();
-    t.part_ml = m->at<float2>(W.part_ml);
-    t.part_acc = m->at<float>(W.part_acc);
+    lf::AttnXArgs t{};
+    t.t.q = m->at<float>(W.q);
+    t.t.kc = kv->kc() + l * layer_cache;
+    t.t.vc = kv->vc() + l * layer_cache;
+    t.t.state = kv->state();
+    t.t.max_ctx = D.ctx;
+    t.t.window = c.window[l];
+    t.t.S = P.S;
+    t.t.chunk = P.chunk;
+    t.t.kpl = D.kpl;
+    t.t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
+    t.part = m->at<lf::u64>(W.attn_part);
     t.o = m->at<float>(W.o);
-    t.counters = counters;
-    t.max_ctx = D.ctx;
-    t.window = c.window[l];
-    t.S = P.S;
-    t.chunk = P.chunk;
-    t.kpl = D.kpl;
-    t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
+    t.epochs = m->at<unsigned>(W.attn_epochs);
+    t.abort = m->at<unsigned>(W.bar) + 2;
+    t.S_max = W.S_max;
+    t.n_kv = D.hkv;
     emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, st); });
 
     // O projection + residual
@@ -692,6 +709,8 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(256), dim3(256), 0, st, m->at<unsigned>(W.tagged_begin), 0u,
                      (W.tagged_end - W.tagged_begin) / sizeof(unsigned));
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar) + 3, 1u, size_t(1));
+  // attention: split states are tagged with the kv head's epoch, which starts at 1
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.attn_epochs), 1u, size_t(D.hkv));
   // Stream-order copies of the repacked GEMV weights, and the tables of the
   // stream step kernel (the host copies live until the stream is
   // synchronized below).
