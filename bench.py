@@ -29,9 +29,10 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 # WRITE_SIZE (a 512 MiB device copy reads as 0.5x FETCH_SIZE, writes as 1.0x
 # WRITE_SIZE; both factors applied), for the GEMV kernel sources whose sha256
 # is given: reported only while the sources are unchanged.
-GATE_UP_TRAFFIC = {"bytes": 118265092,
-                   "sources": ("decode_step_05_amd/csrc/lf_device.h", "decode_step_05_amd/csrc/lf_kernels.h"),
-                   "sha256": "44513e22b0c636cc0b66e3f4f9c4d89e98515c2e86f646189732e39d68e93147"}
+GATE_UP_TRAFFIC = {"bytes": 118150424,
+                   "sources": ("decode_step_05_amd/csrc/lf_device.h", "decode_step_05_amd/csrc/lf_exchange.h",
+                               "decode_step_05_amd/csrc/lf_kernels.h"),
+                   "sha256": "59c7c7d69f032d6225e07d951966a7aaa7b3fcf442735fa39cdeab7e69de7e10"}
 
 
 def measured_traffic(entry):
