@@ -33,6 +33,17 @@ __device__ __forceinline__ void put_t(rsrc_t r, int e, float v, unsigned tag) {
   __builtin_amdgcn_raw_buffer_store_b64(d, r, e * 8, 0, 16);
 }
 
+// Store tagged element e for readers on the same XCD: a plain store, which
+// lands in (and stays in) that XCD's L2, the cache the readers' device-scope
+// loads are served from. Workgroups whose launch indices are congruent
+// modulo 8 share an XCD (workgroups are dealt to the XCDs in turn; checked
+// when a model is initialised). An exchange through the L2 costs about half a
+// memory round trip.
+__device__ __forceinline__ void put_t_xcd(rsrc_t r, int e, float v, unsigned tag) {
+  const u32x2 d = {__float_as_uint(v), tag};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, e * 8, 0, 0);
+}
+
 // Two tagged values (16 bytes at byte offset voff + soff) with a
 // device-coherent load (the cache bypass of a device-scope atomic load; each
 // 8-byte half is one tagged value, written by a single 64-bit store).

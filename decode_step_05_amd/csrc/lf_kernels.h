@@ -10,8 +10,8 @@
 // epilogue fuses what follows the product: rotary embedding and the KV append
 // (QKV), SwiGLU (gate/up), the residual add (O, down), or the logits and the
 // greedy argmax (LM head). Attention splits each kv head's visible keys over
-// workgroups; the last workgroup of a kv head merges the partial softmax
-// states.
+// workgroups; every split merges its share of the kv head's outputs from the
+// partial softmax states of all splits.
 //
 // Data that another workgroup of the same launch reads is written with
 // device-scope stores and read with device-scope loads (they bypass the
@@ -605,18 +605,30 @@ struct AttnXSmem {
 // the split's state as tagged words. Then wave 0 of every split merges its
 // share of the kv head's outputs from the S states (one memory round trip:
 // no counter, no last-workgroup pass) and stores them for the O projection.
-// The S splits of a kv head are consecutive workgroups and wait for each
-// other, so S must not exceed what the device holds at once (it holds many
-// more). The tag is the kv head's epoch, which split 0 advances once it has
-// read every split's state, hence after every split has read the epoch.
-template <int HD, int G, int U>
+// The S splits of a kv head wait for each other, so S must not exceed what
+// the device holds at once (it holds many more). The tag is the kv head's
+// epoch, which split 0 advances once it has read every split's state, hence
+// after every split has read the epoch.
+// XCD: the launch is one-dimensional (S * n_kv workgroups, n_kv a multiple
+// of 8) and the splits of a kv head are the workgroups congruent to it
+// modulo 8, so they run on one XCD and exchange their states through its
+// L2; otherwise the grid is (S, n_kv) and the states go through memory.
+template <int HD, int G, int U, bool XCD>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
   constexpr int LPR = HD / 8, NW = kWavesPerBlock;
   __shared__ AttnXSmem<HD, G> sm;
   const int p = a.t.state[kLen];
   if (p >= a.t.max_ctx) return;  // the host never launches a step on a full cache
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  const int si = blockIdx.x, kvh = blockIdx.y;
+  int si, kvh;
+  if constexpr (XCD) {
+    const int b = blockIdx.x, hpc = a.n_kv >> 3, r = b >> 3;  // hpc kv heads per XCD
+    kvh = (b & 7) + 8 * (r % hpc);
+    si = r / hpc;
+  } else {
+    si = blockIdx.x;
+    kvh = blockIdx.y;
+  }
   const int kin = lane / LPR, ch = lane % LPR;
   constexpr int KPW = kWave / LPR;
 
@@ -722,10 +734,18 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
       }
     }
     const int base = ((kvh * G + g) * a.S_max + si) * (HD + 2);
-    put_t(rp, base + d, A, epoch);
-    if (d == 0) {
-      put_t(rp, base + HD, M, epoch);
-      put_t(rp, base + HD + 1, L, epoch);
+    if constexpr (XCD) {
+      put_t_xcd(rp, base + d, A, epoch);
+      if (d == 0) {
+        put_t_xcd(rp, base + HD, M, epoch);
+        put_t_xcd(rp, base + HD + 1, L, epoch);
+      }
+    } else {
+      put_t(rp, base + d, A, epoch);
+      if (d == 0) {
+        put_t(rp, base + HD, M, epoch);
+        put_t(rp, base + HD + 1, L, epoch);
+      }
     }
   }
   if (wave == 0) {
@@ -766,6 +786,11 @@ __global__ __launch_bounds__(kBlock) void k_repack(RepackArgs a) {
   const u32x4* s = reinterpret_cast<const u32x4*>(a.src + static_cast<size_t>(sr) * a.K);
   u32x4* d = reinterpret_cast<u32x4*>(a.dst + static_cast<size_t>(r) * a.K);
   for (int c = threadIdx.x; c < (a.K >> 3); c += kBlock) d[c] = s[c];
+}
+
+// The XCD each workgroup runs on (hardware register XCC_ID, bits 3:0).
+__global__ void k_xcd_ids(unsigned* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg(20 | (3 << 11)) & 0xFu;
 }
 
 __global__ void k_fill_u32(unsigned* p, unsigned v, size_t n) {

@@ -255,6 +255,7 @@ struct lf_model {
   std::vector<hipEvent_t> events;        // per-kernel brackets for lf_step_kernel_times
   std::vector<lf_kv*> kvs;               // live sequences; detached when the model is freed
   int mode = LF_MODE_GRAPH;
+  bool xcd_classes = false;              // workgroups congruent modulo 8 share an XCD (probed at init)
   const void* step_fn = nullptr;         // stream step kernel for this shape (null: unavailable)
   int step_lds = 0;                      // its LDS bytes per workgroup
   std::vector<GraphEntry> graphs;
@@ -354,18 +355,26 @@ int set_lds_limit_epi() {
   return LF_OK;
 }
 
-template <int HD, int G>
-void launch_attn_t(const lf::AttnXArgs& a, int n_kv, hipStream_t st) {
-  const dim3 grid(a.t.S, n_kv), block(lf::kBlock);
+template <int HD, int G, bool XCD>
+void launch_attn_x(const lf::AttnXArgs& a, int n_kv, hipStream_t st) {
+  const dim3 grid = XCD ? dim3(a.t.S * n_kv) : dim3(a.t.S, n_kv), block(lf::kBlock);
   switch (attn_loads_per_lane(a.t.chunk, HD)) {
-    case 4: hipLaunchKernelGGL((lf::k_attn<HD, G, 4>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((lf::k_attn<HD, G, 8>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((lf::k_attn<HD, G, 16>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((lf::k_attn<HD, G, 4, XCD>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((lf::k_attn<HD, G, 8, XCD>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((lf::k_attn<HD, G, 16, XCD>), grid, block, 0, st, a); break;
   }
 }
 
-void launch_attn(const lf::AttnXArgs& a, int hd, int G, int n_kv, hipStream_t st) {
-#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, n_kv, st);
+// The splits of each kv head exchange their states through one XCD's L2 when
+// the kv heads divide evenly over the 8 XCD classes of workgroups.
+template <int HD, int G>
+void launch_attn_t(const lf::AttnXArgs& a, int n_kv, bool xcd, hipStream_t st) {
+  if (xcd && n_kv % 8 == 0) return launch_attn_x<HD, G, true>(a, n_kv, st);
+  launch_attn_x<HD, G, false>(a, n_kv, st);
+}
+
+void launch_attn(const lf::AttnXArgs& a, int hd, int G, int n_kv, bool xcd, hipStream_t st) {
+#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, n_kv, xcd, st);
   LF_ATTN_CASE(32, 1) LF_ATTN_CASE(32, 2) LF_ATTN_CASE(32, 4)
   LF_ATTN_CASE(64, 1) LF_ATTN_CASE(64, 2) LF_ATTN_CASE(64, 4)
   LF_ATTN_CASE(128, 1) LF_ATTN_CASE(128, 2) LF_ATTN_CASE(128, 4)
@@ -521,7 +530,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     t.abort = m->at<unsigned>(W.bar) + 2;
     t.S_max = W.S_max;
     t.n_kv = D.hkv;
-    emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, st); });
+    emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, m->xcd_classes, st); });
 
     // O projection + residual
     a = base;
@@ -629,6 +638,32 @@ size_t lf_workspace_bytes(const lf_config* cfg) {
 size_t lf_kv_bytes(const lf_config* cfg) {
   if (validate(cfg) != LF_OK) return 0;
   return kv_layout(*cfg).total;
+}
+
+// Whether workgroups whose launch indices are congruent modulo 8 run on one
+// XCD (workgroups are dealt to the XCDs in turn, continuing from where the
+// previous launch stopped): read each workgroup's XCD in launches of 256,
+// 37 and 256 workgroups. Uses the attention state buffer as scratch and
+// zeroes it again.
+static int probe_xcd_classes(lf_model* m, hipStream_t st) {
+  unsigned* ids = m->at<unsigned>(m->W.attn_part);
+  hipLaunchKernelGGL(lf::k_xcd_ids, dim3(256), dim3(64), 0, st, ids);
+  hipLaunchKernelGGL(lf::k_xcd_ids, dim3(37), dim3(64), 0, st, ids + 256);
+  hipLaunchKernelGGL(lf::k_xcd_ids, dim3(256), dim3(64), 0, st, ids + 512);
+  std::vector<unsigned> h(768);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(h.data(), ids, h.size() * sizeof(unsigned), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(256), 0, st, ids, 0u, h.size());
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  }
+  if (e != hipSuccess) return fail(LF_EHIP, "XCD probe: %s", hipGetErrorString(e));
+  bool ok = true;
+  for (int b = 0; b < 256; ++b) ok = ok && h[b] == h[b % 8] && h[512 + b] == h[512 + b % 8];
+  m->xcd_classes = ok;
+  return LF_OK;
 }
 
 int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspace, size_t ws_bytes,
@@ -759,6 +794,7 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
+  if ((rc = probe_xcd_classes(m, st))) return bail(rc);
   *out = m;
   return LF_OK;
 }
