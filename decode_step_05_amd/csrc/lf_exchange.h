@@ -69,88 +69,95 @@ struct SPoll {
   }
 };
 
+// Fold softmax state (m2, l2, a0, a1) into (M, L, A0, A1): maxima in log2
+// units; a state with maximum -inf holds nothing.
+__device__ __forceinline__ void fold_state(float& M, float& L, float& A0, float& A1, float m2, float l2, float a0,
+                                           float a1) {
+  const float Mn = fmaxf(M, m2);
+  if (Mn == -INFINITY) return;
+  const float fo = exp2f(M - Mn), fn = exp2f(m2 - Mn);
+  L = L * fo + l2 * fn;
+  A0 = A0 * fo + a0 * fn;
+  A1 = A1 * fo + a1 * fn;
+  M = Mn;
+}
+
 // One wave of split si of kv head kvh: wait for the S partial states of the
 // kv head's G query heads (part: [n_kv * G][S_max][HD + 2] tagged words:
 // outputs, running max in log2 units, denominator) and store this split's
 // share of the merged attention output to out ([n_kv * G * HD]; tagged words
 // if TAGGED, else fp32 values for a later launch; outputs [si*per,
-// si*per + per) of the G*HD, per even). In rounds of at most
-// 64 output pairs: lane (pair pi, group sg) folds splits sg, sg + NG, ... of
-// pair pi into a running (max, denominator, outputs) state, and the NG groups
-// are folded through mrg (64 words of LDS, this wave's own). Returns false if
+// si*per + per) of the G*HD, per even). In rounds of at most 64 output
+// pairs: lane (pair pi, group sg) of NG groups (P pairs rounded up to a power
+// of two per group) folds splits sg, sg + NG, ... of pair pi into a running
+// (max, denominator, outputs) state, and the groups are folded by lane
+// shuffles. Every load of a batch is issued before the first is waited for,
+// so a batch whose states have landed costs one round trip. Returns false if
 // the launch was aborted.
 template <int HD, int G, bool TAGGED = true>
-__device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int n_kv, int S_max, f32x4* mrg, int kvh,
-                                                 int si, int S, unsigned tag_part, unsigned tag_att, SPoll& poll,
-                                                 int lane) {
+__device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int n_kv, int S_max, int kvh, int si,
+                                                 int S, unsigned tag_part, unsigned tag_att, SPoll& poll, int lane) {
   constexpr int ST = HD + 2;  // tagged words per (head, split)
   constexpr int NE = G * HD;  // outputs of the kv head's query heads
   const int per = ((NE + S - 1) / S + 1) & ~1;
   const int e_begin = si * per, e_end = min(NE, e_begin + per);
   const rsrc_t r = rsrc_of(part, n_kv * G * S_max * ST * 8);
   const rsrc_t ro = rsrc_of(out, n_kv * G * HD * 8);
-  constexpr int MAXS = 8;  // splits per lane per batch of loads
+  constexpr int MAXS = 4;  // splits per lane per batch of loads
   for (int e0 = e_begin; e0 < e_end; e0 += 2 * kWave) {
     const int P = min(kWave, (e_end - e0) / 2);  // output pairs of this round
-    const int NG = kWave / P;                    // lane groups
-    const int pi = lane % P, sg = lane / P;
-    const bool active = sg < NG;
-    const int e = e0 + 2 * pi;
+    int PP = 1;
+    while (PP < P) PP <<= 1;
+    const int NG = kWave / PP;  // lane groups
+    const int pi = lane & (PP - 1), sg = lane / PP;
+    const bool active = pi < P;
+    const int e = e0 + 2 * min(pi, P - 1);
     const int head = kvh * G + e / HD, d = e % HD;
     const int va_off = (head * S_max * ST + d) * 8, vm_off = (head * S_max * ST + HD) * 8;
     float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
     for (int t0 = sg; t0 < S; t0 += NG * MAXS) {
       u32x4 va[MAXS], vm[MAXS];
-      unsigned stale = 0;
+      int so[MAXS];
 #pragma unroll
       for (int u = 0; u < MAXS; ++u) {
         const int t = t0 + u * NG;
-        const bool want = active && t < S;
         // per-lane offsets in the vector operand; splits past S read past the
         // descriptor's range, which returns zero without a memory access
-        const int so = want ? t * ST * 8 : 0x40000000;
-        va[u] = ld_t2(r, va_off + so, 0);
-        vm[u] = ld_t2(r, vm_off + so, 0);
-        if (want && (stale2(va[u], tag_part) || stale2(vm[u], tag_part))) stale |= 1u << u;
+        so[u] = active && t < S ? t * ST * 8 : 0x40000000;
+        va[u] = ld_t2(r, va_off + so[u], 0);
+        vm[u] = ld_t2(r, vm_off + so[u], 0);
       }
+      unsigned stale = 0;
+#pragma unroll
+      for (int u = 0; u < MAXS; ++u)
+        if (so[u] != 0x40000000 && (stale2(va[u], tag_part) || stale2(vm[u], tag_part))) stale |= 1u << u;
       while (__any(stale != 0)) {
         if (!poll.next(lane)) return false;
 #pragma unroll
-        for (int u = 0; u < MAXS; ++u)
+        for (int u = 0; u < MAXS; ++u) {
+          const int o = (stale & (1u << u)) ? so[u] : 0x40000000;
+          const u32x4 na = ld_t2(r, va_off + o, 0), nm = ld_t2(r, vm_off + o, 0);
           if (stale & (1u << u)) {
-            const int t = t0 + u * NG;
-            va[u] = ld_t2(r, va_off + t * ST * 8, 0);
-            vm[u] = ld_t2(r, vm_off + t * ST * 8, 0);
-            if (!stale2(va[u], tag_part) && !stale2(vm[u], tag_part)) stale &= ~(1u << u);
+            va[u] = na;
+            vm[u] = nm;
           }
+        }
+        unsigned still = 0;
+#pragma unroll
+        for (int u = 0; u < MAXS; ++u)
+          if ((stale & (1u << u)) && (stale2(va[u], tag_part) || stale2(vm[u], tag_part))) still |= 1u << u;
+        stale = still;
       }
 #pragma unroll
-      for (int u = 0; u < MAXS; ++u) {
-        const float mu = __uint_as_float(vm[u][0]), lu = __uint_as_float(vm[u][2]);
-        if (!active || t0 + u * NG >= S || mu == -INFINITY) continue;
-        const float Mn = fmaxf(M, mu);
-        const float fo = exp2f(M - Mn), fn = exp2f(mu - Mn);
-        L = L * fo + lu * fn;
-        A0 = A0 * fo + __uint_as_float(va[u][0]) * fn;
-        A1 = A1 * fo + __uint_as_float(va[u][2]) * fn;
-        M = Mn;
-      }
+      for (int u = 0; u < MAXS; ++u)
+        if (so[u] != 0x40000000)
+          fold_state(M, L, A0, A1, __uint_as_float(vm[u][0]), __uint_as_float(vm[u][2]), __uint_as_float(va[u][0]),
+                     __uint_as_float(va[u][2]));
     }
-    // fold the lane groups (LDS written and read by this wave only)
-    mrg[lane] = f32x4{M, L, A0, A1};
-    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    if (lane < P) {
-      for (int g = 1; g < NG; ++g) {
-        const f32x4 o = mrg[g * P + lane];
-        if (o[0] == -INFINITY) continue;
-        const float Mn = fmaxf(M, o[0]);
-        const float fo = exp2f(M - Mn), fn = exp2f(o[0] - Mn);
-        L = L * fo + o[1] * fn;
-        A0 = A0 * fo + o[2] * fn;
-        A1 = A1 * fo + o[3] * fn;
-        M = Mn;
-      }
+    // fold the lane groups: lanes pi + PP * g, g < NG
+    for (int off = PP; off < kWave; off <<= 1)
+      fold_state(M, L, A0, A1, __shfl_xor(M, off), __shfl_xor(L, off), __shfl_xor(A0, off), __shfl_xor(A1, off));
+    if (sg == 0 && active) {
       if constexpr (TAGGED) {
         put_t(ro, head * HD + d, A0 / L, tag_att);
         put_t(ro, head * HD + d + 1, A1 / L, tag_att);
@@ -158,8 +165,6 @@ __device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int
         *reinterpret_cast<float2*>(static_cast<float*>(out) + head * HD + d) = make_float2(A0 / L, A1 / L);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // reads done before the next round's writes
-    asm volatile("" ::: "memory");
   }
   return true;
 }

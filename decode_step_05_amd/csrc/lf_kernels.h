@@ -5,7 +5,8 @@
 // g, g + TW, g + 2 TW, ... (TW = all waves of the launch) and keeps the next
 // group's loads in flight while it reduces the current one, so HBM stays busy
 // through the reductions; the first two groups are issued before the
-// workgroup stages its input vector in LDS. The input stage can apply RMSNorm
+// workgroup stages its input vector in LDS (after it, for QKV). The input
+// stage can apply RMSNorm
 // (each workgroup reduces sum(x^2) itself: no separate norm kernel), and the
 // epilogue fuses what follows the product: rotary embedding and the KV append
 // (QKV), SwiGLU (gate/up), the residual add (O, down), or the logits and the
@@ -405,16 +406,21 @@ __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* re
   Stage<THREADS, KMAX> st;
   // Issue order: input vector, then weights (loads retire in issue order).
   // The embedding row needs the position first; that is one kernel per step.
-  // (Staging the input before requesting any weight was measured slower:
-  // HBM idles for the input's round trip at every launch.)
+  // Staging the input before requesting any weight leaves HBM idle for the
+  // input's round trip at every launch, which was measured slower for every
+  // GEMV but QKV: there every wave requests all its rows (four) at once, the
+  // input comes back behind them, and the reduction of the four rows after
+  // it costs more than the idle round trip.
   constexpr bool embed = IN == kInNormEmbed;
+  constexpr bool stage_first = EPI == kEpiQKV && !embed;
   if constexpr (!embed) stage_load<THREADS, KMAX, COH, IN>(st, a, 0);
+  if constexpr (stage_first) stage_store<THREADS, KMAX, IN>(st, a, xs, red);
   issue_rows<NR, KCH>(buf[0], a.W, min(gw, ng - 1) * NR, a.rows, a.K, lane, res);
   if (GPW > 1) issue_rows<NR, KCH>(buf[1], a.W, min(gw + TW, ng - 1) * NR, a.rows, a.K, lane, res);
   p = a.state[kLen];
   if (p >= a.max_ctx) return false;  // the host never launches a step on a full cache
   if constexpr (embed) stage_load<THREADS, KMAX, COH, IN>(st, a, p);
-  stage_store<THREADS, KMAX, IN>(st, a, xs, red);
+  if constexpr (!stage_first) stage_store<THREADS, KMAX, IN>(st, a, xs, red);
   XRegs<KCH> xr;
   if constexpr (XRegs<KCH>::on) {
     const int K8 = a.K >> 3;
@@ -591,7 +597,6 @@ template <int HD, int G>
 struct AttnXSmem {
   float acc[kWavesPerBlock][G][HD];  // per-wave softmax states
   float2 ml[kWavesPerBlock][G];
-  f32x4 mrg[kWave];                  // merge scratch of wave 0
   unsigned epoch;
 };
 
@@ -750,7 +755,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
   }
   if (wave == 0) {
     SPoll poll{a.abort, 0u};
-    attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, sm.mrg, kvh, si, a.t.S, epoch, epoch, poll, lane);
+    attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, kvh, si, a.t.S, epoch, epoch, poll, lane);
     if (si == 0 && lane == 0) a.epochs[kvh] = epoch + 1 == 0 ? 1u : epoch + 1;
   }
 }

@@ -99,7 +99,6 @@ struct SSmem {
   float kv_new[2][HD];           // attention: key and value at p
   float comb[G][HD];             // attention: combined state of the workgroup
   float2 comb_ml[G];
-  f32x4 mrg[kWave];              // attention: per-lane merge states (max, denominator, two outputs)
   float res[kSResMax];           // GEMV results of the workgroup's rows
   float resid[kSResMax];         // the residual stream rows the workgroup's O and down phases produce
   int flag;
@@ -781,7 +780,7 @@ __device__ __forceinline__ void s_ctrl_main(const SCtx<HD, G>& c) {
         put_t(rpart, ml + 1, sm.comb_ml[lane].y, tp);
       }
       // every split merges its share of the outputs (an abort shows up at the next wait)
-      attn_merge_share<HD, G>(s.partt, s.ot, s.n_kv, s.S_max, sm.mrg, kvh, si, t.S, tp, stag(epoch, l, kTAtt), poll,
+      attn_merge_share<HD, G>(s.partt, s.ot, s.n_kv, s.S_max, kvh, si, t.S, tp, stag(epoch, l, kTAtt), poll,
                               lane);
     }
     alive = stage(4 * l + 1, kSO, l);
