@@ -58,6 +58,31 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
 }
 
 // Butterfly sum over the whole wave; every lane receives the total.
+// The value of lane (this lane ^ off) within a wave64. Offsets 1, 2 and 8
+// are DPP moves (quad permutations; a rotation by 8 within each 16-lane row),
+// 16 and 32 the gfx950 lane swaps between rows (v_permlane16_swap swaps the
+// odd rows of its first operand with the even rows of its second,
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second); only 4 goes through the LDS crossbar.
+__device__ __forceinline__ float lane_xor(float v, int off) {
+  const unsigned u = __float_as_uint(v);
+  const unsigned lane = threadIdx.x & 63;
+  switch (off) {
+    case 1: return __uint_as_float(__builtin_amdgcn_update_dpp(0u, u, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    case 2: return __uint_as_float(__builtin_amdgcn_update_dpp(0u, u, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    case 8: return __uint_as_float(__builtin_amdgcn_update_dpp(0u, u, 0x128, 0xF, 0xF, false));  // row_ror:8
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    }
+    case 32: {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    }
+    default: return __shfl_xor(v, off);
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

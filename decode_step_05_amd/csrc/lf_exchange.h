@@ -154,9 +154,14 @@ __device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int
           fold_state(M, L, A0, A1, __uint_as_float(vm[u][0]), __uint_as_float(vm[u][2]), __uint_as_float(va[u][0]),
                      __uint_as_float(va[u][2]));
     }
-    // fold the lane groups: lanes pi + PP * g, g < NG
-    for (int off = PP; off < kWave; off <<= 1)
-      fold_state(M, L, A0, A1, __shfl_xor(M, off), __shfl_xor(L, off), __shfl_xor(A0, off), __shfl_xor(A1, off));
+    // fold the lane groups: lanes pi + PP * g, g < NG (unrolled, so that each
+    // exchange has a constant offset)
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int off = 1 << k;
+      if (off >= PP)
+        fold_state(M, L, A0, A1, lane_xor(M, off), lane_xor(L, off), lane_xor(A0, off), lane_xor(A1, off));
+    }
     if (sg == 0 && active) {
       if constexpr (TAGGED) {
         put_t(ro, head * HD + d, A0 / L, tag_att);

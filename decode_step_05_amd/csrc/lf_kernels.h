@@ -109,7 +109,9 @@ __device__ __forceinline__ int argmax_index(unsigned long long key) {
 // issued before it (a runtime choice between paths that issue it before and
 // after the weights makes the compiler wait for every load at their join).
 enum InKind : int { kInF32 = 0, kInNormF32 = 1, kInNormEmbed = 2 };
-enum Epi : int { kEpiQKV = 0, kEpiSwiGLU = 1, kEpiResid = 2, kEpiLogits = 3 };
+// kEpiQKVX: QKV whose queries and new keys and values also go to the
+// exchange words of the attention that runs in the same launch.
+enum Epi : int { kEpiQKV = 0, kEpiSwiGLU = 1, kEpiResid = 2, kEpiLogits = 3, kEpiQKVX = 4 };
 
 struct GemvArgs {
   const half_t* W;        // [rows, K] (QKV and gate/up repacked so that epilogue pairs are adjacent rows)
@@ -133,6 +135,8 @@ struct GemvArgs {
   half_t* vc;             //          and V cache
   const float2* rope;     // (cos, sin) [max_ctx][hd / 2]
   int hd, qpl, kpl;
+  u64* qkvx;              // kEpiQKVX: tagged words [Hkv][(G + 2) hd]: per kv head its G queries, key, value
+  unsigned tag;           // kEpiQKVX: their tag
   // finishing work of the last workgroup (kEpiLogits: argmax + step end; kEpiResid: step end)
   unsigned* counter;      // null: none
   unsigned long long* best;  // kEpiLogits: packed greedy key
@@ -315,6 +319,41 @@ __device__ __forceinline__ void qkv_put(const QkvOut& a, int r, float y0, float 
   }
 }
 
+// qkv_put for QKV fused with attention: rotate as qkv_put, append k / v to
+// the cache, and store the rotated queries and the new key and value as
+// tagged words for the attention workgroups on this XCD (plain stores: they
+// stay in the XCD's L2, where those workgroups read them).
+__device__ __forceinline__ void qkv_put_x(const QkvOut& a, u64* x, unsigned tag, int r, float y0, float y1, int p) {
+  const int half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl, G = a.qpl / a.kpl;
+  const int u = r / a.hd, c = (r % a.hd) >> 1;
+  const int ln = u / upl, j = u % upl;
+  if (j < a.qpl + a.kpl) {
+    const int ri = __builtin_amdgcn_readfirstlane(p * half_hd + c);
+    const float2 cs = __builtin_bit_cast(float2, cload(reinterpret_cast<const unsigned long long*>(a.rope + ri)));
+    const float t0 = y0 * cs.x - y1 * cs.y;
+    const float t1 = y0 * cs.y + y1 * cs.x;
+    y0 = t0;
+    y1 = t1;
+  }
+  int kvh, slot;  // exchange slot: G queries, then the key, then the value
+  if (j < a.qpl) {
+    kvh = ln * a.kpl + j / G;
+    slot = j % G;
+  } else {
+    const bool is_k = j < a.qpl + a.kpl;
+    const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
+    kvh = ln * a.kpl + h;
+    slot = is_k ? G : G + 1;
+    half_t* dst = (is_k ? a.kc : a.vc) + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
+    dst[c] = static_cast<half_t>(y0);  // read by later launches only
+    dst[c + half_hd] = static_cast<half_t>(y1);
+  }
+  u64* e = x + (static_cast<size_t>(kvh) * (G + 2) + slot) * a.hd + c;
+  const u64 t = static_cast<u64>(tag) << 32;
+  e[0] = t | __float_as_uint(y0);
+  e[half_hd] = t | __float_as_uint(y1);
+}
+
 // This lane's chunks of the staged input in registers (zero past K): read
 // from LDS once per wave instead of once per row group, for K up to 4096.
 template <int KCH>
@@ -366,6 +405,10 @@ __device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KC
     static_assert(NR == 2, "QKV rows come in rotary pairs");
     if (r >= a.rows) return;
     qkv_put(QkvOut{a.q, a.kc, a.vc, a.rope, a.hd, a.qpl, a.kpl, a.max_ctx}, r, out[0], out[1], p);
+  } else if constexpr (EPI == kEpiQKVX) {
+    static_assert(NR == 2, "QKV rows come in rotary pairs");
+    if (r >= a.rows) return;
+    qkv_put_x(QkvOut{a.q, a.kc, a.vc, a.rope, a.hd, a.qpl, a.kpl, a.max_ctx}, a.qkvx, a.tag, r, out[0], out[1], p);
   } else if constexpr (EPI == kEpiSwiGLU) {
     static_assert(NR == 2, "gate/up rows come in pairs");
     if (r >= a.rows) return;
@@ -388,15 +431,44 @@ __device__ __forceinline__ void finish_rows(const GemvArgs& a, const Rows<NR, KC
   }
 }
 
+// Row group of wave gw (of TW) at its k-th group. MAP 0: gw + k TW. MAP 1,
+// the QKV projection fused with attention (256 workgroups of 8 waves, two
+// groups each; 16 kv heads of G + 2 heads of hd rows, G = qpl / kpl, and
+// (G + 2) hd / 2 = 256 rotary pairs each): workgroup b's k-th groups are
+// pairs of kv head (b mod 8) + 8 k, whose attention runs on the workgroups
+// congruent to b modulo 8 (one XCD), pair (b / 8) * 8 + wave of the head's
+// queries, key and value, in the lane-major row order of the repacked
+// weights.
+template <int MAP>
+__device__ __forceinline__ int row_group(const GemvArgs& a, int gw, int TW, int k) {
+  if constexpr (MAP == 0) {
+    return gw + k * TW;
+  } else {
+    const int b = gw >> 3, w = gw & 7;
+    const int kvh = (b & 7) + 8 * k, j = (b >> 3) * 8 + w;
+    const int G = a.qpl / a.kpl, half = a.hd >> 1;
+    const int u = j / half, jj = j % half;  // unit of the kv head: query u < G, key G, value G + 1
+    const int ln = kvh / a.kpl, kvl = kvh % a.kpl;
+    const int unit = u < G ? kvl * G + u : u == G ? a.qpl + kvl : a.qpl + a.kpl + kvl;
+    return (ln * (a.qpl + 2 * a.kpl) + unit) * half + jj;
+  }
+}
+
 // The GEMV work of one workgroup: wave gw of TW handles row groups gw + k*TW
 // for k < GPW (the launch covers the matrix: GPW * TW >= groups). The loop is
 // unrolled at compile time so that each group's loads are waited for exactly
 // (the next group's loads stay in flight while this one is reduced).
 // Must be called by every thread of the workgroup (the input stage has barriers).
 // Returns false (in every thread) if the sequence is full and nothing was done.
-template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH, int IN>
+struct NoLoads {
+  __device__ void operator()(int) const {}
+};
+
+// pre(p): further loads of the caller at position p, issued after the input
+// is staged (QKV) and before the weights.
+template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH, int IN, int MAP = 0, class Pre = NoLoads>
 __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* red, int gw, int TW, int& p, float& bv,
-                                         int& bi) {
+                                         int& bi, const Pre& pre = Pre{}) {
   const int lane = threadIdx.x & (kWave - 1);
   const int ng = (a.rows + NR - 1) / NR;
   const float* res = EPI == kEpiResid ? a.y : nullptr;
@@ -412,12 +484,16 @@ __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* re
   // input comes back behind them, and the reduction of the four rows after
   // it costs more than the idle round trip.
   constexpr bool embed = IN == kInNormEmbed;
-  constexpr bool stage_first = EPI == kEpiQKV && !embed;
+  constexpr bool stage_first = (EPI == kEpiQKV || EPI == kEpiQKVX) && !embed;
+  // The position, read before any store of this launch (so with a scalar
+  // load), is waited for only where it is first used.
+  p = a.state[kLen];
   if constexpr (!embed) stage_load<THREADS, KMAX, COH, IN>(st, a, 0);
   if constexpr (stage_first) stage_store<THREADS, KMAX, IN>(st, a, xs, red);
-  issue_rows<NR, KCH>(buf[0], a.W, min(gw, ng - 1) * NR, a.rows, a.K, lane, res);
-  if (GPW > 1) issue_rows<NR, KCH>(buf[1], a.W, min(gw + TW, ng - 1) * NR, a.rows, a.K, lane, res);
-  p = a.state[kLen];
+  pre(p);
+  issue_rows<NR, KCH>(buf[0], a.W, min(row_group<MAP>(a, gw, TW, 0), ng - 1) * NR, a.rows, a.K, lane, res);
+  if (GPW > 1)
+    issue_rows<NR, KCH>(buf[1], a.W, min(row_group<MAP>(a, gw, TW, 1), ng - 1) * NR, a.rows, a.K, lane, res);
   if (p >= a.max_ctx) return false;  // the host never launches a step on a full cache
   if constexpr (embed) stage_load<THREADS, KMAX, COH, IN>(st, a, p);
   if constexpr (!stage_first) stage_store<THREADS, KMAX, IN>(st, a, xs, red);
@@ -434,14 +510,15 @@ __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* re
   }
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
-    const int g = gw + k * TW;
+    const int g = row_group<MAP>(a, gw, TW, k);
     if (g < ng) {
       if (full)
         finish_rows<EPI, NR, KCH, true>(a, buf[k & 1], xs, xr, g * NR, lane, p, bv, bi);
       else
         finish_rows<EPI, NR, KCH, false>(a, buf[k & 1], xs, xr, g * NR, lane, p, bv, bi);
     }
-    if (k + 2 < GPW) issue_rows<NR, KCH>(buf[k & 1], a.W, min(gw + (k + 2) * TW, ng - 1) * NR, a.rows, a.K, lane, res);
+    if (k + 2 < GPW)
+      issue_rows<NR, KCH>(buf[k & 1], a.W, min(row_group<MAP>(a, gw, TW, k + 2), ng - 1) * NR, a.rows, a.K, lane, res);
   }
   return true;
 }
@@ -570,10 +647,10 @@ template <int G>
 __device__ __forceinline__ void fold_xor(float (&m)[G], float (&l)[G], float (&acc)[G][8], int off) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float m2 = __shfl_xor(m[g], off), l2 = __shfl_xor(l[g], off);
+    const float m2 = lane_xor(m[g], off), l2 = lane_xor(l[g], off);
     float a2[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a2[i] = __shfl_xor(acc[g][i], off);
+    for (int i = 0; i < 8; ++i) a2[i] = lane_xor(acc[g][i], off);
     const float M = fmaxf(m[g], m2);
     if (M == -INFINITY) continue;
     const float f1 = exp2f(m[g] - M), f2 = exp2f(m2 - M);
@@ -581,6 +658,117 @@ __device__ __forceinline__ void fold_xor(float (&m)[G], float (&l)[G], float (&a
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = acc[g][i] * f1 + a2[i] * f2;
     m[g] = M;
+  }
+}
+
+// One iteration of a work item: the scores of the U key rows of this lane
+// group (key (b0 + u NW) KPW + kin of the split; keys at or past nk are
+// masked) against the G queries qr (this lane's 8 dimensions, scaled to log2
+// units), then the online-softmax update of (m, l, acc) with their values.
+template <int HD, int G, int U, int NW>
+__device__ __forceinline__ void attn_step(const AttnLoads<U>& x, int b0, int kin, int nk, const float (&qr)[G][8],
+                                          float (&m)[G], float (&l)[G], float (&acc)[G][8]) {
+  constexpr int LPR = HD / 8, KPW = kWave / LPR;
+  float sc[U][G];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = (b0 + u * NW) * KPW + kin;
+    float kf[8];
+    unpack8(x.kk[u], kf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d = fmaf(qr[g][i], kf[i], d);
+      d = row_sum<LPR>(d);
+      sc[u][g] = t < nk ? d : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = m[g];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+    if (mx == -INFINITY) continue;
+    const float al = exp2f(m[g] - mx);
+    l[g] *= al;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] *= al;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pu = exp2f(sc[u][g] - mx);
+      l[g] += pu;
+      float vf[8];
+      unpack8(x.vv[u], vf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(pu, vf[i], acc[g][i]);
+    }
+    m[g] = mx;
+  }
+}
+
+// LDS of the combine step: per-wave softmax states.
+template <int HD, int G, int NW>
+struct AttnCombine {
+  float acc[NW][G][HD];
+  float2 ml[NW][G];
+};
+
+// End of a work item (split si of kv head kvh) computed by waves 0 .. NW-1
+// (every wave of the workgroup calls it; any further waves only take part
+// in its barrier): fold each wave's key rows (lanes ch, ch + LPR, ...),
+// combine the waves in LDS, and store the split's state (outputs, max,
+// denominator) as tagged words (part: [n_kv * G][S_max][HD + 2]); XCD: for
+// readers on this XCD.
+template <int HD, int G, int NW, bool XCD>
+__device__ __forceinline__ void attn_store_state(float (&m)[G], float (&l)[G], float (&acc)[G][8],
+                                                 AttnCombine<HD, G, NW>& cb, u64* part, int n_kv, int S_max,
+                                                 int kvh, int si, unsigned epoch) {
+  constexpr int LPR = HD / 8;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1), ch = lane % LPR;
+  if (wave < NW) {
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) fold_xor<G>(m, l, acc, off);
+  }
+  if (wave < NW && lane < LPR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cb.acc[wave][g][ch * 8 + i] = acc[g][i];
+      if (ch == 0) cb.ml[wave][g] = make_float2(m[g], l[g]);
+    }
+  }
+  lds_barrier();
+  const rsrc_t rp = rsrc_of(part, n_kv * G * S_max * (HD + 2) * 8);
+  for (int idx = tid; idx < G * HD; idx += NW * kWave) {
+    const int d = idx % HD, g = idx / HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, cb.ml[w][g].x);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float2 ml = cb.ml[w][g];
+        const float f = exp2f(ml.x - M);
+        L = fmaf(ml.y, f, L);
+        A = fmaf(cb.acc[w][g][d], f, A);
+      }
+    }
+    const int base = ((kvh * G + g) * S_max + si) * (HD + 2);
+    if constexpr (XCD) {
+      put_t_xcd(rp, base + d, A, epoch);
+      if (d == 0) {
+        put_t_xcd(rp, base + HD, M, epoch);
+        put_t_xcd(rp, base + HD + 1, L, epoch);
+      }
+    } else {
+      put_t(rp, base + d, A, epoch);
+      if (d == 0) {
+        put_t(rp, base + HD, M, epoch);
+        put_t(rp, base + HD + 1, L, epoch);
+      }
+    }
   }
 }
 
@@ -595,9 +783,7 @@ struct AttnXArgs {
 
 template <int HD, int G>
 struct AttnXSmem {
-  float acc[kWavesPerBlock][G][HD];  // per-wave softmax states
-  float2 ml[kWavesPerBlock][G];
-  unsigned epoch;
+  AttnCombine<HD, G, kWavesPerBlock> cb;
 };
 
 // Attention of work item (split s = blockIdx.x, kv head kvh = blockIdx.y):
@@ -651,7 +837,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
       qr[g][4 + i] = q1[i] * a.t.scale_log2;
     }
   }
-  if (tid == 0) sm.epoch = a.epochs[kvh];
+  const unsigned epoch = a.epochs[kvh];  // every wave reads it before its part of the state is stored
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -662,101 +848,162 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
   }
   const int nk = sp.nk;
-  // one iteration: the scores of U key rows per lane group, then the online
-  // softmax update with their values
-  auto step = [&](const AttnLoads<U>& x, int b0) {
-    float sc[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = (b0 + u * NW) * KPW + kin;
-      float kf[8];
-      unpack8(x.kk[u], kf);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d = fmaf(qr[g][i], kf[i], d);
-        d = row_sum<LPR>(d);
-        sc[u][g] = t < nk ? d : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = m[g];
-#pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
-      if (mx == -INFINITY) continue;
-      const float al = exp2f(m[g] - mx);
-      l[g] *= al;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[g][i] *= al;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float pu = exp2f(sc[u][g] - mx);
-        l[g] += pu;
-        float vf[8];
-        unpack8(x.vv[u], vf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(pu, vf[i], acc[g][i]);
-      }
-      m[g] = mx;
-    }
-  };
   if (nk > 0) {
-    step(ld, wave);
+    attn_step<HD, G, U, NW>(ld, wave, kin, nk, qr, m, l, acc);
     for (int b0 = wave + NW * U; b0 * KPW < nk; b0 += NW * U) {
       attn_load<HD, U, NW>(ld, sp, b0);
-      step(ld, b0);
+      attn_step<HD, G, U, NW>(ld, b0, kin, nk, qr, m, l, acc);
     }
   }
-  // fold the wave's key rows (lanes ch, ch + LPR, ...), then the waves in LDS
-#pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) fold_xor<G>(m, l, acc, off);
-  if (lane < LPR) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.acc[wave][g][ch * 8 + i] = acc[g][i];
-      if (ch == 0) sm.ml[wave][g] = make_float2(m[g], l[g]);
-    }
-  }
-  lds_barrier();
-  const unsigned epoch = __builtin_amdgcn_readfirstlane(sm.epoch);
-  const rsrc_t rp = rsrc_of(a.part, a.n_kv * G * a.S_max * (HD + 2) * 8);
-  for (int idx = tid; idx < G * HD; idx += kBlock) {
-    const int d = idx % HD, g = idx / HD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.ml[w][g].x);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float2 ml = sm.ml[w][g];
-        const float f = exp2f(ml.x - M);
-        L = fmaf(ml.y, f, L);
-        A = fmaf(sm.acc[w][g][d], f, A);
-      }
-    }
-    const int base = ((kvh * G + g) * a.S_max + si) * (HD + 2);
-    if constexpr (XCD) {
-      put_t_xcd(rp, base + d, A, epoch);
-      if (d == 0) {
-        put_t_xcd(rp, base + HD, M, epoch);
-        put_t_xcd(rp, base + HD + 1, L, epoch);
-      }
-    } else {
-      put_t(rp, base + d, A, epoch);
-      if (d == 0) {
-        put_t(rp, base + HD, M, epoch);
-        put_t(rp, base + HD + 1, L, epoch);
-      }
-    }
-  }
+  attn_store_state<HD, G, NW, XCD>(m, l, acc, sm.cb, a.part, a.n_kv, a.S_max, kvh, si, epoch);
   if (wave == 0) {
     SPoll poll{a.abort, 0u};
     attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, kvh, si, a.t.S, epoch, epoch, poll, lane);
     if (si == 0 && lane == 0) a.epochs[kvh] = epoch + 1 == 0 ? 1u : epoch + 1;
+  }
+}
+
+// ------------------------------------------- QKV fused with attention
+
+// One layer's QKV projection and attention in one launch of 256 workgroups
+// of 8 waves, one attention work item each (16 kv heads x 16 splits). The
+// kv heads of a class of workgroups congruent modulo 8 (one XCD) are
+// computed and attended to by that class alone, so every exchange goes
+// through the XCD's L2 (about 0.4 us per round trip, against 0.9 us through
+// memory):
+//  1. copy the work item's cached keys and values (before any weight load)
+//     straight to LDS;
+//  2. the QKV GEMV (row_group<1>): rotary embedding, KV append, and the
+//     queries and new key / value as tagged words (kEpiQKVX);
+//  3. wait for the kv head's queries (and, in the split that holds the new
+//     position, its key and value) from the other workgroups of the class,
+//     then attend to the split's keys from LDS as k_attn does;
+//  4. store the split state and merge a share of the kv head's outputs.
+// The tag of the launch is its class's epoch, read by every workgroup at its
+// start; the workgroup holding the new position of the class's first kv head
+// reads words from all 32 workgroups of the class, so after those reads it
+// advances the epoch for the next launch.
+struct QkvAttnArgs {
+  GemvArgs g;              // the QKV GEMV (EPI kEpiQKVX; g.tag set in-kernel)
+  AttnXArgs at;            // this layer's attention (at.t.q and at.epochs unused)
+  unsigned* class_epochs;  // [8] epoch per class (>= 1)
+};
+
+template <int HD, int G, int UKV, int IN>
+__global__ __launch_bounds__(8 * kWave) void k_qkv_attn(QkvAttnArgs a) {
+  constexpr int NW = 8, THREADS = NW * kWave, LPR = HD / 8, KPW = kWave / LPR;
+  constexpr int CH = NW * UKV * KPW;  // keys of a split held in LDS
+  static_assert(HD == 128, "a wave reads 128 of the exchange words");
+  static_assert(G * HD + sizeof(AttnCombine<HD, G, 4>) / 4 <= 4096, "combine states fit in the input stage");
+  // Two LDS arrays: the compiler then knows that the copies to kv do not
+  // write the input stage, and does not make the input's wait also wait for
+  // them.
+  __shared__ f32x4 xs[1024];           // GEMV input (K = 4096), then q + combine states
+  __shared__ u32x4 kv[2 * CH * LPR];   // keys [CH][LPR], then values [CH][LPR]
+  __shared__ float red[NW];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int b = blockIdx.x, cls = b & 7, idx = b >> 3;
+  const int S = a.at.t.S;
+  const int kvh = cls + 8 * (idx / S), si = idx % S;
+  const unsigned epoch = a.class_epochs[cls];
+  const int kin = lane / LPR, ch = lane % LPR;
+
+  // 1. the split's cached keys and values to LDS, after the GEMV input is
+  // staged and before the weights are requested (keys past the split repeat
+  // its last key and are masked; the new position's slot is replaced in 3.;
+  // an empty split copies its first in-range key, unused)
+  auto copy_kv = [&](int pos) {
+    const AttnSpan sp = attn_span<HD>(a.at.t, si, kvh, pos);
+#pragma unroll
+    for (int u = 0; u < UKV; ++u) {
+      const int t0 = (wave + u * NW) * KPW;
+      const size_t off = static_cast<size_t>(max(0, min(t0 + kin, sp.nk - 1))) * sp.key_stride;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(sp.Kb + off),
+                                       (__attribute__((address_space(3))) void*)(kv + t0 * LPR), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(sp.Vb + off),
+                                       (__attribute__((address_space(3))) void*)(kv + (CH + t0) * LPR), 16, 0, 0);
+    }
+  };
+
+  // 2. QKV
+  GemvArgs ga = a.g;
+  ga.tag = epoch;
+  int p0;
+  float bv = 0.f;
+  int bi = 0;
+  if (!gemv_run<kEpiQKVX, 2, 8, 2, THREADS, false, IN, 1>(ga, xs, red, b * NW + wave, gridDim.x * NW, p0, bv, bi,
+                                                         copy_kv))
+    return;  // the host never launches a step on a full cache
+  const AttnSpan sp = attn_span<HD>(a.at.t, si, kvh, p0);
+
+  // 3. every copy of step 1 has landed (a wave's loads complete in issue
+  // order, and each wave has waited for its weights, requested after its
+  // copies) and the input stage is free
+  lds_barrier();
+  float* qs = reinterpret_cast<float*>(xs);  // [G][HD]
+  constexpr int NA = 4, UA = UKV * NW / NA;  // waves that attend (all keys), loads of each
+  AttnCombine<HD, G, NA>& cb = *reinterpret_cast<AttnCombine<HD, G, NA>*>(qs + G * HD);
+  const bool has_p = sp.nk > 0 && p0 < sp.k0 + sp.nk;  // the split holds the new position (its last key)
+  SPoll poll{a.at.abort, 0u};
+  {
+    // wave w reads tagged words 128 w .. 128 w + 127 of the kv head's
+    // [G queries][key][value]: waves 0 .. G-1 the queries, G and G+1 the key
+    // and value (only where they are needed)
+    const int nwaves = has_p ? G + 2 : G;
+    if (wave < nwaves) {
+      const rsrc_t rx = rsrc_of(a.g.qkvx + static_cast<size_t>(kvh) * (G + 2) * HD, (G + 2) * HD * 8);
+      const int wo = (wave * kWave + lane) * 16;
+      u32x4 v = ld_t2(rx, wo, 0);
+      bool st = stale2(v, epoch);
+      while (__any(st)) {
+        if (!poll.next(lane)) break;
+        const u32x4 nv = ld_t2(rx, st ? wo : 0x40000000, 0);
+        if (st) v = nv;
+        st = st && stale2(v, epoch);
+      }
+      const int e = 2 * (wave * kWave + lane);  // word index in the kv head's block
+      if (e < G * HD) {
+        qs[e] = __uint_as_float(v[0]);
+        qs[e + 1] = __uint_as_float(v[2]);
+      } else {
+        const int d = (e - G * HD) % HD;
+        const bool is_v = e >= (G + 1) * HD;
+        half_t* row = reinterpret_cast<half_t*>(kv + ((is_v ? CH : 0) + (p0 - sp.k0)) * LPR);
+        row[d] = static_cast<half_t>(__uint_as_float(v[0]));
+        row[d + 1] = static_cast<half_t>(__uint_as_float(v[2]));
+      }
+    }
+  }
+  lds_barrier();
+  float qr[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qr[g][i] = qs[g * HD + ch * 8 + i] * a.at.t.scale_log2;
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+  }
+  if (wave < NA && sp.nk > 0) {
+    AttnLoads<UA> ld;
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int t = (wave + u * NA) * KPW + kin;
+      ld.kk[u] = kv[t * LPR + ch];
+      ld.vv[u] = kv[(CH + t) * LPR + ch];
+    }
+    attn_step<HD, G, UA, NA>(ld, wave, kin, sp.nk, qr, m, l, acc);
+  }
+
+  // 4. split state, merge
+  attn_store_state<HD, G, NA, true>(m, l, acc, cb, a.at.part, a.at.n_kv, a.at.S_max, kvh, si, epoch);
+  if (wave == 0) {
+    attn_merge_share<HD, G, false>(a.at.part, a.at.o, a.at.n_kv, a.at.S_max, kvh, si, S, epoch, epoch, poll, lane);
+    if (has_p && kvh == cls && lane == 0) a.class_epochs[cls] = epoch + 1 == 0 ? 1u : epoch + 1;
   }
 }
 

@@ -51,6 +51,7 @@ struct AttnPlan {
 // smallest of 4, 8, 16 that covers its chunk in one round.
 constexpr int kAttnSplits = 16;
 constexpr int kMaxSplits = 64;  // partial-state buffers hold this many splits per head
+constexpr int kFusedSplits = 16;  // splits per kv head of QKV fused with attention
 AttnPlan split_plan(int visible, int S) {
   S = std::max(1, std::min(S, kMaxSplits));
   const int chunk = (visible + S - 1) / S;
@@ -143,7 +144,8 @@ struct WsLayout {
   size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, best, counters, bar, attn_epochs, sphases, slayers, total;
   // tagged exchange buffers of the attention kernel and of the stream step
   // kernel (one zeroed region)
-  size_t attn_part, xt, qt, kvt, ot, actt, partt, tagged_begin, tagged_end;
+  size_t attn_part, xt, qt, kvt, ot, actt, partt, fpart, qkvx, tagged_begin, tagged_end;
+  size_t class_epochs;  // QKV fused with attention: epoch per XCD class
   int S_max;
 };
 
@@ -208,7 +210,10 @@ WsLayout ws_layout(const lf_config& c) {
   W.ot = take(D.qdim * tw);
   W.actt = take(D.ffn * tw);
   W.partt = take(static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2) * tw);
+  W.fpart = take(static_cast<size_t>(D.hq) * kFusedSplits * (D.hd + 2) * tw);
+  W.qkvx = take(static_cast<size_t>(D.qkv_rows) * tw);
   W.tagged_end = off;
+  W.class_epochs = take(8 * sizeof(unsigned));
   const std::vector<StreamPhaseShape> sp = stream_shapes(D);
   for (const StreamPhaseShape& e : sp) W.sw.push_back(take(e.bytes()));
   W.sphases = take(sp.size() * sizeof(lf::SPhase));
@@ -256,6 +261,8 @@ struct lf_model {
   std::vector<lf_kv*> kvs;               // live sequences; detached when the model is freed
   int mode = LF_MODE_GRAPH;
   bool xcd_classes = false;              // workgroups congruent modulo 8 share an XCD (probed at init)
+  bool fused_ok = false;                 // QKV and attention can run as one kernel per layer
+  bool fused = false;                    // ... and do
   const void* step_fn = nullptr;         // stream step kernel for this shape (null: unavailable)
   int step_lds = 0;                      // its LDS bytes per workgroup
   std::vector<GraphEntry> graphs;
@@ -379,6 +386,51 @@ void launch_attn(const lf::AttnXArgs& a, int hd, int G, int n_kv, bool xcd, hipS
   LF_ATTN_CASE(64, 1) LF_ATTN_CASE(64, 2) LF_ATTN_CASE(64, 4)
   LF_ATTN_CASE(128, 1) LF_ATTN_CASE(128, 2) LF_ATTN_CASE(128, 4)
 #undef LF_ATTN_CASE
+}
+
+// QKV fused with attention (k_qkv_attn): the decoder shape of 16 kv heads of
+// 128 dimensions, 2 query heads each, d 4096, whose QKV GEMV runs as 256
+// workgroups of 8 waves with two rotary pairs each, on a device whose
+// workgroups congruent modulo 8 share an XCD. Every layer has kFusedSplits
+// splits per kv head (one work item per workgroup); a split's keys must fit
+// in LDS.
+bool fused_shape(const Dims& D) {
+  const GemvShape sh = gemv_shape(lf::kEpiQKV, D.qkv_rows);
+  return D.hd == 128 && D.G == 2 && D.hkv == 16 && D.d == 4096 && sh.waves == 8 && sh.gpw == 2 && sh.blocks == 256 &&
+         D.hkv * kFusedSplits == sh.blocks;
+}
+AttnPlan fused_plan(const lf_config& c, int layer) {
+  const int visible = visible_keys(c, layer);
+  return {kFusedSplits, (visible + kFusedSplits - 1) / kFusedSplits};
+}
+// Loads per lane per wave that cover a split of `chunk` keys (8 waves, 4 keys per wave load).
+int fused_ukv(int chunk) {
+  for (int u : {1, 2, 4, 8})
+    if (32 * u >= chunk) return u;
+  return 0;
+}
+
+template <int UKV, int IN>
+const void* qkv_attn_fn() {
+  return reinterpret_cast<const void*>(&lf::k_qkv_attn<128, 2, UKV, IN>);
+}
+template <int IN>
+const void* qkv_attn_fn_in(int ukv) {
+  switch (ukv) {
+    case 1: return qkv_attn_fn<1, IN>();
+    case 2: return qkv_attn_fn<2, IN>();
+    case 4: return qkv_attn_fn<4, IN>();
+    default: return qkv_attn_fn<8, IN>();
+  }
+}
+const void* qkv_attn_kernel(int ukv, int in) {
+  return in == lf::kInNormEmbed ? qkv_attn_fn_in<lf::kInNormEmbed>(ukv) : qkv_attn_fn_in<lf::kInNormF32>(ukv);
+}
+
+void launch_qkv_attn(const lf::QkvAttnArgs& a, hipStream_t st) {
+  const int ukv = fused_ukv(a.at.t.chunk);
+  void* args[] = {const_cast<lf::QkvAttnArgs*>(&a)};
+  (void)hipLaunchKernel(qkv_attn_kernel(ukv, a.g.in_kind), dim3(256), dim3(8 * lf::kWave), args, 0, st);
 }
 
 int set_lds_limits() {
@@ -509,10 +561,9 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     a.q = m->at<float>(W.q);
     a.kc = kv->kc() + l * layer_cache;
     a.vc = kv->vc() + l * layer_cache;
-    emit_kernel(tm, st, LF_KERNEL_QKV, l, [&] { launch_gemv<lf::kEpiQKV>(a, st); });
 
     // attention over the visible keys, split over key ranges, merged in-kernel
-    const AttnPlan P = attn_plan(c, l);
+    const AttnPlan P = m->fused ? fused_plan(c, l) : attn_plan(c, l);
     lf::AttnXArgs t{};
     t.t.q = m->at<float>(W.q);
     t.t.kc = kv->kc() + l * layer_cache;
@@ -530,7 +581,19 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     t.abort = m->at<unsigned>(W.bar) + 2;
     t.S_max = W.S_max;
     t.n_kv = D.hkv;
-    emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, m->xcd_classes, st); });
+    if (m->fused) {
+      lf::QkvAttnArgs f{};
+      f.g = a;
+      f.g.qkvx = m->at<lf::u64>(W.qkvx);
+      f.at = t;
+      f.at.part = m->at<lf::u64>(W.fpart);
+      f.at.S_max = kFusedSplits;
+      f.class_epochs = m->at<unsigned>(W.class_epochs);
+      emit_kernel(tm, st, LF_KERNEL_QKV_ATTN, l, [&] { launch_qkv_attn(f, st); });
+    } else {
+      emit_kernel(tm, st, LF_KERNEL_QKV, l, [&] { launch_gemv<lf::kEpiQKV>(a, st); });
+      emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, m->xcd_classes, st); });
+    }
 
     // O projection + residual
     a = base;
@@ -746,6 +809,7 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar) + 3, 1u, size_t(1));
   // attention: split states are tagged with the kv head's epoch, which starts at 1
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.attn_epochs), 1u, size_t(D.hkv));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.class_epochs), 1u, size_t(8));
   // Stream-order copies of the repacked GEMV weights, and the tables of the
   // stream step kernel (the host copies live until the stream is
   // synchronized below).
@@ -795,6 +859,13 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
   if ((rc = probe_xcd_classes(m, st))) return bail(rc);
+  int dev = 0, ncu = 0;
+  const bool cus = hipGetDevice(&dev) == hipSuccess &&
+                   hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu >= 256;
+  (void)hipGetLastError();
+  m->fused_ok = m->xcd_classes && cus && fused_shape(D);  // its 256 workgroups wait for each other: one per CU
+  for (int l = 0; l < D.L && m->fused_ok; ++l) m->fused_ok = fused_ukv(fused_plan(*cfg, l).chunk) > 0;
+  m->fused = m->fused_ok;
   *out = m;
   return LF_OK;
 }
@@ -827,6 +898,16 @@ int lf_model_set_mode(lf_model* m, int mode) {
 }
 
 int lf_model_mode(const lf_model* m) { return m ? m->mode : -1; }
+
+int lf_model_set_fused(lf_model* m, int enabled) {
+  if (!m) return fail(LF_EINVAL, "model is null");
+  if (enabled && !m->fused_ok) return fail(LF_EINVAL, "QKV and attention cannot run fused for this shape or device");
+  if (m->fused != (enabled != 0)) drop_graphs(m, nullptr);  // recorded graphs hold the other kernels
+  m->fused = enabled != 0;
+  return LF_OK;
+}
+
+int lf_model_fused(const lf_model* m) { return m ? (m->fused ? 1 : 0) : -1; }
 
 int lf_kv_alloc(lf_model* m, void* d_buf, size_t bytes, lf_kv** out) {
   if (!m || !d_buf || !out) return fail(LF_EINVAL, "null argument");
@@ -1009,7 +1090,11 @@ int lf_kernel_time(lf_model* m, lf_kv* kv, int32_t kind, int32_t layer, int32_t 
   if (!m || !kv || !avg_ms) return fail(LF_EINVAL, "null argument");
   if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
   const bool hidden = m->D.V == 0;
-  if (kind < LF_KERNEL_QKV || kind > LF_KERNEL_DOWN) return fail(LF_EINVAL, "kind %d cannot be repeated", kind);
+  if ((kind < LF_KERNEL_QKV || kind > LF_KERNEL_DOWN) && kind != LF_KERNEL_QKV_ATTN)
+    return fail(LF_EINVAL, "kind %d cannot be repeated", kind);
+  if ((kind == LF_KERNEL_QKV_ATTN) != m->fused && (kind == LF_KERNEL_QKV || kind == LF_KERNEL_ATTN || kind == LF_KERNEL_QKV_ATTN))
+    return fail(LF_EINVAL, "kind %d is not launched by this model (QKV and attention %s)", kind,
+                m->fused ? "run fused" : "run apart");
   if (layer < -1 || layer >= m->D.L) return fail(LF_EINVAL, "layer %d out of range", layer);
   if (hidden && kind == LF_KERNEL_DOWN && (layer == m->D.L - 1 || layer < 0))
     return fail(LF_EINVAL, "the last down projection ends the step in hidden mode");

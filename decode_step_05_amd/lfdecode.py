@@ -20,13 +20,13 @@ LF_MODE_EAGER, LF_MODE_GRAPH, LF_MODE_PERSISTENT = 0, 1, 2
 # Every symbol include/lfdecode.h declares.
 EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
-    "lf_model_set_mode", "lf_model_mode",
+    "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
     "lf_step_kernel_times", "lf_kernel_time", "lf_last_error",
 )
 
-KERNEL_KINDS = ("qkv", "attn", "o", "gate_up", "down", "lm_head")
+KERNEL_KINDS = ("qkv", "attn", "o", "gate_up", "down", "lm_head", "qkv_attn")
 
 
 class lf_config(ctypes.Structure):
@@ -67,6 +67,8 @@ def load():
         "lf_model_set_graph": (c_int, [P, c_int]),
         "lf_model_set_mode": (c_int, [P, c_int]),
         "lf_model_mode": (c_int, [P]),
+        "lf_model_set_fused": (c_int, [P, c_int]),
+        "lf_model_fused": (c_int, [P]),
         "lf_kv_alloc": (c_int, [P, P, c_size_t, POINTER(P)]),
         "lf_kv_free": (None, [P]),
         "lf_kv_cache_ptrs": (c_int, [P, POINTER(P), POINTER(P)]),
@@ -184,6 +186,14 @@ def lf_model_set_mode(model, mode: int) -> None:
 
 def lf_model_mode(model) -> int:
     return load().lf_model_mode(model)
+
+
+def lf_model_set_fused(model, enabled: bool) -> None:
+    _check(load().lf_model_set_fused(model, int(bool(enabled))))
+
+
+def lf_model_fused(model) -> bool:
+    return load().lf_model_fused(model) == 1
 
 
 def lf_kv_alloc(model, buf):

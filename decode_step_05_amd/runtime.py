@@ -48,6 +48,14 @@ class Decoder:
     def set_graph(self, enabled: bool):
         C.lf_model_set_graph(self.handle, enabled)
 
+    @property
+    def fused(self) -> bool:
+        """Whether each layer's QKV projection and attention run as one kernel."""
+        return C.lf_model_fused(self.handle)
+
+    def set_fused(self, enabled: bool):
+        C.lf_model_set_fused(self.handle, enabled)
+
     def sequence(self) -> "Sequence":
         return Sequence(self)
 

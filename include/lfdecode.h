@@ -137,6 +137,21 @@ int lf_model_mode(const lf_model* m);
 int lf_model_set_graph(lf_model* m, int enabled);
 
 /*
+ * QKV fused with attention: one kernel per layer computes the QKV projection
+ * and the layer's attention (instead of LF_KERNEL_QKV then LF_KERNEL_ATTN),
+ * with each kv head's exchanges kept on one XCD of the device. Available for
+ * 16 kv heads of head_dim 128 with 2 query heads each and d_model 4096, on a
+ * device that deals a launch's workgroups to its XCDs in turn (probed by
+ * lf_model_init); the default where available. lf_model_set_fused(m, 1)
+ * returns LF_EINVAL where it is not; lf_model_set_fused(m, 0) selects the
+ * two kernels. The same computation either way (the order of floating-point
+ * sums inside attention differs). lf_model_fused returns 1 or 0 (-1 for a
+ * null model).
+ */
+int lf_model_set_fused(lf_model* m, int enabled);
+int lf_model_fused(const lf_model* m);
+
+/*
  * Bind a caller buffer (>= lf_kv_bytes, 256-byte aligned) as one sequence with
  * length 0. Layout of the caches, so a caller can fill them (K holds keys
  * after the rotary embedding):
@@ -223,13 +238,15 @@ int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
 #define LF_KERNEL_GATE_UP 3  /* RMSNorm + gate/up GEMV + SwiGLU */
 #define LF_KERNEL_DOWN 4     /* down GEMV + residual */
 #define LF_KERNEL_LM_HEAD 5  /* RMSNorm + LM head + greedy argmax */
+#define LF_KERNEL_QKV_ATTN 6 /* QKV (as LF_KERNEL_QKV) and attention in one kernel */
 int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const float* d_x_in, float* d_x_out,
                          float* ms, int32_t* kinds, int32_t cap, int32_t* n_out, void* stream);
 
 /*
  * Profiling aid: the average duration of one per-phase kernel of the step's
  * graph, launched back to back as graph replays run it. Captures `reps`
- * launches (1..256) of the kernel of kind `kind` (LF_KERNEL_QKV .. DOWN; not
+ * launches (1..256) of the kernel of kind `kind` (LF_KERNEL_QKV .. DOWN, or
+ * LF_KERNEL_QKV_ATTN, whichever the model launches; not
  * the LM head, nor in hidden mode the last layer's down projection, which end
  * the step) of layer `layer` (layer -1: of every layer in order, so that each
  * launch streams other weights, as in a step) with the arguments of the

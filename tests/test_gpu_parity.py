@@ -242,6 +242,52 @@ def test_single_layer_full_shape(cfg):
     say(f"[parity] {cfg.name}: max|d|={a:.2e} rel={r:.2e}")
 
 
+# QKV fused with attention (the default for the Laneformer layer shape):
+# positions that start, end and straddle splits, for split sizes of 32, 64,
+# 128 and 256 keys (max_ctx 512, the 1024-key window, max_ctx 2000, 4096),
+# each against the oracle and against the two-kernel path.
+_FUSED_CASES = [
+    (LAYER_FULL, (0, 1, 255, 256, 2047, 4095)),
+    (LAYER_SWA, (0, 63, 64, 1023, 1024, 1025, 3000)),
+    (LAYER_FULL.replace(max_ctx=2000, name="layer_full2000"), (124, 125, 1999)),
+    (LAYER_SWA.replace(max_ctx=512, name="layer_swa512"), (31, 32, 511)),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg,lens", _FUSED_CASES, ids=[c.name for c, _ in _FUSED_CASES])
+def test_fused_qkv_attention_positions(cfg, lens):
+    torch = _torch()
+    w = make_weights(cfg, seed=0)
+    dec = _dec(cfg, w)
+    assert dec.fused, "QKV and attention should run fused for this shape on MI355X"
+    orc = OracleDecoder(cfg, w)
+    x = make_hidden(cfg, seed=3)
+    xin = torch.from_numpy(x).cuda()
+    for kv_len in lens:
+        say(f"[parity] fused cfg={cfg.name} kv={kv_len} p={kv_len}")
+        K, V = make_kv(cfg, kv_len, seed=2)
+        seq = dec.sequence()
+        seq.load_cache(K, V)
+        out = {}
+        for fused in (True, False):
+            dec.set_fused(fused)
+            seq.set_len(kv_len)
+            xout = torch.empty_like(xin)
+            seq.step_hidden(xin, xout)
+            out[fused] = xout.cpu().numpy()
+        dec.set_fused(True)
+        cache = orc.new_cache()
+        orc.load_cache(cache, K, V)
+        want = orc.step(cache, x=x)
+        a1, r1 = assert_close(out[True], want, f"{cfg.name} fused kv={kv_len}")
+        assert_close(out[False], want, f"{cfg.name} two kernels kv={kv_len}")
+        d = float(np.max(np.abs(out[True] - out[False])))
+        assert d <= 1e-4, (kv_len, d)
+        say(f"[parity] fused {cfg.name} kv={kv_len}: max|d|={a1:.2e} rel={r1:.2e} fused-vs-two={d:.1e}")
+        del seq
+
+
 def test_lane_share_full_depth():
     # one lane's slice of all 15 layers at ctx 4096
     say("[parity] lane share kv=4095 p=4095")
@@ -283,8 +329,11 @@ def test_full_model_step_at_ctx4096():
     w = make_weights(cfg, seed=0)
     K, V = make_kv(cfg, 4095, seed=2)
     results = {}
-    for mode in ("persistent", "graph"):
-        dec = _dec(cfg, w, mode=_modes()[mode])
+    for mode in ("persistent", "graph", "graph-two-kernels"):
+        dec = _dec(cfg, w, mode=_modes()[mode.split("-")[0]])
+        if mode == "graph":
+            assert dec.fused
+        dec.set_fused(mode == "graph")
         seq = dec.sequence()
         seq.load_cache(K, V)
         seq.step(17)
