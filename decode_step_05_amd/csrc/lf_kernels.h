@@ -219,7 +219,7 @@ __device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, cons
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int i = (tid + j * THREADS) * 8;
-    if (i >= K) break;
+    if (i >= K || tid >= THREADS) break;  // threads past THREADS only take part in the barriers
 #pragma unroll
     for (int t = 0; t < 8; ++t) ss = fmaf(st.v[j][t], st.v[j][t], ss);
     if (a.resid_copy)
@@ -230,7 +230,7 @@ __device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, cons
   float r = 1.f;
   if (norm) {
     ss = wave_total(ss);
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+    if ((tid & (kWave - 1)) == 0 && tid < THREADS) red[tid / kWave] = ss;
     lds_barrier();  // not __syncthreads: its fence would wait for the weight loads in flight
     float tot = 0.f;
 #pragma unroll
@@ -240,7 +240,7 @@ __device__ __forceinline__ void stage_store(const Stage<THREADS, KMAX>& st, cons
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int q = tid + j * THREADS;
-    if (q * 8 >= K) break;
+    if (q * 8 >= K || tid >= THREADS) break;
     float g[8];
     if (norm) unpack8(st.gn[j], g);
     f32x4 o0, o1;
@@ -464,9 +464,13 @@ struct NoLoads {
   __device__ void operator()(int) const {}
 };
 
-// pre(p): further loads of the caller at position p, issued after the input
-// is staged (QKV) and before the weights.
-template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH, int IN, int MAP = 0, class Pre = NoLoads>
+// pre(p): further loads of the caller at position p, issued before the
+// input's wait and before the weights; with STH below THREADS only the
+// waves that do not stage the input should issue any (a wave's loads
+// complete in issue order, so the stagers' input wait would include them).
+// STH: the threads (the first ones of the workgroup) that stage the input.
+template <int EPI, int NR, int KCH, int GPW, int THREADS, bool COH, int IN, int MAP = 0, class Pre = NoLoads,
+          int STH = THREADS>
 __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* red, int gw, int TW, int& p, float& bv,
                                          int& bi, const Pre& pre = Pre{}) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -475,7 +479,7 @@ __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* re
   const bool full = a.K == KCH * kWave * 8;
   constexpr int KMAX = KCH * kWave * 8;
   Rows<NR, KCH> buf[2];
-  Stage<THREADS, KMAX> st;
+  Stage<STH, KMAX> st;
   // Issue order: input vector, then weights (loads retire in issue order).
   // The embedding row needs the position first; that is one kernel per step.
   // Staging the input before requesting any weight leaves HBM idle for the
@@ -488,15 +492,17 @@ __device__ __forceinline__ bool gemv_run(const GemvArgs& a, f32x4* xs, float* re
   // The position, read before any store of this launch (so with a scalar
   // load), is waited for only where it is first used.
   p = a.state[kLen];
-  if constexpr (!embed) stage_load<THREADS, KMAX, COH, IN>(st, a, 0);
-  if constexpr (stage_first) stage_store<THREADS, KMAX, IN>(st, a, xs, red);
+  if constexpr (!embed)
+    if (STH == THREADS || static_cast<int>(threadIdx.x) < STH) stage_load<STH, KMAX, COH, IN>(st, a, 0);
   pre(p);
+  if constexpr (stage_first) stage_store<STH, KMAX, IN>(st, a, xs, red);
   issue_rows<NR, KCH>(buf[0], a.W, min(row_group<MAP>(a, gw, TW, 0), ng - 1) * NR, a.rows, a.K, lane, res);
   if (GPW > 1)
     issue_rows<NR, KCH>(buf[1], a.W, min(row_group<MAP>(a, gw, TW, 1), ng - 1) * NR, a.rows, a.K, lane, res);
   if (p >= a.max_ctx) return false;  // the host never launches a step on a full cache
-  if constexpr (embed) stage_load<THREADS, KMAX, COH, IN>(st, a, p);
-  if constexpr (!stage_first) stage_store<THREADS, KMAX, IN>(st, a, xs, red);
+  if constexpr (embed)
+    if (STH == THREADS || static_cast<int>(threadIdx.x) < STH) stage_load<STH, KMAX, COH, IN>(st, a, p);
+  if constexpr (!stage_first) stage_store<STH, KMAX, IN>(st, a, xs, red);
   XRegs<KCH> xr;
   if constexpr (XRegs<KCH>::on) {
     const int K8 = a.K >> 3;
@@ -908,15 +914,18 @@ __global__ __launch_bounds__(8 * kWave) void k_qkv_attn(QkvAttnArgs a) {
   const unsigned epoch = a.class_epochs[cls];
   const int kin = lane / LPR, ch = lane % LPR;
 
-  // 1. the split's cached keys and values to LDS, after the GEMV input is
-  // staged and before the weights are requested (keys past the split repeat
-  // its last key and are masked; the new position's slot is replaced in 3.;
-  // an empty split copies its first in-range key, unused)
+  // 1. the split's cached keys and values to LDS, copied by waves 4-7 while
+  // waves 0-3 load and stage the GEMV input, before any weight is requested
+  // (keys past the split repeat its last key and are masked; the new
+  // position's slot is replaced in 3.; an empty split copies its first
+  // in-range key, unused)
+  constexpr int NS = 4, UC = UKV * NW / (NW - NS);  // input-staging waves; copies per copying wave
   auto copy_kv = [&](int pos) {
+    if (wave < NS) return;
     const AttnSpan sp = attn_span<HD>(a.at.t, si, kvh, pos);
 #pragma unroll
-    for (int u = 0; u < UKV; ++u) {
-      const int t0 = (wave + u * NW) * KPW;
+    for (int u = 0; u < UC; ++u) {
+      const int t0 = (wave - NS + u * (NW - NS)) * KPW;
       const size_t off = static_cast<size_t>(max(0, min(t0 + kin, sp.nk - 1))) * sp.key_stride;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(sp.Kb + off),
                                        (__attribute__((address_space(3))) void*)(kv + t0 * LPR), 16, 0, 0);
@@ -931,8 +940,8 @@ __global__ __launch_bounds__(8 * kWave) void k_qkv_attn(QkvAttnArgs a) {
   int p0;
   float bv = 0.f;
   int bi = 0;
-  if (!gemv_run<kEpiQKVX, 2, 8, 2, THREADS, false, IN, 1>(ga, xs, red, b * NW + wave, gridDim.x * NW, p0, bv, bi,
-                                                         copy_kv))
+  if (!gemv_run<kEpiQKVX, 2, 8, 2, THREADS, false, IN, 1, decltype(copy_kv), NS * kWave>(
+          ga, xs, red, b * NW + wave, gridDim.x * NW, p0, bv, bi, copy_kv))
     return;  // the host never launches a step on a full cache
   const AttnSpan sp = attn_span<HD>(a.at.t, si, kvh, p0);
 
