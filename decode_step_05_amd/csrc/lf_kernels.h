@@ -1084,6 +1084,30 @@ __global__ void k_put_tokens(int32_t* state, int32_t* tokens, int32_t len, const
   }
 }
 
+// Streaming read of n 16-byte words (the practical HBM read ceiling):
+// workgroup b reads its contiguous share of `per` words, each thread words
+// i, i + 256, ... with non-temporal loads, 8 in flight, folded into one word
+// that is stored only if it matches a value the data never produces (so the
+// loads are kept).
+__global__ __launch_bounds__(kBlock) void k_read_probe(const u32x4* __restrict__ p, size_t n, size_t per,
+                                                        unsigned* sink) {
+  const size_t b0 = static_cast<size_t>(blockIdx.x) * per, b1 = min(b0 + per, n);
+  unsigned acc = 0;
+  size_t i = b0 + threadIdx.x;
+  for (; i + 7 * kBlock < b1; i += 8 * kBlock) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld_stream(p + i + u * kBlock);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < b1; i += kBlock) {
+    const u32x4 v = ld_stream(p + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
 __global__ void k_copy_out(float* dst, const float* src, int n, int32_t* argmax_dst, const int32_t* state) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = src[i];

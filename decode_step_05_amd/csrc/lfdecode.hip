@@ -1085,6 +1085,38 @@ int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const f
   return LF_OK;
 }
 
+int lf_read_bandwidth(const void* d_buf, size_t bytes, int32_t iters, void* d_sink, float* gbs, void* stream) {
+  if (!d_buf || !d_sink || !gbs) return fail(LF_EINVAL, "null argument");
+  if (reinterpret_cast<uintptr_t>(d_buf) % 16 || bytes < 16 || iters < 1)
+    return fail(LF_EINVAL, "need a 16-byte aligned buffer of at least 16 bytes and iters >= 1");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t n = bytes / 16;
+  const dim3 grid(1024), block(lf::kBlock);
+  const size_t per = (n + grid.x - 1) / grid.x;
+  const auto* p = static_cast<const lf::u32x4*>(d_buf);
+  auto* sink = static_cast<unsigned*>(d_sink);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(LF_EHIP, "event create: %s", hipGetErrorString(hipGetLastError()));
+  }
+  hipLaunchKernelGGL(lf::k_read_probe, grid, block, 0, st, p, n, per, sink);  // warm-up
+  hipError_t e = hipEventRecord(e0, st);
+  for (int i = 0; i < iters && e == hipSuccess; ++i) {
+    hipLaunchKernelGGL(lf::k_read_probe, grid, block, 0, st, p, n, per, sink);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipEventRecord(e1, st);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(LF_EHIP, "read probe: %s", hipGetErrorString(e));
+  *gbs = static_cast<float>(static_cast<double>(n) * 16 * iters / (ms * 1e-3) / 1e9);
+  return LF_OK;
+}
+
 int lf_kernel_time(lf_model* m, lf_kv* kv, int32_t kind, int32_t layer, int32_t reps, int32_t iters,
                    const float* d_x_in, float* d_x_out, float* avg_ms, void* stream) {
   if (!m || !kv || !avg_ms) return fail(LF_EINVAL, "null argument");

@@ -23,7 +23,7 @@ EXPORTS = (
     "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
-    "lf_step_kernel_times", "lf_kernel_time", "lf_last_error",
+    "lf_step_kernel_times", "lf_kernel_time", "lf_read_bandwidth", "lf_last_error",
 )
 
 KERNEL_KINDS = ("qkv", "attn", "o", "gate_up", "down", "lm_head", "qkv_attn")
@@ -84,6 +84,7 @@ def load():
         "lf_step_kernel_times": (c_int, [P, P, P, P, P, POINTER(c_float), POINTER(c_int32), c_int32,
                                          POINTER(c_int32), P]),
         "lf_kernel_time": (c_int, [P, P, c_int32, c_int32, c_int32, c_int32, P, P, POINTER(c_float), P]),
+        "lf_read_bandwidth": (c_int, [P, c_size_t, c_int32, P, POINTER(c_float), P]),
         "lf_last_error": (c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -269,3 +270,13 @@ def lf_kernel_time(model, kv, kind, layer, reps=16, iters=8, x_in=None, x_out=No
     _check(load().lf_kernel_time(model, kv, k, layer, reps, iters, _ptr(x_in), _ptr(x_out), ctypes.byref(ms),
                                  _stream(stream)))
     return float(ms.value)
+
+
+def lf_read_bandwidth(buf, iters=10, stream=None) -> float:
+    """GB/s of a plain streaming read of the device tensor `buf` (see the header)."""
+    import torch
+    sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    gbs = c_float()
+    _check(load().lf_read_bandwidth(_ptr(buf), buf.numel() * buf.element_size(), iters, _ptr(sink),
+                                    ctypes.byref(gbs), _stream(stream)))
+    return float(gbs.value)

@@ -259,6 +259,19 @@ int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const f
 int lf_kernel_time(lf_model* m, lf_kv* kv, int32_t kind, int32_t layer, int32_t reps, int32_t iters,
                    const float* d_x_in, float* d_x_out, float* avg_ms, void* stream);
 
+/*
+ * Measurement aid: the practical HBM read ceiling. Reads the device buffer
+ * d_buf (bytes long, 16-byte aligned; caller-owned, not modified) `iters`
+ * times with a plain streaming kernel of 16-byte non-temporal loads (1024
+ * workgroups of 256 threads, each reading a contiguous share, 8 loads in
+ * flight per thread), after one
+ * untimed pass, between two HIP events on `stream`; waits and writes the
+ * read rate in GB/s (1e9 bytes) to *gbs. d_sink: 4 bytes of device memory the
+ * kernel may write. Use a buffer well above the 256 MB last-level cache.
+ * LF_EINVAL for null pointers, misalignment, bytes < 16 or iters < 1.
+ */
+int lf_read_bandwidth(const void* d_buf, size_t bytes, int32_t iters, void* d_sink, float* gbs, void* stream);
+
 /* Text of the calling thread's last error ("" if none). */
 const char* lf_last_error(void);
 
