@@ -44,9 +44,10 @@ struct AttnPlan {
 };
 
 // Attention splits each kv head's visible keys over at most kAttnSplits work
-// items (16 kv heads x 16 = 256 workgroups: one per CU), at least 64 keys
-// each; every split's merge reads all S split states, so more splits cost
-// more than they gain. A work item reads its keys in rounds of U loads of K
+// items (16 kv heads x 16 = 256 workgroups: one per CU), or, with fewer kv
+// heads, as many as make 256 work items in all (at most kMaxSplits per kv
+// head), at least 64 keys each; every split's merge reads all S split states,
+// so more splits than that cost more than they gain. A work item reads its keys in rounds of U loads of K
 // and of V per lane (4 waves, 512/head_dim keys per wave load), U the
 // smallest of 4, 8, 16 that covers its chunk in one round.
 constexpr int kAttnSplits = 16;
@@ -62,7 +63,9 @@ int visible_keys(const lf_config& c, int layer) {
 }
 AttnPlan attn_plan(const lf_config& c, int layer) {
   const int visible = visible_keys(c, layer);
-  return split_plan(visible, std::min(kAttnSplits, (visible + 63) / 64));
+  // up to 256 work items in all: kv heads below 16 get more splits
+  const int cap = std::max(kAttnSplits, std::min(kMaxSplits, 256 / c.n_kv_heads));
+  return split_plan(visible, std::min(cap, (visible + 63) / 64));
 }
 int attn_loads_per_lane(int chunk, int head_dim) {
   const int per_load = lf::kWavesPerBlock * (512 / head_dim);  // keys per load round of the workgroup
@@ -86,10 +89,10 @@ struct GemvShape {
 };
 
 GemvShape gemv_shape(int epi, int rows) {
-  static const int qkv[][2] = {{8, 2}, {8, 1}}, glu[][2] = {{4, 7}, {8, 2}, {8, 1}},
-                   res[][2] = {{8, 2}, {8, 1}}, lgt[][2] = {{4, 16}, {8, 2}, {8, 1}};
+  static const int qkv[][2] = {{8, 2}, {8, 1}, {2, 1}}, glu[][2] = {{4, 7}, {8, 2}, {8, 1}, {2, 1}},
+                   res[][2] = {{8, 2}, {8, 1}, {2, 1}}, lgt[][2] = {{4, 16}, {8, 2}, {8, 1}, {2, 1}};
   const int(*cand)[2] = epi == lf::kEpiQKV ? qkv : epi == lf::kEpiSwiGLU ? glu : epi == lf::kEpiResid ? res : lgt;
-  const int n = epi == lf::kEpiQKV ? 2 : epi == lf::kEpiSwiGLU ? 3 : epi == lf::kEpiResid ? 2 : 3;
+  const int n = epi == lf::kEpiQKV ? 3 : epi == lf::kEpiSwiGLU ? 4 : epi == lf::kEpiResid ? 3 : 4;
   const int nr = (epi == lf::kEpiQKV || epi == lf::kEpiSwiGLU) ? 2 : 1;
   const int ng = (rows + nr - 1) / nr;
   GemvShape best{0, 0, 0};
@@ -315,6 +318,7 @@ const void* gemv_fn_k(int waves, int gpw) {
   if (waves == 4 && gpw == 7) return gemv_fn<EPI, KCH, 7, 4, IN>();
   if (waves == 4 && gpw == 16) return gemv_fn<EPI, KCH, 16, 4, IN>();
   if (waves == 8 && gpw == 2) return gemv_fn<EPI, KCH, 2, 8, IN>();
+  if (waves == 2 && gpw == 1) return gemv_fn<EPI, KCH, 1, 2, IN>();
   return gemv_fn<EPI, KCH, 1, 8, IN>();
 }
 
@@ -353,7 +357,7 @@ void launch_gemv(const lf::GemvArgs& a, hipStream_t st) {
 template <int EPI>
 int set_lds_limit_epi() {
   const int bytes = 8192 * sizeof(float);
-  static const int shapes[][2] = {{4, 7}, {4, 16}, {8, 2}, {8, 1}};  // (waves, row groups per wave)
+  static const int shapes[][2] = {{4, 7}, {4, 16}, {8, 2}, {8, 1}, {2, 1}};  // (waves, row groups per wave)
   for (int in : {lf::kInF32, lf::kInNormF32, lf::kInNormEmbed})
     for (int K : {512, 1024, 2048, 4096, 7168, 8192})
       for (const auto& wg : shapes)
