@@ -288,6 +288,27 @@ def test_fused_qkv_attention_positions(cfg, lens):
         del seq
 
 
+def test_fusion_switch_and_kernel_kinds():
+    # QKV and attention run fused only for the Laneformer layer shape; the
+    # per-kernel timer refuses kinds the model does not launch
+    torch = _torch()
+    say("[parity] fusion switch cfg=tiny")
+    from decode_step_05_amd import lfdecode as C
+    dec = _dec(TINY, make_weights(TINY, seed=0))
+    assert not dec.fused
+    with pytest.raises(C.LfError):
+        dec.set_fused(True)
+    dec.set_fused(False)
+    seq = dec.sequence()
+    seq.prefill(np.array([1, 2, 3], dtype=np.int32))
+    with pytest.raises(C.LfError):
+        C.lf_kernel_time(dec.handle, seq.handle, "qkv_attn", -1, reps=1, iters=1)
+    assert C.lf_kernel_time(dec.handle, seq.handle, "qkv", -1, reps=1, iters=1) > 0
+    say("[parity] read bandwidth probe")
+    buf = torch.ones(1 << 20, dtype=torch.float32, device="cuda")
+    assert C.lf_read_bandwidth(buf, iters=2) > 0
+
+
 def test_lane_share_full_depth():
     # one lane's slice of all 15 layers at ctx 4096
     say("[parity] lane share kv=4095 p=4095")

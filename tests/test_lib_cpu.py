@@ -120,3 +120,16 @@ def test_null_handles_rejected():
     assert lib.lf_kv_len(None) == -1
     lib.lf_model_free(None)
     lib.lf_kv_free(None)
+    assert lib.lf_model_set_fused(None, 1) == C.LF_EINVAL
+    assert lib.lf_model_fused(None) == -1
+
+
+def test_read_bandwidth_argument_errors_before_any_device_call():
+    lib = C.load()
+    g = ctypes.c_float()
+    assert lib.lf_read_bandwidth(None, 1 << 20, 1, 0x1000, ctypes.byref(g), None) == C.LF_EINVAL
+    assert lib.lf_read_bandwidth(0x1000, 1 << 20, 1, None, ctypes.byref(g), None) == C.LF_EINVAL
+    rc = lib.lf_read_bandwidth(0x1008, 1 << 20, 1, 0x1000, ctypes.byref(g), None)
+    assert rc == C.LF_EINVAL and "aligned" in C.lf_last_error()
+    assert lib.lf_read_bandwidth(0x1000, 8, 1, 0x1000, ctypes.byref(g), None) == C.LF_EINVAL
+    assert lib.lf_read_bandwidth(0x1000, 1 << 20, 0, 0x1000, ctypes.byref(g), None) == C.LF_EINVAL
