@@ -89,10 +89,10 @@ struct GemvShape {
 };
 
 GemvShape gemv_shape(int epi, int rows) {
-  static const int qkv[][2] = {{8, 2}, {8, 1}, {2, 1}}, glu[][2] = {{4, 7}, {8, 2}, {8, 1}, {2, 1}},
-                   res[][2] = {{8, 2}, {8, 1}, {2, 1}}, lgt[][2] = {{4, 16}, {8, 2}, {8, 1}, {2, 1}};
+  static const int qkv[][2] = {{8, 2}, {8, 1}, {2, 1}}, glu[][2] = {{2, 7}, {8, 2}, {8, 1}, {2, 1}},
+                   res[][2] = {{4, 4}, {8, 2}, {8, 1}, {2, 1}}, lgt[][2] = {{4, 16}, {8, 2}, {8, 1}, {2, 1}};
   const int(*cand)[2] = epi == lf::kEpiQKV ? qkv : epi == lf::kEpiSwiGLU ? glu : epi == lf::kEpiResid ? res : lgt;
-  const int n = epi == lf::kEpiQKV ? 3 : epi == lf::kEpiSwiGLU ? 4 : epi == lf::kEpiResid ? 3 : 4;
+  const int n = epi == lf::kEpiQKV ? 3 : 4;
   const int nr = (epi == lf::kEpiQKV || epi == lf::kEpiSwiGLU) ? 2 : 1;
   const int ng = (rows + nr - 1) / nr;
   GemvShape best{0, 0, 0};
@@ -315,7 +315,8 @@ const void* gemv_fn() {
 
 template <int EPI, int KCH, int IN>
 const void* gemv_fn_k(int waves, int gpw) {
-  if (waves == 4 && gpw == 7) return gemv_fn<EPI, KCH, 7, 4, IN>();
+  if (waves == 2 && gpw == 7) return gemv_fn<EPI, KCH, 7, 2, IN>();
+  if (waves == 4 && gpw == 4) return gemv_fn<EPI, KCH, 4, 4, IN>();
   if (waves == 4 && gpw == 16) return gemv_fn<EPI, KCH, 16, 4, IN>();
   if (waves == 8 && gpw == 2) return gemv_fn<EPI, KCH, 2, 8, IN>();
   if (waves == 2 && gpw == 1) return gemv_fn<EPI, KCH, 1, 2, IN>();
@@ -357,7 +358,7 @@ void launch_gemv(const lf::GemvArgs& a, hipStream_t st) {
 template <int EPI>
 int set_lds_limit_epi() {
   const int bytes = 8192 * sizeof(float);
-  static const int shapes[][2] = {{4, 7}, {4, 16}, {8, 2}, {8, 1}, {2, 1}};  // (waves, row groups per wave)
+  static const int shapes[][2] = {{2, 7}, {4, 4}, {4, 16}, {8, 2}, {8, 1}, {2, 1}};  // (waves, row groups per wave)
   for (int in : {lf::kInF32, lf::kInNormF32, lf::kInNormEmbed})
     for (int K : {512, 1024, 2048, 4096, 7168, 8192})
       for (const auto& wg : shapes)
