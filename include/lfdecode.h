@@ -141,12 +141,13 @@ int lf_model_set_graph(lf_model* m, int enabled);
  * and the layer's attention (instead of LF_KERNEL_QKV then LF_KERNEL_ATTN),
  * with each kv head's exchanges kept on one XCD of the device. Available for
  * 16 kv heads of head_dim 128 with 2 query heads each and d_model 4096, on a
- * device that deals a launch's workgroups to its XCDs in turn (probed by
- * lf_model_init); the default where available. lf_model_set_fused(m, 1)
- * returns LF_EINVAL where it is not; lf_model_set_fused(m, 0) selects the
- * two kernels. The same computation either way (the order of floating-point
- * sums inside attention differs). lf_model_fused returns 1 or 0 (-1 for a
- * null model).
+ * device of at least 256 CUs that deals a launch's workgroups to its XCDs in
+ * turn (probed by lf_model_init); the default where available.
+ * lf_model_set_fused(m, 1) returns LF_EINVAL where it is not;
+ * lf_model_set_fused(m, 0) selects the two kernels. A switch applies from the
+ * next step (recorded graphs are discarded). The same computation either way
+ * (the order of floating-point sums inside attention differs).
+ * lf_model_fused returns 1 or 0 (-1 for a null model).
  */
 int lf_model_set_fused(lf_model* m, int enabled);
 int lf_model_fused(const lf_model* m);
