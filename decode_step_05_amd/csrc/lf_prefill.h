@@ -1,0 +1,373 @@
+// Batched prompt pass (prefill) for gfx950: the decoder applied to a chunk of
+// prompt positions at once. Every projection becomes a GEMM of the chunk's
+// activations with the layer's fp16 weights on the matrix cores
+// (v_mfma_f32_32x32x16_f16, fp32 accumulation), attention is causal / sliding
+// window over the cache with the same matrix instructions, and the keys and
+// values land in the cache layout the decode step reads. It computes the same
+// function as one decode step per prompt position (the decoder of the
+// Laneformer blog post, "Designing the architecture": pre-norm GQA decoder,
+// sliding-window attention on some layers). Activations stay fp32 as in the
+// decode step: an fp32 operand of a matrix instruction is fed as the sum of
+// two fp16 parts (hi = fp16(a), lo = fp16(a - hi), about 22 significant bits),
+// each multiplied with the fp16 weights or values, fp32 accumulation.
+#pragma once
+#include "lf_device.h"
+
+namespace lf {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- GEMM
+// C[M][N] (=, +=) A[M][K] · W[N][K]^T. A: activations, fp32 row-major, split
+// into hi and lo fp16 parts on the way into LDS; W: a weight matrix as the
+// model stores it, fp16 row-major [out][in]; C fp32.
+// Workgroup tile 128 x 128, K step 64, four waves of 64 x 64 (2 x 2 blocks of
+// 32 x 32). A 32x32x16 matrix instruction takes, in lane l, row l % 32 of its
+// A block and column l % 32 of its B block with 8 consecutive k each (k group
+// l / 32), and returns in lane l column l % 32, rows 8 (r / 4) + 4 (l / 32) +
+// r % 4 of register r. Both operands are K-contiguous rows here (activation
+// rows, weight rows), so each lane reads 16 contiguous bytes per operand.
+constexpr int kPfBM = 128, kPfBN = 128, kPfBK = 64, kPfThreads = 256;
+constexpr int kPfLd = kPfBK + 8;  // LDS row stride in halves (144 B: rows 4 banks apart)
+
+enum PfEpi : int { kPfStore = 0, kPfAccum = 1 };
+
+struct PfGemmArgs {
+  const float* A;
+  const half_t* W;
+  float* C;
+  int M, N, K;  // K a multiple of 8
+  int tiles_m, tiles_n;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t As[kPfBM * kPfLd];  // hi parts of the activations
+  __shared__ __attribute__((aligned(16))) half_t Al[kPfBM * kPfLd];  // lo parts
+  __shared__ __attribute__((aligned(16))) half_t Bs[kPfBN * kPfLd];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // Workgroups are dealt to the 8 XCDs in turn: give each XCD a contiguous
+  // run of tiles, N-major, so the M tiles that share a weight tile share an L2.
+  const int T = a.tiles_m * a.tiles_n, b = blockIdx.x;
+  const int t = (T & 7) ? b : (b & 7) * (T >> 3) + (b >> 3);
+  const int m0 = (t % a.tiles_m) * kPfBM, n0 = (t / a.tiles_m) * kPfBN;
+
+  // loader: weight chunk i of this thread is row (tid / 8) + 32 i, halves
+  // (tid % 8) * 8 of the K step; activation chunk i is row (tid / 16) + 16 i,
+  // floats (tid % 16) * 4
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+  const int arow = tid >> 4, acol = (tid & 15) * 4;
+  const float* ap[8];
+  const half_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ap[i] = a.A + static_cast<size_t>(min(m0 + arow + 16 * i, a.M - 1)) * a.K + acol;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bp[i] = a.W + static_cast<size_t>(min(n0 + lrow + 32 * i, a.N - 1)) * a.K + lcol;
+  f32x4 ra[8];
+  u32x4 rb[4];
+  auto load = [&](int k0) {
+    const bool ina = k0 + acol < a.K, inb = k0 + lcol < a.K;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ra[i] = ina ? *reinterpret_cast<const f32x4*>(ap[i] + k0) : zf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[i] = inb ? ld16(bp[i] + k0) : z;
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  load(0);
+  for (int k0 = 0; k0 < a.K; k0 += kPfBK) {
+    __syncthreads();  // every wave is done reading the previous K step
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = static_cast<half_t>(ra[i][e]);
+        lo[e] = static_cast<half_t>(ra[i][e] - static_cast<float>(hi[e]));
+      }
+      *reinterpret_cast<h4*>(&As[(arow + 16 * i) * kPfLd + acol]) = hi;
+      *reinterpret_cast<h4*>(&Al[(arow + 16 * i) * kPfLd + acol]) = lo;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Bs[(lrow + 32 * i) * kPfLd + lcol]) = rb[i];
+    __syncthreads();
+    if (k0 + kPfBK < a.K) load(k0 + kPfBK);
+#pragma unroll
+    for (int kk = 0; kk < kPfBK / 16; ++kk) {
+      h8 af[2], al[2], bf[2];
+      const int col = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const h8*>(&As[(wm * 64 + i * 32 + (lane & 31)) * kPfLd + col]);
+        al[i] = *reinterpret_cast<const h8*>(&Al[(wm * 64 + i * 32 + (lane & 31)) * kPfLd + col]);
+        bf[i] = *reinterpret_cast<const h8*>(&Bs[(wn * 64 + i * 32 + (lane & 31)) * kPfLd + col]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < a.M && n < a.N) {
+          float* c = a.C + static_cast<size_t>(m) * a.N + n;
+          if constexpr (EPI == kPfAccum)
+            *c += acc[i][j][r];
+          else
+            *c = acc[i][j][r];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------- attention
+// Causal attention of a chunk of query positions over the cache, with the
+// sliding window where the layer has one: keys j with p - W < j <= p for the
+// query at position p (all j <= p when W = 0). Workgroup: 32 consecutive query
+// positions and one kv head; wave w handles query head G·kvh + w (the G query
+// heads of a kv head share its keys and values). Per 32-key tile a wave forms
+// S^T = K · Q^T (so lane l owns query l % 32 and 16 of the 32 keys; its
+// partner lane l ^ 32 holds the other 16), applies the mask, updates an online
+// softmax (running max and denominator per query), and adds V^T · P^T into
+// O^T (HD x 32 queries). Q^T and P^T are fed as hi + lo fp16 parts. V is
+// staged transposed in LDS so that each lane reads its keys for one head
+// dimension contiguously.
+struct PfAttnArgs {
+  const float* q;    // [M][n_q][hd] rotated queries of the chunk
+  const half_t* kc;  // this layer's K cache [lanes][max_ctx][kpl][hd], keys 0..pos0+M-1 written
+  const half_t* vc;
+  float* o;          // [M][n_q * hd] attention outputs (input of the O projection)
+  int M, pos0, max_ctx, window, kpl, n_q;
+  float scale_log2;  // log2(e) / sqrt(hd)
+};
+
+template <int HD, int G>
+__global__ __launch_bounds__(G * kWave) void k_pf_attn(PfAttnArgs a) {
+  constexpr int VLD = 32 + 4;  // V^T row stride in halves
+  __shared__ __attribute__((aligned(16))) half_t Vt[HD * VLD];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int qb = blockIdx.x, kvh = blockIdx.y;
+  const int head = kvh * G + w;
+  const int ln = kvh / a.kpl, hk = kvh % a.kpl;
+  const int q_first = a.pos0 + qb * 32;
+  const int q_last = min(q_first + 31, a.pos0 + a.M - 1);
+  const int qrow = qb * 32 + (lane & 31);  // chunk row of this lane's query (past M in the last block)
+  const int qpos = a.pos0 + qrow;
+  const int grp = lane >> 5;
+
+  h8 qf[HD / 16], ql[HD / 16];
+  {
+    const float* qp = a.q + (static_cast<size_t>(min(qrow, a.M - 1)) * a.n_q + head) * HD + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) {
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(qp + kk * 16);
+      const f32x4 u1 = *reinterpret_cast<const f32x4*>(qp + kk * 16 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = e < 4 ? u0[e] : u1[e - 4];
+        qf[kk][e] = static_cast<half_t>(v);
+        ql[kk][e] = static_cast<half_t>(v - static_cast<float>(qf[kk][e]));
+      }
+    }
+  }
+  const size_t kstride = static_cast<size_t>(a.kpl) * HD;  // between consecutive positions
+  const size_t base = (static_cast<size_t>(ln) * a.max_ctx * a.kpl + hk) * HD;
+  const half_t* kbase = a.kc + base;
+  const half_t* vbase = a.vc + base;
+  const int k_lo = (a.window ? max(0, q_first - a.window + 1) : 0) & ~31;
+  const int k_hi = q_last;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 ot[HD / 32];
+#pragma unroll
+  for (int th = 0; th < HD / 32; ++th)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ot[th][r] = 0.f;
+
+  for (int k0 = k_lo; k0 <= k_hi; k0 += 32) {
+    // keys of this tile (A operand of S^T): row l % 32, hd group l / 32
+    h8 kf[HD / 16];
+    {
+      const half_t* kp = kbase + static_cast<size_t>(min(k0 + (lane & 31), k_hi)) * kstride + grp * 8;
+#pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = *reinterpret_cast<const h8*>(kp + kk * 16);
+    }
+    __syncthreads();  // every wave is done reading the previous tile's V^T
+    for (int c = tid; c < 32 * HD / 8; c += G * kWave) {
+      const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
+      const h8 v = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(k0 + key, k_hi)) * kstride + d8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(d8 + e) * VLD + key] = v[e];
+    }
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qf[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], ql[kk], s, 0, 0, 0);
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
+      const bool vis = key <= qpos && (a.window == 0 || key > qpos - a.window);
+      s[r] = vis ? s[r] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
+    h8 pf[2], pl[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = s[r] == -INFINITY ? 0.f : exp2f(s[r] - m_new);
+      ps += p;
+      pf[r >> 3][r & 7] = static_cast<half_t>(p);
+      pl[r >> 3][r & 7] = static_cast<half_t>(p - static_cast<float>(pf[r >> 3][r & 7]));
+    }
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int th = 0; th < HD / 32; ++th)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ot[th][r] *= alpha;
+    __syncthreads();  // V^T of this tile staged
+    // P^T in B-operand order: register r = 8 mm + s holds key 16 mm + 8 (s / 4) + 4 grp + s % 4,
+    // which is where the A operand (V^T) takes its k slot s from
+#pragma unroll
+    for (int th = 0; th < HD / 32; ++th)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const half_t* vr = &Vt[(th * 32 + (lane & 31)) * VLD + 16 * mm + 4 * grp];
+        const h4 v0 = *reinterpret_cast<const h4*>(vr);
+        const h4 v1 = *reinterpret_cast<const h4*>(vr + 8);
+        const h8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        ot[th] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[mm], ot[th], 0, 0, 0);
+        ot[th] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[mm], ot[th], 0, 0, 0);
+      }
+  }
+
+  if (qrow < a.M) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* op = a.o + static_cast<size_t>(qrow) * a.n_q * HD + head * HD;
+#pragma unroll
+    for (int th = 0; th < HD / 32; ++th)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) op[th * 32 + 8 * (r >> 2) + 4 * grp + (r & 3)] = ot[th][r] * inv;
+  }
+}
+
+// ------------------------------------------------------- elementwise
+// RMSNorm of each residual row (x / sqrt(mean(x^2) + eps) · gain);
+// with emb set, the row is first loaded from the embedding of its token.
+struct PfNormArgs {
+  float* x;            // [M][d] residual
+  float* h;            // [M][d]
+  const half_t* gain;
+  const half_t* emb;   // [vocab][d], or null
+  const int32_t* tokens;
+  int32_t* state;
+  int M, d, vocab, tok0;  // row t holds token tokens[tok0 + t]
+  float eps;
+};
+
+__global__ __launch_bounds__(kBlock) void k_pf_norm(PfNormArgs a) {
+  __shared__ float red[kWavesPerBlock];
+  const int t = blockIdx.x;
+  float* x = a.x + static_cast<size_t>(t) * a.d;
+  if (a.emb) {
+    int tok = a.tokens[a.tok0 + t];
+    if (tok < 0 || tok >= a.vocab) {
+      tok = tok < 0 ? 0 : a.vocab - 1;
+      if (threadIdx.x == 0) a.state[kBadToken] = 1;
+    }
+    const half_t* e = a.emb + static_cast<size_t>(tok) * a.d;
+    for (int i = threadIdx.x; i < a.d; i += kBlock) x[i] = static_cast<float>(e[i]);
+  }
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < a.d; i += kBlock) ss = fmaf(x[i], x[i], ss);
+  const float inv = rsqrtf(block_sum(ss, red) / a.d + a.eps);
+  float* h = a.h + static_cast<size_t>(t) * a.d;
+  for (int i = threadIdx.x; i < a.d; i += kBlock) h[i] = x[i] * inv * static_cast<float>(a.gain[i]);
+}
+
+// Rotary embedding and cache append for the QKV GEMM's output, whose columns
+// follow the model's lane-major row order (per lane: its query heads, key
+// heads, value heads; within a head, dimensions c and c + hd/2 adjacent).
+struct PfQkvArgs {
+  const float* y;  // [M][rows]
+  float* q;        // [M][n_q][hd]
+  half_t* kc;      // this layer's cache
+  half_t* vc;
+  const float2* rope;  // [max_ctx][hd/2] (cos, sin)
+  int M, rows, hd, qpl, kpl, n_q, max_ctx, pos0;
+};
+
+__global__ __launch_bounds__(kBlock) void k_pf_qkv(PfQkvArgs a) {
+  const int i = blockIdx.x * kBlock + threadIdx.x, t = blockIdx.y;
+  if (2 * i >= a.rows) return;
+  const float2 y = reinterpret_cast<const float2*>(a.y + static_cast<size_t>(t) * a.rows)[i];
+  const int r = 2 * i, half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl, p = a.pos0 + t;
+  const int u = r / a.hd, c = (r % a.hd) >> 1;
+  const int ln = u / upl, j = u % upl;
+  float y0 = y.x, y1 = y.y;
+  if (j < a.qpl + a.kpl) {
+    const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
+    y0 = y.x * cs.x - y.y * cs.y;
+    y1 = y.x * cs.y + y.y * cs.x;
+  }
+  if (j < a.qpl) {
+    float* qh = a.q + (static_cast<size_t>(t) * a.n_q + ln * a.qpl + j) * a.hd;
+    qh[c] = y0;
+    qh[c + half_hd] = y1;
+  } else {
+    const bool is_k = j < a.qpl + a.kpl;
+    const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
+    half_t* dst = (is_k ? a.kc : a.vc) + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
+    dst[c] = static_cast<half_t>(y0);
+    dst[c + half_hd] = static_cast<half_t>(y1);
+  }
+}
+
+// SwiGLU over the gate/up GEMM's output (gate f and up f in columns 2f, 2f+1).
+__global__ __launch_bounds__(kBlock) void k_pf_swiglu(const float* y, float* act, int ffn) {
+  const int f = blockIdx.x * kBlock + threadIdx.x, t = blockIdx.y;
+  if (f >= ffn) return;
+  const float2 gu = reinterpret_cast<const float2*>(y + static_cast<size_t>(t) * 2 * ffn)[f];
+  act[static_cast<size_t>(t) * ffn + f] = gu.x / (1.0f + expf(-gu.x)) * gu.y;
+}
+
+// Hand the last prompt position's residual to the decode step's LM head and
+// point the sequence at that position (its LM head then advances it).
+__global__ __launch_bounds__(kBlock) void k_pf_finish(const float* xrow, float* x, int d, int32_t* state, int32_t pos) {
+  for (int i = threadIdx.x; i < d; i += kBlock) x[i] = xrow[i];
+  if (threadIdx.x == 0) state[kLen] = pos;
+}
+
+}  // namespace lf

@@ -4,6 +4,7 @@
 #include "lfdecode.h"
 #include "lf_kernels.h"
 #include "lf_stream.h"
+#include "lf_prefill.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -690,6 +691,75 @@ void drop_graphs(lf_model* m, lf_kv* kv) {
   m->graphs.swap(keep);
 }
 
+// Scratch of the batched prompt pass for chunks of mc positions.
+struct PfLayout {
+  size_t x, y, h, q, total;
+};
+
+PfLayout pf_layout(const Dims& D, int mc) {
+  PfLayout P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t rows = static_cast<size_t>(mc);
+  P.x = take(rows * D.d * sizeof(float));
+  P.y = take(rows * std::max(D.qkv_rows, 2 * D.ffn) * sizeof(float));
+  P.h = take(rows * std::max(std::max(D.d, D.ffn), D.qdim) * sizeof(float));
+  P.q = take(rows * D.qdim * sizeof(float));
+  P.total = off;
+  return P;
+}
+
+template <int EPI>
+void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int K, hipStream_t st) {
+  lf::PfGemmArgs g{A, W, C, M, N, K, (M + lf::kPfBM - 1) / lf::kPfBM, (N + lf::kPfBN - 1) / lf::kPfBN};
+  hipLaunchKernelGGL(lf::k_pf_gemm<EPI>, dim3(g.tiles_m * g.tiles_n), dim3(lf::kPfThreads), 0, st, g);
+}
+
+void launch_pf_attn(const lf::PfAttnArgs& a, int hd, int G, int n_kv, hipStream_t st) {
+  const dim3 grid((a.M + 31) / 32, n_kv);
+#define LF_PF_ATTN(HD, GG)                                                                   \
+  if (hd == HD && G == GG) {                                                                 \
+    hipLaunchKernelGGL((lf::k_pf_attn<HD, GG>), grid, dim3(GG * lf::kWave), 0, st, a);      \
+    return;                                                                                  \
+  }
+  LF_PF_ATTN(128, 1) LF_PF_ATTN(128, 2) LF_PF_ATTN(128, 4)
+  LF_PF_ATTN(64, 1) LF_PF_ATTN(64, 2) LF_PF_ATTN(64, 4)
+  LF_PF_ATTN(32, 1) LF_PF_ATTN(32, 2) LF_PF_ATTN(32, 4)
+#undef LF_PF_ATTN
+}
+
+// One chunk of the batched prompt pass: M positions from pos0 through every
+// layer (the residual rows end in P.x).
+void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M, int pos0, hipStream_t st) {
+  const Dims& D = m->D;
+  const WsLayout& W = m->W;
+  const lf_config& c = m->cfg;
+  const size_t layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
+  float* x = reinterpret_cast<float*>(ws + P.x);
+  float* y = reinterpret_cast<float*>(ws + P.y);
+  float* h = reinterpret_cast<float*>(ws + P.h);
+  float* q = reinterpret_cast<float*>(ws + P.q);
+  for (int l = 0; l < D.L; ++l) {
+    lf::PfNormArgs na{x, h, m->at<half_t>(W.g1[l]), l == 0 ? m->at<half_t>(W.embed) : nullptr, kv->tokens(), kv->state(),
+                      M, D.d, D.V, pos0, c.rms_eps};
+    hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
+    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wqkv[l]), y, M, D.qkv_rows, D.d, st);
+    lf::PfQkvArgs qa{y, q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, m->at<float2>(W.rope),
+                     M, D.qkv_rows, D.hd, D.qpl, D.kpl, D.hq, D.ctx, pos0};
+    hipLaunchKernelGGL(lf::k_pf_qkv, dim3((D.qkv_rows / 2 + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, qa);
+    lf::PfAttnArgs aa{q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, h, M, pos0, D.ctx, c.window[l], D.kpl,
+                      D.hq, static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)))};
+    launch_pf_attn(aa, D.hd, D.G, D.hkv, st);
+    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wo[l]), x, M, D.d, D.qdim, st);
+    na.gain = m->at<half_t>(W.g2[l]);
+    na.emb = nullptr;
+    hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
+    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, st);
+    hipLaunchKernelGGL(lf::k_pf_swiglu, dim3((D.ffn + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, y, h, D.ffn);
+    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, st);
+  }
+}
+
 }  // namespace
 
 // ===================================================================== C ABI
@@ -991,6 +1061,61 @@ int lf_prefill(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, void*
     if (rc) return rc;
     kv->len += 1;
   }
+  return LF_OK;
+}
+
+size_t lf_prefill_workspace_bytes(const lf_config* cfg, int32_t chunk) {
+  if (validate(cfg) != LF_OK || chunk < 1 || chunk > LF_MAX_PREFILL_CHUNK) return 0;
+  return pf_layout(dims(*cfg), chunk).total;
+}
+
+int lf_prefill_batched(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, int32_t chunk, void* d_workspace,
+                       size_t ws_bytes, void* stream) {
+  if (!m || !kv || !d_tokens || !d_workspace) return fail(LF_EINVAL, "null argument");
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  if (m->D.V == 0) return fail(LF_EINVAL, "lf_prefill_batched needs vocab > 0");
+  if (n < 1) return fail(LF_EINVAL, "n = %d < 1", n);
+  if (chunk < 1 || chunk > LF_MAX_PREFILL_CHUNK) return fail(LF_EINVAL, "chunk %d out of [1, %d]", chunk, LF_MAX_PREFILL_CHUNK);
+  if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign) return fail(LF_EINVAL, "workspace not 256-byte aligned");
+  const PfLayout P = pf_layout(m->D, chunk);
+  if (ws_bytes < P.total) return fail(LF_EINVAL, "workspace %zu bytes < %zu needed for chunk %d", ws_bytes, P.total, chunk);
+  if (static_cast<long>(kv->len) + n > m->D.ctx) return fail(LF_ERANGE, "len %d + n %d > max_ctx %d", kv->len, n, m->D.ctx);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(d_workspace);
+  hipLaunchKernelGGL(lf::k_put_tokens, dim3((n + 255) / 256), dim3(256), 0, st, kv->state(), kv->tokens(), kv->len, d_tokens, n);
+  int last = 0;
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    last = std::min(chunk, n - c0);
+    enqueue_pf_chunk(m, kv, ws, P, last, kv->len + c0, st);
+  }
+  const Dims& D = m->D;
+  const WsLayout& W = m->W;
+  hipLaunchKernelGGL(lf::k_pf_finish, dim3(1), dim3(lf::kBlock), 0, st,
+                     reinterpret_cast<const float*>(ws + P.x) + static_cast<size_t>(last - 1) * D.d, m->at<float>(W.x), D.d,
+                     kv->state(), kv->len + n - 1);
+  // final RMSNorm + LM head + greedy argmax of the last position (the decode step's kernel)
+  lf::GemvArgs a{};
+  a.eps = m->cfg.rms_eps;
+  a.vocab = D.V;
+  a.state = kv->state();
+  a.tokens = kv->tokens();
+  a.max_ctx = D.ctx;
+  a.hd = D.hd;
+  a.qpl = D.qpl;
+  a.kpl = D.kpl;
+  a.rope = m->at<float2>(W.rope);
+  a.W = m->at<half_t>(W.lm);
+  a.rows = D.V;
+  a.K = D.d;
+  a.in_kind = lf::kInNormF32;
+  a.x = m->at<float>(W.x);
+  a.gain = m->at<half_t>(W.gf);
+  a.y = kv->logits();
+  a.counter = m->at<unsigned>(W.counters) + D.hkv;
+  a.best = m->at<unsigned long long>(W.best);
+  launch_gemv<lf::kEpiLogits>(a, st);
+  LF_HIP(hipPeekAtLastError());
+  kv->len += n;
   return LF_OK;
 }
 

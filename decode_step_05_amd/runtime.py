@@ -114,6 +114,22 @@ class Sequence:
         t = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(self.dec.device) if not torch.is_tensor(tokens) else tokens
         C.lf_prefill(self.dec.handle, self.handle, t.to(torch.int32).contiguous(), None, stream)
 
+    def prefill_batched(self, tokens, chunk=1024, stream=None):
+        """The prompt pass on the matrix cores, `chunk` positions at a time
+        (lf_prefill_batched); its scratch is allocated here with torch and
+        kept for later calls of the same or a smaller chunk."""
+        torch = _torch()
+        t = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(self.dec.device) if not torch.is_tensor(tokens) else tokens
+        t = t.to(self.dec.device, torch.int32).contiguous()
+        chunk = max(1, min(int(chunk), t.numel()))
+        need = C.lf_prefill_workspace_bytes(self.dec.c, chunk)
+        if need == 0:
+            raise ValueError(f"chunk {chunk} is not a valid prompt-pass chunk")
+        ws = getattr(self, "_pf_ws", None)
+        if ws is None or ws.numel() < need:
+            ws = self._pf_ws = torch.empty(need, dtype=torch.uint8, device=self.dec.device)
+        C.lf_prefill_batched(self.dec.handle, self.handle, t, chunk, ws, None, stream)
+
     def step(self, token=None, stream=None):
         """token: None (feed the previous greedy token), an int, or a device int32 tensor."""
         torch = _torch()

@@ -191,6 +191,36 @@ int lf_kv_tokens(const lf_kv* kv, int32_t* d_out, int32_t start, int32_t n, void
 int lf_prefill(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, void* stream);
 
 /*
+ * Batched prompt pass. The prompt is consumed in one pass before decoding (the
+ * asector summary, "Performance and infrastructure", times a whole generation
+ * pass), and across the prompt's positions every projection of the decoder
+ * (the blog post, "Designing the architecture") is a matrix product.
+ *
+ * Same result and state as lf_prefill: it appends n positions (tokens
+ * d_tokens[0..n), device int32), writes their keys and values to the cache, and
+ * leaves the logits and greedy argmax of the last position. The positions are
+ * taken `chunk` at a time (1 <= chunk <= LF_MAX_PREFILL_CHUNK). In each chunk,
+ * each layer runs:
+ *   - the projections as matrix-core GEMMs of the fp32 activations with the
+ *     fp16 weights, fp32 accumulation. Each activation goes in as two fp16
+ *     parts, hi = fp16(a) and lo = fp16(a - hi), about 22 significant bits;
+ *     the residual stays fp32 as in the decode step;
+ *   - causal / sliding-window attention over the cache, on the matrix cores,
+ *     with the queries and the softmax weights split the same way.
+ *
+ * d_workspace: caller-owned device scratch, 256-byte aligned, at least
+ * lf_prefill_workspace_bytes(cfg, chunk) bytes. Its contents do not matter
+ * before or after the call. It must not be used by another call until the
+ * stream has passed this one.
+ * LF_EINVAL: null arguments, vocab == 0, n < 1, bad chunk, or a small or
+ * unaligned workspace. LF_ERANGE: len + n > max_ctx. Enqueued on stream.
+ */
+#define LF_MAX_PREFILL_CHUNK 4096
+size_t lf_prefill_workspace_bytes(const lf_config* cfg, int32_t chunk);  /* 0 if cfg or chunk is invalid */
+int lf_prefill_batched(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, int32_t chunk, void* d_workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
  * Append one position. d_token (device int32) gives its token id; NULL feeds
  * the greedy argmax of the previous position, which stays on the device.
  * Leaves the logits and argmax of the new position. LF_ERANGE if len == max_ctx.

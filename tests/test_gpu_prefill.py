@@ -1,0 +1,195 @@
+"""GPU parity of the batched prompt pass (lf_prefill_batched: matrix-core
+GEMMs and attention over chunks of the prompt) against the CPU oracle, through
+the C ABI.
+
+For every shape: the logits and greedy token of the last prompt position, the
+keys and values written to the cache (compared with the oracle's
+full-sequence pass, which fills its cache as decoding would), and decode
+steps that continue from the batched pass. The chunk sizes leave ragged
+chunks, and the sliding windows are narrower than a chunk. The 15-layer
+decoder's 3584-token prompt is compared with the stored oracle results of
+that workload. Acceptance: tests/parity.py.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import OracleDecoder
+from synth import TINY, WORKLOADS, DecoderConfig, make_prompt, make_weights
+
+from parity import MAX_ABS, MAX_REL, assert_close, check_token, greedy_fp32, vec_err
+from test_gpu_parity import RAGGED, WIDE_GROUP
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# one query head per kv head (G = 1) at head_dim 128, 3 lanes, a window
+# narrower than the chunk on the second layer
+MHA = DecoderConfig("mha", n_layers=2, d_model=384, n_q_heads=3, n_kv_heads=3, head_dim=128, ffn=528,
+                    vocab=600, n_lanes=3, max_ctx=200, windows=(0, 45))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _cache_np(seq, n):
+    """The device caches as [layer, pos, kv_head, hd] float64 for positions [0, n)."""
+    c = seq.dec.c
+    L, hkv, hd = c.n_layers, c.n_kv_heads, c.head_dim
+    out = []
+    for t in (seq.K, seq.V):
+        out.append(t[:, :, :n].permute(0, 2, 1, 3, 4).reshape(L, n, hkv, hd).float().cpu().numpy().astype(np.float64))
+    return out
+
+
+def _check_caches(seq, cache, n, what):
+    K, V = _cache_np(seq, n)
+    worst = 0.0
+    for l in range(K.shape[0]):
+        for name, got, want in (("K", K[l], cache["K"][l, :n]), ("V", V[l], cache["V"][l, :n])):
+            a, r = vec_err(got.ravel(), want.ravel())
+            assert a <= MAX_ABS and r <= MAX_REL, f"{what}: layer {l} {name} cache max|d|={a:.3e} rel={r:.3e}"
+            worst = max(worst, r)
+    return worst
+
+
+@pytest.mark.parametrize("cfg,plen,chunk,steps", [
+    (TINY, 128, 128, 8),
+    (TINY, 128, 48, 8),
+    (RAGGED, 40, 17, 6),
+    (WIDE_GROUP, 150, 64, 6),
+    (MHA, 130, 100, 6),
+])
+def test_prefill_batched_matches_oracle(cfg, plen, chunk, steps):
+    import torch
+    from decode_step_05_amd import Decoder
+
+    say(f"[prefill] cfg={cfg.name} prompt={plen} chunk={chunk} steps={steps} seeds=(0,1)")
+    w = make_weights(cfg, seed=0)
+    prompt = make_prompt(cfg, plen, seed=1)
+    o = OracleDecoder(cfg, w)
+    cache = o.new_cache()
+    o.forward_sequence(tokens=prompt, cache=cache)
+    ref_z, ref_t = o.generate(prompt, steps)
+
+    dec = Decoder(cfg, w)
+    seq = dec.sequence()
+    seq.prefill_batched(prompt, chunk=chunk)
+    z, a = seq.logits()
+    z = z.cpu().numpy()
+    amax, rel = assert_close(z, ref_z[0], f"{cfg.name} last prompt position")
+    assert check_token(int(a.item()), ref_z[0], amax), f"{cfg.name}: token {int(a.item())} != oracle {ref_t[0]}"
+    assert int(a.item()) == greedy_fp32(z)
+    assert seq.status()[0] == plen
+    hist = seq.tokens(0, plen + 1).cpu().numpy()
+    assert np.array_equal(hist[:plen], prompt) and hist[plen] == int(a.item())
+    crel = _check_caches(seq, cache, plen, cfg.name)
+
+    # decoding continues from the cache the batched pass wrote
+    for s in range(steps):
+        seq.step(int(ref_t[s]))
+        zs, _ = seq.logits()
+        assert_close(zs.cpu().numpy(), ref_z[s + 1], f"{cfg.name} decode step {s} after the batched pass")
+    torch.cuda.synchronize()
+    say(f"[prefill] {cfg.name}: logits max|d|={amax:.2e} rel={rel:.2e}, worst cache rel={crel:.2e}, "
+        f"{steps} decode steps close")
+
+
+def test_prefill_batched_after_a_prefix_and_bad_token():
+    """Positions already in the cache (written by token-by-token steps) are
+    attended to by the batched pass, which starts at len > 0; a token id out
+    of range is clamped and flagged as in the decode path."""
+    import torch
+    from decode_step_05_amd import Decoder
+
+    cfg = TINY
+    say(f"[prefill] prefix cfg={cfg.name} prompt=50+78 chunk=32")
+    w = make_weights(cfg, seed=0)
+    prompt = make_prompt(cfg, 128, seed=1)
+    o = OracleDecoder(cfg, w)
+    cache = o.new_cache()
+    ref = o.forward_sequence(tokens=prompt, cache=cache)
+    dec = Decoder(cfg, w)
+    seq = dec.sequence()
+    seq.prefill(prompt[:50])
+    seq.prefill_batched(prompt[50:], chunk=32)
+    z, _ = seq.logits()
+    assert_close(z.cpu().numpy(), ref[-1], "prefix + batched")
+    _check_caches(seq, cache, 128, "prefix + batched")
+    assert seq.status()[2] == 0
+
+    bad = np.array(prompt[:20], np.int32)
+    bad[7] = cfg.vocab + 5
+    seq2 = dec.sequence()
+    seq2.prefill_batched(bad, chunk=16)
+    assert seq2.status()[2] & 1, "out-of-range token not flagged"
+    fixed = bad.copy()
+    fixed[7] = cfg.vocab - 1
+    ref2 = o.forward_sequence(tokens=fixed)
+    assert_close(seq2.logits()[0].cpu().numpy(), ref2[-1], "clamped token")
+    torch.cuda.synchronize()
+
+
+def test_prefill_batched_argument_errors():
+    from decode_step_05_amd import Decoder
+    from decode_step_05_amd import lfdecode as C
+
+    cfg = TINY
+    say(f"[prefill] argument errors cfg={cfg.name}")
+    dec = Decoder(cfg, make_weights(cfg, seed=0))
+    seq = dec.sequence()
+    import torch
+    toks = torch.zeros(8, dtype=torch.int32, device="cuda")
+    need = C.lf_prefill_workspace_bytes(dec.c, 8)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(C.LfError, match="workspace"):
+        C.lf_prefill_batched(dec.handle, seq.handle, toks, 8, ws[: need - 256])
+    with pytest.raises(C.LfError, match="aligned"):
+        C.lf_prefill_batched(dec.handle, seq.handle, toks, 8, ws[16:])
+    with pytest.raises(C.LfError, match="chunk"):
+        C.lf_prefill_batched(dec.handle, seq.handle, toks, 0, ws)
+    seq.set_len(cfg.max_ctx - 4)
+    with pytest.raises(C.LfError) as e:
+        C.lf_prefill_batched(dec.handle, seq.handle, toks, 8, ws)
+    assert e.value.code == C.LF_ERANGE
+    assert seq.len == cfg.max_ctx - 4
+
+
+@pytest.mark.timeout(600)
+def test_prefill_batched_full_size_matches_stored_oracle():
+    """The 15-layer decoder's 3584-token prompt in chunks of 1024 (the last one
+    512), then 32 teacher-forced decode steps over the cache it wrote, against
+    the stored oracle results of the 3584 + 512 generation workload."""
+    import torch
+    from decode_step_05_amd import Decoder
+
+    name = "ctx4096"
+    g = np.load(os.path.join(GOLDEN, f"oracle_{name}.npz"))
+    wl = WORKLOADS[name]
+    cfg = wl.cfg
+    say(f"[prefill] {name}: batched prompt {wl.prompt_len} chunk 1024, seeds ({wl.weight_seed},{wl.prompt_seed})")
+    w = make_weights(cfg, seed=wl.weight_seed, threads=16)
+    prompt = make_prompt(cfg, wl.prompt_len, seed=wl.prompt_seed)
+    dec = Decoder(cfg, w)
+    del w
+    seq = dec.sequence()
+    seq.prefill_batched(prompt, chunk=1024)
+    z, a = seq.logits()
+    a0, r0 = vec_err(z.cpu().numpy(), g["full"][0])
+    assert a0 <= MAX_ABS and r0 <= MAX_REL, f"last prompt position: max|d|={a0:.3e} rel={r0:.3e}"
+    toks = g["tokens"]
+    assert int(a.item()) == toks[0] or g["gaps"][0] <= 2 * a0
+    idx = torch.from_numpy(g["sample_idx"].astype(np.int64)).cuda()
+    top_i = torch.from_numpy(g["top_i"].astype(np.int64)).cuda()
+    worst = (a0, r0)
+    for s in range(1, 33):
+        seq.step(int(toks[s - 1]))
+        zs, _ = seq.logits()
+        a1, r1 = vec_err(zs[idx].cpu().numpy(), g["sample_v"][s])
+        a2, _ = vec_err(zs[top_i[s]].cpu().numpy(), g["top_v"][s])
+        assert max(a1, a2) <= MAX_ABS and r1 <= MAX_REL, f"decode step {s}: max|d|={max(a1, a2):.3e} rel={r1:.3e}"
+        worst = (max(worst[0], a1, a2), max(worst[1], r1))
+    torch.cuda.synchronize()
+    say(f"[prefill] {name}: last prompt position and 32 decode steps, worst max|d|={worst[0]:.2e} rel={worst[1]:.2e}")

@@ -133,3 +133,20 @@ def test_read_bandwidth_argument_errors_before_any_device_call():
     assert rc == C.LF_EINVAL and "aligned" in C.lf_last_error()
     assert lib.lf_read_bandwidth(0x1000, 8, 1, 0x1000, ctypes.byref(g), None) == C.LF_EINVAL
     assert lib.lf_read_bandwidth(0x1000, 1 << 20, 0, 0x1000, ctypes.byref(g), None) == C.LF_EINVAL
+
+
+def test_prefill_workspace_sizes_and_null_checks():
+    # chunk rows of fp32: the residual, the widest projection output (gate/up,
+    # 2 x 7168), the widest GEMM input (the SwiGLU output, 7168) and the
+    # queries (4096); each region 256-byte aligned
+    lib = C.load()
+    c = C.make_config(FULL)
+    for mc in (1, 100, 1024, 4096):
+        exact = mc * (4096 * 4 + 14336 * 4 + 7168 * 4 + 4096 * 4)
+        assert exact <= C.lf_prefill_workspace_bytes(c, mc) < exact + 4 * 256
+    assert C.lf_prefill_workspace_bytes(c, 0) == 0
+    assert C.lf_prefill_workspace_bytes(c, 4097) == 0
+    assert lib.lf_prefill_workspace_bytes(None, 16) == 0
+    assert C.lf_prefill_workspace_bytes(C.make_config(TINY), 64) > 0
+    assert lib.lf_prefill_batched(None, None, None, 1, 16, None, 0, None) == C.LF_EINVAL
+    assert lib.lf_prefill_batched(None, None, 0x1000, 1, 16, 0x1000, 1 << 20, None) == C.LF_EINVAL
