@@ -5,7 +5,8 @@ context 4096 on one MI355X.
 Workload: seeded random fp16 weights (N(0, 0.02)), a 3584-token random
 prompt, then greedy decode steps toward 4096 positions (each step reads every
 weight once plus the visible KV cache: 5 full-attention layers see all
-positions, 10 sliding-window layers at most 1024). Prefill is not timed.
+positions, 10 sliding-window layers at most 1024). The prompt is filled by
+the batched prompt pass on the matrix cores, timed on its own (`prefill`).
 W warm-up steps run first; the sequence is then rewound to the prompt so the
 K timed steps replay the same positions 3584 .. 3584+K-1, device-fed (the
 greedy token never leaves the GPU), as hipGraph replays.
@@ -24,6 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak, vendor figure
+PREFILL_CHUNK = 2048
 
 # HBM bytes per gate/up GEMV launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (a 512 MiB device copy reads as 0.5x FETCH_SIZE, writes as 1.0x
@@ -92,6 +95,20 @@ def lane_share(torch, Decoder):
                         "down 4096x896, hidden in/out, positions 4031..4094",
             "us_per_token": round(us, 2), "bytes_per_token": int(moved),
             "hbm_gbs": round(moved / (us * 1e-6) / 1e9, 1), "roofline_us": round(moved / (PEAK_HBM_GBS * 1e3), 2)}
+
+
+def prefill_flops(cfg, n):
+    """Algorithmic flops of the prompt pass over positions 0..n-1: every
+    projection as a GEMM of n rows (2 flops per weight per row), attention
+    over exactly the visible keys of each query (q.k and the weighted sum of
+    v: 4 * head_dim flops per (query head, key)), and the LM head for the last
+    position."""
+    d, q, f = cfg.d_model, cfg.n_q_heads * cfg.head_dim, cfg.ffn
+    per_row = cfg.n_layers * (cfg.qkv_rows * d + d * q + 2 * f * d + d * f)
+    pairs = 0
+    for w in cfg.windows:
+        pairs += sum(p + 1 if w == 0 else min(p + 1, w) for p in range(n))
+    return 2 * n * per_row + 4 * cfg.head_dim * cfg.n_q_heads * pairs + 2 * cfg.vocab * d
 
 
 def gate_up_bytes(cfg):
@@ -203,8 +220,30 @@ def main():
     dec = Decoder(cfg, weights, mode=None if args.mode == "default" else modes[args.mode])
     mode_name = {v: k for k, v in modes.items()}[dec.mode]
     log(f"[bench] step launch mode: {mode_name}")
-    seq = dec.sequence()
     prompt = make_prompt(cfg, P, seed=wl.prompt_seed)
+    prompt_dev = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+
+    # the batched prompt pass on the matrix cores: 3 timed runs from an empty cache
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    pseq = dec.sequence()
+    pseq.prefill_batched(prompt_dev, chunk=PREFILL_CHUNK)
+    pf_ms = []
+    for _ in range(3):
+        pseq.set_len(0)
+        torch.cuda.synchronize()
+        e0.record()
+        pseq.prefill_batched(prompt_dev, chunk=PREFILL_CHUNK)
+        e1.record()
+        torch.cuda.synchronize()
+        pf_ms.append(e0.elapsed_time(e1))
+    del pseq
+    pf_med = float(np.median(pf_ms))
+    pf_tflops = prefill_flops(cfg, P) / (pf_med / 1e3) / 1e12
+    log(f"[bench] batched prompt pass of {P} positions: {', '.join(f'{x:.2f}' for x in pf_ms)} ms "
+        f"-> {pf_tflops:.0f} TFLOP/s")
+
+    seq = dec.sequence()
     torch.cuda.synchronize()
     t = time.perf_counter()
     if args.synthetic_cache:
@@ -213,7 +252,7 @@ def main():
         seq.set_len(P)
         del K_, V_
     else:
-        seq.prefill(prompt)
+        seq.prefill_batched(prompt_dev, chunk=PREFILL_CHUNK)
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t
     log(f"[bench] {'synthetic cache' if args.synthetic_cache else 'prefill'} {P} positions in {prefill_s:.2f}s")
@@ -223,8 +262,6 @@ def main():
         seq.steps(args.warmup)
     torch.cuda.synchronize()
     seq.set_len(P)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
@@ -351,7 +388,15 @@ def main():
         "qkv_attention_fused": bool(fused),
         "stream_read_ceiling_gbs": round(ceiling, 1),
         "lane_share": lane,
-        "prefill_s": round(prefill_s, 2),
+        "prefill_s": round(prefill_s, 3),
+        "prefill": {"positions": P, "chunk": PREFILL_CHUNK, "runs_ms": [round(x, 3) for x in pf_ms],
+                    "ms": round(pf_med, 3), "tok_s": round(P / (pf_med / 1e3), 1),
+                    "roofline": {"bound": "mfma", "kernel": "whole batched prompt pass (lf_prefill_batched)",
+                                 "achieved": round(pf_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(pf_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                                 "flops": prefill_flops(cfg, P),
+                                 "note": "algorithmic flops; the fp32 activations enter the fp16 matrix "
+                                         "instructions as hi + lo parts, so the GEMMs issue twice these flops"}},
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "roofline": {"bound": "hbm", "kernel": "gate_up GEMV (RMSNorm + SwiGLU fused), 14336x4096 fp16",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

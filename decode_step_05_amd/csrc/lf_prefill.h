@@ -12,6 +12,7 @@
 // each multiplied with the fp16 weights or values, fp32 accumulation.
 #pragma once
 #include "lf_device.h"
+#include "lf_kernels.h"  // lds_barrier
 
 namespace lf {
 
@@ -164,9 +165,13 @@ struct PfAttnArgs {
 };
 
 template <int HD, int G>
-__global__ __launch_bounds__(G * kWave) void k_pf_attn(PfAttnArgs a) {
-  constexpr int VLD = 32 + 4;  // V^T row stride in halves
+__global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_attn(PfAttnArgs a) {
+  constexpr int VLD = 32 + 4;   // V^T row stride in halves
+  constexpr int QLD = HD + 8;   // query row stride in halves
+  constexpr int NC = 32 * HD / 8;  // 16-byte pieces of V per key tile
+  constexpr int NV = (NC + G * kWave - 1) / (G * kWave);
   __shared__ __attribute__((aligned(16))) half_t Vt[HD * VLD];
+  __shared__ __attribute__((aligned(16))) half_t Qs[G][2][32 * QLD];  // per wave: hi, lo parts of its queries
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int qb = blockIdx.x, kvh = blockIdx.y;
   const int head = kvh * G + w;
@@ -177,19 +182,25 @@ __global__ __launch_bounds__(G * kWave) void k_pf_attn(PfAttnArgs a) {
   const int qpos = a.pos0 + qrow;
   const int grp = lane >> 5;
 
-  h8 qf[HD / 16], ql[HD / 16];
+  // This lane's query fragments (B operand of S^T: query l % 32, head
+  // dimensions 16 kk + 8 grp ..), split into hi and lo parts and parked in LDS
+  // to leave registers for the next tile's loads; a lane reads back only what
+  // it wrote.
   {
     const float* qp = a.q + (static_cast<size_t>(min(qrow, a.M - 1)) * a.n_q + head) * HD + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) {
       const f32x4 u0 = *reinterpret_cast<const f32x4*>(qp + kk * 16);
       const f32x4 u1 = *reinterpret_cast<const f32x4*>(qp + kk * 16 + 4);
+      h8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = e < 4 ? u0[e] : u1[e - 4];
-        qf[kk][e] = static_cast<half_t>(v);
-        ql[kk][e] = static_cast<half_t>(v - static_cast<float>(qf[kk][e]));
+        hi[e] = static_cast<half_t>(v);
+        lo[e] = static_cast<half_t>(v - static_cast<float>(hi[e]));
       }
+      *reinterpret_cast<h8*>(&Qs[w][0][(lane & 31) * QLD + kk * 16 + grp * 8]) = hi;
+      *reinterpret_cast<h8*>(&Qs[w][1][(lane & 31) * QLD + kk * 16 + grp * 8]) = lo;
     }
   }
   const size_t kstride = static_cast<size_t>(a.kpl) * HD;  // between consecutive positions
@@ -199,6 +210,21 @@ __global__ __launch_bounds__(G * kWave) void k_pf_attn(PfAttnArgs a) {
   const int k_lo = (a.window ? max(0, q_first - a.window + 1) : 0) & ~31;
   const int k_hi = q_last;
 
+  // one key tile's loads: the keys as the A operand of S^T (key l % 32, head
+  // dimensions 16 kk + 8 grp ..) and this thread's pieces of V; keys past k_hi
+  // are clamped to it (masked below), so every address is a written position
+  auto load_tile = [&](int k0, h8 (&kf)[HD / 16], h8 (&vr)[NV]) {
+    const half_t* kp = kbase + static_cast<size_t>(min(k0 + (lane & 31), k_hi)) * kstride + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = *reinterpret_cast<const h8*>(kp + kk * 16);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = min(tid + i * G * kWave, NC - 1);
+      const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
+      vr[i] = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(k0 + key, k_hi)) * kstride + d8);
+    }
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 ot[HD / 32];
 #pragma unroll
@@ -206,36 +232,42 @@ __global__ __launch_bounds__(G * kWave) void k_pf_attn(PfAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) ot[th][r] = 0.f;
 
+  h8 kf[HD / 16], vr[NV];
+  load_tile(k_lo, kf, vr);
   for (int k0 = k_lo; k0 <= k_hi; k0 += 32) {
-    // keys of this tile (A operand of S^T): row l % 32, hd group l / 32
-    h8 kf[HD / 16];
-    {
-      const half_t* kp = kbase + static_cast<size_t>(min(k0 + (lane & 31), k_hi)) * kstride + grp * 8;
+    lds_barrier();  // every wave is done reading the previous tile's V^T
 #pragma unroll
-      for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = *reinterpret_cast<const h8*>(kp + kk * 16);
+    for (int i = 0; i < NV; ++i) {
+      const int c = tid + i * G * kWave;
+      if (NC % (G * kWave) == 0 || c < NC) {
+        const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Vt[(d8 + e) * VLD + key] = vr[i][e];
+      }
     }
-    __syncthreads();  // every wave is done reading the previous tile's V^T
-    for (int c = tid; c < 32 * HD / 8; c += G * kWave) {
-      const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-      const h8 v = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(k0 + key, k_hi)) * kstride + d8);
+    // the next tile's loads fly while this one is computed (issued every
+    // iteration: a conditional load would make the compiler wait at the join)
+    h8 kn[HD / 16], vn[NV];
+    load_tile(k0 + 32, kn, vn);
+
+    f32x16 sa, sb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(d8 + e) * VLD + key] = v[e];
-    }
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int r = 0; r < 16; ++r) sa[r] = sb[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qf[kk], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], ql[kk], s, 0, 0, 0);
+      const h8 qh = *reinterpret_cast<const h8*>(&Qs[w][0][(lane & 31) * QLD + kk * 16 + grp * 8]);
+      const h8 ql = *reinterpret_cast<const h8*>(&Qs[w][1][(lane & 31) * QLD + kk * 16 + grp * 8]);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qh, sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], ql, sb, 0, 0, 0);
     }
 
+    float s[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
       const bool vis = key <= qpos && (a.window == 0 || key > qpos - a.window);
-      s[r] = vis ? s[r] * a.scale_log2 : -INFINITY;
+      s[r] = vis ? (sa[r] + sb[r]) * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -257,20 +289,24 @@ __global__ __launch_bounds__(G * kWave) void k_pf_attn(PfAttnArgs a) {
     for (int th = 0; th < HD / 32; ++th)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ot[th][r] *= alpha;
-    __syncthreads();  // V^T of this tile staged
+    lds_barrier();  // V^T of this tile staged by every wave
     // P^T in B-operand order: register r = 8 mm + s holds key 16 mm + 8 (s / 4) + 4 grp + s % 4,
     // which is where the A operand (V^T) takes its k slot s from
 #pragma unroll
     for (int th = 0; th < HD / 32; ++th)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const half_t* vr = &Vt[(th * 32 + (lane & 31)) * VLD + 16 * mm + 4 * grp];
-        const h4 v0 = *reinterpret_cast<const h4*>(vr);
-        const h4 v1 = *reinterpret_cast<const h4*>(vr + 8);
+        const half_t* vp = &Vt[(th * 32 + (lane & 31)) * VLD + 16 * mm + 4 * grp];
+        const h4 v0 = *reinterpret_cast<const h4*>(vp);
+        const h4 v1 = *reinterpret_cast<const h4*>(vp + 8);
         const h8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         ot[th] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[mm], ot[th], 0, 0, 0);
         ot[th] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[mm], ot[th], 0, 0, 0);
       }
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = kn[kk];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vr[i] = vn[i];
   }
 
   if (qrow < a.M) {
