@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only copy a MB-MiB device buffer three times and exit (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the batched prompt pass (3 runs) and print its JSON object")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this decode path runs on one GPU; --gpus must be 1 "
@@ -242,6 +244,17 @@ def main():
     pf_tflops = prefill_flops(cfg, P) / (pf_med / 1e3) / 1e12
     log(f"[bench] batched prompt pass of {P} positions: {', '.join(f'{x:.2f}' for x in pf_ms)} ms "
         f"-> {pf_tflops:.0f} TFLOP/s")
+    prefill = {"positions": P, "chunk": PREFILL_CHUNK, "runs_ms": [round(x, 3) for x in pf_ms],
+               "ms": round(pf_med, 3), "tok_s": round(P / (pf_med / 1e3), 1),
+               "roofline": {"bound": "mfma", "kernel": "whole batched prompt pass (lf_prefill_batched)",
+                            "achieved": round(pf_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(pf_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                            "flops": prefill_flops(cfg, P),
+                            "note": "algorithmic flops; the fp32 activations enter the fp16 matrix "
+                                    "instructions as hi + lo parts, so the GEMMs issue twice these flops"}}
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill}), flush=True)
+        return
 
     seq = dec.sequence()
     torch.cuda.synchronize()
@@ -389,14 +402,7 @@ def main():
         "stream_read_ceiling_gbs": round(ceiling, 1),
         "lane_share": lane,
         "prefill_s": round(prefill_s, 3),
-        "prefill": {"positions": P, "chunk": PREFILL_CHUNK, "runs_ms": [round(x, 3) for x in pf_ms],
-                    "ms": round(pf_med, 3), "tok_s": round(P / (pf_med / 1e3), 1),
-                    "roofline": {"bound": "mfma", "kernel": "whole batched prompt pass (lf_prefill_batched)",
-                                 "achieved": round(pf_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(pf_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
-                                 "flops": prefill_flops(cfg, P),
-                                 "note": "algorithmic flops; the fp32 activations enter the fp16 matrix "
-                                         "instructions as hi + lo parts, so the GEMMs issue twice these flops"}},
+        "prefill": prefill,
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "roofline": {"bound": "hbm", "kernel": "gate_up GEMV (RMSNorm + SwiGLU fused), 14336x4096 fp16",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
