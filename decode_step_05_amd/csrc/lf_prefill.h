@@ -54,27 +54,29 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
   const int t = (T & 7) ? b : (b & 7) * (T >> 3) + (b >> 3);
   const int m0 = (t % a.tiles_m) * kPfBM, n0 = (t / a.tiles_m) * kPfBN;
 
-  // loader: weight chunk i of this thread is row (tid / 8) + 32 i, halves
-  // (tid % 8) * 8 of the K step; activation chunk i is row (tid / 16) + 16 i,
-  // floats (tid % 16) * 4
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-  const int arow = tid >> 4, acol = (tid & 15) * 4;
-  const float* ap[8];
-  const half_t* bp[4];
+  // loader: per K step a thread loads NA chunks of 4 activations (rows
+  // tid / ACR + ARS i, floats (tid % ACR) * 4) and NB chunks of 8 weights
+  // (rows tid / BCR + BRS i, halves (tid % BCR) * 8)
+  constexpr int ACR = kPfBK / 4, ARS = kPfThreads / ACR, NA = kPfBM / ARS;
+  constexpr int BCR = kPfBK / 8, BRS = kPfThreads / BCR, NB = kPfBN / BRS;
+  const int lrow = tid / BCR, lcol = (tid % BCR) * 8;
+  const int arow = tid / ACR, acol = (tid % ACR) * 4;
+  const float* ap[NA];
+  const half_t* bp[NB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ap[i] = a.A + static_cast<size_t>(min(m0 + arow + 16 * i, a.M - 1)) * a.K + acol;
+  for (int i = 0; i < NA; ++i) ap[i] = a.A + static_cast<size_t>(min(m0 + arow + ARS * i, a.M - 1)) * a.K + acol;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bp[i] = a.W + static_cast<size_t>(min(n0 + lrow + 32 * i, a.N - 1)) * a.K + lcol;
-  f32x4 ra[8];
-  u32x4 rb[4];
+  for (int i = 0; i < NB; ++i) bp[i] = a.W + static_cast<size_t>(min(n0 + lrow + BRS * i, a.N - 1)) * a.K + lcol;
+  f32x4 ra[NA];
+  u32x4 rb[NB];
   auto load = [&](int k0) {
     const bool ina = k0 + acol < a.K, inb = k0 + lcol < a.K;
     const u32x4 z = {0u, 0u, 0u, 0u};
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = ina ? *reinterpret_cast<const f32x4*>(ap[i] + k0) : zf;
+    for (int i = 0; i < NA; ++i) ra[i] = ina ? *reinterpret_cast<const f32x4*>(ap[i] + k0) : zf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rb[i] = inb ? ld16(bp[i] + k0) : z;
+    for (int i = 0; i < NB; ++i) rb[i] = inb ? ld16(bp[i] + k0) : z;
   };
 
   const int wm = wave & 1, wn = wave >> 1;
@@ -90,18 +92,18 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
   for (int k0 = 0; k0 < a.K; k0 += kPfBK) {
     __syncthreads();  // every wave is done reading the previous K step
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NA; ++i) {
       h4 hi, lo;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         hi[e] = static_cast<half_t>(ra[i][e]);
         lo[e] = static_cast<half_t>(ra[i][e] - static_cast<float>(hi[e]));
       }
-      *reinterpret_cast<h4*>(&As[(arow + 16 * i) * kPfLd + acol]) = hi;
-      *reinterpret_cast<h4*>(&Al[(arow + 16 * i) * kPfLd + acol]) = lo;
+      *reinterpret_cast<h4*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
+      *reinterpret_cast<h4*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&Bs[(lrow + 32 * i) * kPfLd + lcol]) = rb[i];
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4*>(&Bs[(lrow + BRS * i) * kPfLd + lcol]) = rb[i];
     __syncthreads();
     if (k0 + kPfBK < a.K) load(k0 + kPfBK);
 #pragma unroll

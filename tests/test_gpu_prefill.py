@@ -7,8 +7,8 @@ keys and values written to the cache (compared with the oracle's
 full-sequence pass, which fills its cache as decoding would), and decode
 steps that continue from the batched pass. The chunk sizes leave ragged
 chunks, and the sliding windows are narrower than a chunk. The 15-layer
-decoder's 3584-token prompt is compared with the stored oracle results of
-that workload. Acceptance: tests/parity.py.
+decoder's 512- and 3584-token prompts are compared with the stored oracle
+results of those workloads. Acceptance: tests/parity.py.
 """
 import os
 
@@ -56,6 +56,7 @@ def _check_caches(seq, cache, n, what):
 
 
 @pytest.mark.parametrize("cfg,plen,chunk,steps", [
+    (TINY, 1, 1, 4),
     (TINY, 128, 128, 8),
     (TINY, 128, 48, 8),
     (RAGGED, 40, 17, 6),
@@ -158,24 +159,25 @@ def test_prefill_batched_argument_errors():
 
 
 @pytest.mark.timeout(600)
-def test_prefill_batched_full_size_matches_stored_oracle():
-    """The 15-layer decoder's 3584-token prompt in chunks of 1024 (the last one
-    512), then 32 teacher-forced decode steps over the cache it wrote, against
-    the stored oracle results of the 3584 + 512 generation workload."""
+@pytest.mark.parametrize("name,chunk", [("ctx1024", 200), ("ctx4096", 1024)])
+def test_prefill_batched_full_size_matches_stored_oracle(name, chunk):
+    """The 15-layer decoder's prompt (512 positions in chunks of 200, 200, 112;
+    3584 in chunks of 1024, the last one 512), then 32 teacher-forced decode
+    steps over the cache it wrote, against the stored oracle results of the
+    generation workload."""
     import torch
     from decode_step_05_amd import Decoder
 
-    name = "ctx4096"
     g = np.load(os.path.join(GOLDEN, f"oracle_{name}.npz"))
     wl = WORKLOADS[name]
     cfg = wl.cfg
-    say(f"[prefill] {name}: batched prompt {wl.prompt_len} chunk 1024, seeds ({wl.weight_seed},{wl.prompt_seed})")
+    say(f"[prefill] {name}: batched prompt {wl.prompt_len} chunk {chunk}, seeds ({wl.weight_seed},{wl.prompt_seed})")
     w = make_weights(cfg, seed=wl.weight_seed, threads=16)
     prompt = make_prompt(cfg, wl.prompt_len, seed=wl.prompt_seed)
     dec = Decoder(cfg, w)
     del w
     seq = dec.sequence()
-    seq.prefill_batched(prompt, chunk=1024)
+    seq.prefill_batched(prompt, chunk=chunk)
     z, a = seq.logits()
     a0, r0 = vec_err(z.cpu().numpy(), g["full"][0])
     assert a0 <= MAX_ABS and r0 <= MAX_REL, f"last prompt position: max|d|={a0:.3e} rel={r0:.3e}"
