@@ -148,9 +148,11 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
 // ---------------------------------------------------------- attention
 // Causal attention of a chunk of query positions over the cache, with the
 // sliding window where the layer has one: keys j with p - W < j <= p for the
-// query at position p (all j <= p when W = 0). Workgroup: 32 consecutive query
-// positions and one kv head; wave w handles query head G·kvh + w (the G query
-// heads of a kv head share its keys and values). Per 32-key tile a wave forms
+// query at position p (all j <= p when W = 0). Workgroup: QB blocks of 32
+// consecutive query positions and one kv head; wave w handles block w / G and
+// query head G·kvh + w % G (the G query heads of a kv head and the QB blocks
+// share the workgroup's key and value tiles; a tile outside a wave's own
+// range is fully masked for it). Per 32-key tile a wave forms
 // S^T = K · Q^T (so lane l owns query l % 32 and 16 of the 32 keys; its
 // partner lane l ^ 32 holds the other 16), applies the mask, updates an online
 // softmax (running max and denominator per query), and adds V^T · P^T into
@@ -166,21 +168,22 @@ struct PfAttnArgs {
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
-template <int HD, int G>
-__global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_attn(PfAttnArgs a) {
+template <int HD, int G, int QB>
+__global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_attn(PfAttnArgs a) {
+  constexpr int NW = QB * G;    // waves
   constexpr int VLD = 32 + 4;   // V^T row stride in halves
   constexpr int QLD = HD + 8;   // query row stride in halves
   constexpr int NC = 32 * HD / 8;  // 16-byte pieces of V per key tile
-  constexpr int NV = (NC + G * kWave - 1) / (G * kWave);
+  constexpr int NV = (NC + NW * kWave - 1) / (NW * kWave);
   __shared__ __attribute__((aligned(16))) half_t Vt[HD * VLD];
-  __shared__ __attribute__((aligned(16))) half_t Qs[G][2][32 * QLD];  // per wave: hi, lo parts of its queries
+  __shared__ __attribute__((aligned(16))) half_t Qs[NW][2][32 * QLD];  // per wave: hi, lo parts of its queries
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int qb = blockIdx.x, kvh = blockIdx.y;
-  const int head = kvh * G + w;
+  const int kvh = blockIdx.y;
+  const int head = kvh * G + w % G;
   const int ln = kvh / a.kpl, hk = kvh % a.kpl;
-  const int q_first = a.pos0 + qb * 32;
-  const int q_last = min(q_first + 31, a.pos0 + a.M - 1);
-  const int qrow = qb * 32 + (lane & 31);  // chunk row of this lane's query (past M in the last block)
+  const int q_first = a.pos0 + blockIdx.x * QB * 32;  // the workgroup's query range
+  const int q_last = min(q_first + QB * 32 - 1, a.pos0 + a.M - 1);
+  const int qrow = (blockIdx.x * QB + w / G) * 32 + (lane & 31);  // chunk row of this lane's query (may pass M)
   const int qpos = a.pos0 + qrow;
   const int grp = lane >> 5;
 
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = *reinterpret_cast<const h8*>(kp + kk * 16);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c = min(tid + i * G * kWave, NC - 1);
+      const int c = min(tid + i * NW * kWave, NC - 1);
       const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
       vr[i] = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(k0 + key, k_hi)) * kstride + d8);
     }
@@ -240,8 +243,8 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2))) 
     lds_barrier();  // every wave is done reading the previous tile's V^T
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c = tid + i * G * kWave;
-      if (NC % (G * kWave) == 0 || c < NC) {
+      const int c = tid + i * NW * kWave;
+      if (NC % (NW * kWave) == 0 || c < NC) {
         const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) Vt[(d8 + e) * VLD + key] = vr[i][e];

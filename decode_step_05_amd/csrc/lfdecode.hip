@@ -715,12 +715,15 @@ void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int
   hipLaunchKernelGGL(lf::k_pf_gemm<EPI>, dim3(g.tiles_m * g.tiles_n), dim3(lf::kPfThreads), 0, st, g);
 }
 
+// Two blocks of 32 queries per workgroup share its key / value tiles where
+// the group has at most 2 query heads (4 waves), one block for 4 query heads.
 void launch_pf_attn(const lf::PfAttnArgs& a, int hd, int G, int n_kv, hipStream_t st) {
-  const dim3 grid((a.M + 31) / 32, n_kv);
-#define LF_PF_ATTN(HD, GG)                                                                   \
-  if (hd == HD && G == GG) {                                                                 \
-    hipLaunchKernelGGL((lf::k_pf_attn<HD, GG>), grid, dim3(GG * lf::kWave), 0, st, a);      \
-    return;                                                                                  \
+#define LF_PF_ATTN(HD, GG)                                                                          \
+  if (hd == HD && G == GG) {                                                                        \
+    constexpr int QB = GG <= 2 ? 2 : 1;                                                             \
+    hipLaunchKernelGGL((lf::k_pf_attn<HD, GG, QB>), dim3((a.M + 32 * QB - 1) / (32 * QB), n_kv),    \
+                       dim3(QB * GG * lf::kWave), 0, st, a);                                        \
+    return;                                                                                         \
   }
   LF_PF_ATTN(128, 1) LF_PF_ATTN(128, 2) LF_PF_ATTN(128, 4)
   LF_PF_ATTN(64, 1) LF_PF_ATTN(64, 2) LF_PF_ATTN(64, 4)
