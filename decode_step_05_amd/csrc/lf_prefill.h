@@ -18,6 +18,7 @@ namespace lf {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- GEMM
 // C[M][N] (=, +=) A[M][K] · W[N][K]^T. A: activations, fp32 row-major, split
@@ -173,8 +174,12 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   constexpr int NW = QB * G;    // waves
   constexpr int VLD = 32 + 4;   // V^T row stride in halves
   constexpr int QLD = HD + 8;   // query row stride in halves
-  constexpr int NC = 32 * HD / 8;  // 16-byte pieces of V per key tile
-  constexpr int NV = (NC + NW * kWave - 1) / (NW * kWave);
+  // V staging unit: 8 head dimensions of two adjacent keys, written to V^T as
+  // 8 32-bit key pairs; unit c is key pair c % 16, dimensions 8 (c / 16) ..,
+  // so 16 lanes fill 16 consecutive words of a V^T row and the 4 rows a wave
+  // writes at once start 16 banks apart
+  constexpr int NU = 2 * HD;
+  constexpr int NV = (NU + NW * kWave - 1) / (NW * kWave);
   __shared__ __attribute__((aligned(16))) half_t Vt[HD * VLD];
   __shared__ __attribute__((aligned(16))) half_t Qs[NW][2][32 * QLD];  // per wave: hi, lo parts of its queries
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -218,15 +223,16 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   // one key tile's loads: the keys as the A operand of S^T (key l % 32, head
   // dimensions 16 kk + 8 grp ..) and this thread's pieces of V; keys past k_hi
   // are clamped to it (masked below), so every address is a written position
-  auto load_tile = [&](int k0, h8 (&kf)[HD / 16], h8 (&vr)[NV]) {
+  auto load_tile = [&](int k0, h8 (&kf)[HD / 16], h8 (&vr)[NV][2]) {
     const half_t* kp = kbase + static_cast<size_t>(min(k0 + (lane & 31), k_hi)) * kstride + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = *reinterpret_cast<const h8*>(kp + kk * 16);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c = min(tid + i * NW * kWave, NC - 1);
-      const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-      vr[i] = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(k0 + key, k_hi)) * kstride + d8);
+      const int c = min(tid + i * NW * kWave, NU - 1);
+      const int key = k0 + 2 * (c % 16), d8 = (c / 16) * 8;
+      vr[i][0] = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(key, k_hi)) * kstride + d8);
+      vr[i][1] = *reinterpret_cast<const h8*>(vbase + static_cast<size_t>(min(key + 1, k_hi)) * kstride + d8);
     }
   };
 
@@ -237,22 +243,25 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int r = 0; r < 16; ++r) ot[th][r] = 0.f;
 
-  h8 kf[HD / 16], vr[NV];
+  h8 kf[HD / 16], vr[NV][2];
   load_tile(k_lo, kf, vr);
   for (int k0 = k_lo; k0 <= k_hi; k0 += 32) {
     lds_barrier();  // every wave is done reading the previous tile's V^T
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = tid + i * NW * kWave;
-      if (NC % (NW * kWave) == 0 || c < NC) {
-        const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
+      if (NU % (NW * kWave) == 0 || c < NU) {
+        const int key = 2 * (c % 16), d8 = (c / 16) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(d8 + e) * VLD + key] = vr[i][e];
+        for (int e = 0; e < 8; ++e) {
+          const h2 pr = {vr[i][0][e], vr[i][1][e]};
+          *reinterpret_cast<h2*>(&Vt[(d8 + e) * VLD + key]) = pr;
+        }
       }
     }
     // the next tile's loads fly while this one is computed (issued every
     // iteration: a conditional load would make the compiler wait at the join)
-    h8 kn[HD / 16], vn[NV];
+    h8 kn[HD / 16], vn[NV][2];
     load_tile(k0 + 32, kn, vn);
 
     f32x16 sa, sb;
@@ -311,7 +320,10 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = kn[kk];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vr[i] = vn[i];
+    for (int i = 0; i < NV; ++i) {
+      vr[i][0] = vn[i][0];
+      vr[i][1] = vn[i][1];
+    }
   }
 
   if (qrow < a.M) {
