@@ -173,7 +173,10 @@ template <int HD, int G, int QB>
 __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_attn(PfAttnArgs a) {
   constexpr int NW = QB * G;    // waves
   constexpr int VLD = 32 + 4;   // V^T row stride in halves
-  constexpr int QLD = HD + 8;   // query row stride in halves
+  constexpr int KLD = HD + 8;   // key row stride in halves (rows 4 banks apart)
+  // K staging unit: 8 head dimensions of one key (unit c: key c / (HD / 8))
+  constexpr int NKU = 32 * HD / 8;
+  constexpr int NK = (NKU + NW * kWave - 1) / (NW * kWave);
   // V staging unit: 8 head dimensions of two adjacent keys, written to V^T as
   // 8 32-bit key pairs; unit c is key pair c % 16, dimensions 8 (c / 16) ..,
   // so 16 lanes fill 16 consecutive words of a V^T row and the 4 rows a wave
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   constexpr int NU = 2 * HD;
   constexpr int NV = (NU + NW * kWave - 1) / (NW * kWave);
   __shared__ __attribute__((aligned(16))) half_t Vt[HD * VLD];
-  __shared__ __attribute__((aligned(16))) half_t Qs[NW][2][32 * QLD];  // per wave: hi, lo parts of its queries
+  __shared__ __attribute__((aligned(16))) half_t Ks[32 * KLD];  // the tile's keys, staged once for all waves
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int kvh = blockIdx.y;
   const int head = kvh * G + w % G;
@@ -193,24 +196,20 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   const int grp = lane >> 5;
 
   // This lane's query fragments (B operand of S^T: query l % 32, head
-  // dimensions 16 kk + 8 grp ..), split into hi and lo parts and parked in LDS
-  // to leave registers for the next tile's loads; a lane reads back only what
-  // it wrote.
+  // dimensions 16 kk + 8 grp ..), split into hi and lo parts.
+  h8 qf[HD / 16], ql[HD / 16];
   {
     const float* qp = a.q + (static_cast<size_t>(min(qrow, a.M - 1)) * a.n_q + head) * HD + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) {
       const f32x4 u0 = *reinterpret_cast<const f32x4*>(qp + kk * 16);
       const f32x4 u1 = *reinterpret_cast<const f32x4*>(qp + kk * 16 + 4);
-      h8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = e < 4 ? u0[e] : u1[e - 4];
-        hi[e] = static_cast<half_t>(v);
-        lo[e] = static_cast<half_t>(v - static_cast<float>(hi[e]));
+        qf[kk][e] = static_cast<half_t>(v);
+        ql[kk][e] = static_cast<half_t>(v - static_cast<float>(qf[kk][e]));
       }
-      *reinterpret_cast<h8*>(&Qs[w][0][(lane & 31) * QLD + kk * 16 + grp * 8]) = hi;
-      *reinterpret_cast<h8*>(&Qs[w][1][(lane & 31) * QLD + kk * 16 + grp * 8]) = lo;
     }
   }
   const size_t kstride = static_cast<size_t>(a.kpl) * HD;  // between consecutive positions
@@ -220,13 +219,15 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   const int k_lo = (a.window ? max(0, q_first - a.window + 1) : 0) & ~31;
   const int k_hi = q_last;
 
-  // one key tile's loads: the keys as the A operand of S^T (key l % 32, head
-  // dimensions 16 kk + 8 grp ..) and this thread's pieces of V; keys past k_hi
+  // one key tile's loads: this thread's pieces of K and of V; keys past k_hi
   // are clamped to it (masked below), so every address is a written position
-  auto load_tile = [&](int k0, h8 (&kf)[HD / 16], h8 (&vr)[NV][2]) {
-    const half_t* kp = kbase + static_cast<size_t>(min(k0 + (lane & 31), k_hi)) * kstride + grp * 8;
+  auto load_tile = [&](int k0, h8 (&kr)[NK], h8 (&vr)[NV][2]) {
 #pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = *reinterpret_cast<const h8*>(kp + kk * 16);
+    for (int i = 0; i < NK; ++i) {
+      const int c = min(tid + i * NW * kWave, NKU - 1);
+      kr[i] = *reinterpret_cast<const h8*>(kbase + static_cast<size_t>(min(k0 + c / (HD / 8), k_hi)) * kstride +
+                                           (c % (HD / 8)) * 8);
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = min(tid + i * NW * kWave, NU - 1);
@@ -243,10 +244,10 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int r = 0; r < 16; ++r) ot[th][r] = 0.f;
 
-  h8 kf[HD / 16], vr[NV][2];
-  load_tile(k_lo, kf, vr);
+  h8 kr[NK], vr[NV][2];
+  load_tile(k_lo, kr, vr);
   for (int k0 = k_lo; k0 <= k_hi; k0 += 32) {
-    lds_barrier();  // every wave is done reading the previous tile's V^T
+    lds_barrier();  // every wave is done reading the previous tile's K and V^T
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = tid + i * NW * kWave;
@@ -259,20 +260,27 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int c = tid + i * NW * kWave;
+      if (NKU % (NW * kWave) == 0 || c < NKU)
+        *reinterpret_cast<h8*>(&Ks[(c / (HD / 8)) * KLD + (c % (HD / 8)) * 8]) = kr[i];
+    }
     // the next tile's loads fly while this one is computed (issued every
     // iteration: a conditional load would make the compiler wait at the join)
-    h8 kn[HD / 16], vn[NV][2];
+    h8 kn[NK], vn[NV][2];
     load_tile(k0 + 32, kn, vn);
+    lds_barrier();  // K and V^T of this tile staged by every wave
 
+    // S^T = K Q^T: keys (A operand: key l % 32, head dimensions 16 kk + 8 grp ..) from LDS
     f32x16 sa, sb;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[r] = sb[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) {
-      const h8 qh = *reinterpret_cast<const h8*>(&Qs[w][0][(lane & 31) * QLD + kk * 16 + grp * 8]);
-      const h8 ql = *reinterpret_cast<const h8*>(&Qs[w][1][(lane & 31) * QLD + kk * 16 + grp * 8]);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qh, sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], ql, sb, 0, 0, 0);
+      const h8 kf = *reinterpret_cast<const h8*>(&Ks[(lane & 31) * KLD + kk * 16 + grp * 8]);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[kk], sb, 0, 0, 0);
     }
 
     float s[16];
@@ -303,7 +311,6 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
     for (int th = 0; th < HD / 32; ++th)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ot[th][r] *= alpha;
-    lds_barrier();  // V^T of this tile staged by every wave
     // P^T in B-operand order: register r = 8 mm + s holds key 16 mm + 8 (s / 4) + 4 grp + s % 4,
     // which is where the A operand (V^T) takes its k slot s from
 #pragma unroll
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
         ot[th] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[mm], ot[th], 0, 0, 0);
       }
 #pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk) kf[kk] = kn[kk];
+    for (int i = 0; i < NK; ++i) kr[i] = kn[i];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       vr[i][0] = vn[i][0];
