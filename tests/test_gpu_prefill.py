@@ -195,3 +195,39 @@ def test_prefill_batched_full_size_matches_stored_oracle(name, chunk):
         worst = (max(worst[0], a1, a2), max(worst[1], r1))
     torch.cuda.synchronize()
     say(f"[prefill] {name}: last prompt position and 32 decode steps, worst max|d|={worst[0]:.2e} rel={worst[1]:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_prefill_batched_whole_context_in_one_chunk():
+    """Maximum sizes: the 3584-token prompt followed by the oracle's 512 greedy
+    tokens, 4096 positions (the whole context) as one chunk of 4096, must give
+    the stored oracle logits of position 4095 (computed there by 512
+    teacher-forced decode steps) and leave the sequence full."""
+    import torch
+    from decode_step_05_amd import Decoder
+    from decode_step_05_amd import lfdecode as C
+
+    name = "ctx4096"
+    g = np.load(os.path.join(GOLDEN, f"oracle_{name}.npz"))
+    wl = WORKLOADS[name]
+    cfg = wl.cfg
+    say(f"[prefill] {name}: whole context 4096 in one chunk, seeds ({wl.weight_seed},{wl.prompt_seed})")
+    w = make_weights(cfg, seed=wl.weight_seed, threads=16)
+    prompt = make_prompt(cfg, wl.prompt_len, seed=wl.prompt_seed)
+    toks = np.concatenate([prompt, g["tokens"][:wl.steps]]).astype(np.int32)
+    assert toks.size == cfg.max_ctx
+    dec = Decoder(cfg, w)
+    del w
+    seq = dec.sequence()
+    seq.prefill_batched(toks, chunk=cfg.max_ctx)
+    z, a = seq.logits()
+    k = list(g["full_at"]).index(wl.steps)
+    a0, r0 = vec_err(z.cpu().numpy(), g["full"][k])
+    assert a0 <= MAX_ABS and r0 <= MAX_REL, f"position 4095: max|d|={a0:.3e} rel={r0:.3e}"
+    assert int(a.item()) == g["tokens"][wl.steps] or g["gaps"][wl.steps] <= 2 * a0
+    assert seq.status()[0] == cfg.max_ctx
+    with pytest.raises(C.LfError) as e:
+        seq.step(0)
+    assert e.value.code == C.LF_ERANGE
+    torch.cuda.synchronize()
+    say(f"[prefill] {name}: position 4095 after one 4096-position chunk, max|d|={a0:.2e} rel={r0:.2e}")
