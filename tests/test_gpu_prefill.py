@@ -55,19 +55,23 @@ def _check_caches(seq, cache, n, what):
     return worst
 
 
-@pytest.mark.parametrize("cfg,plen,chunk,steps", [
-    (TINY, 1, 1, 4),
-    (TINY, 128, 128, 8),
-    (TINY, 128, 48, 8),
-    (RAGGED, 40, 17, 6),
-    (WIDE_GROUP, 150, 64, 6),
-    (MHA, 130, 100, 6),
+@pytest.mark.parametrize("cfg,plen,chunk,steps,mode", [
+    (TINY, 1, 1, 4, "graph"),
+    (TINY, 128, 128, 8, "graph"),
+    (TINY, 128, 48, 8, "graph"),
+    (TINY, 128, 48, 8, "persistent"),
+    (TINY, 128, 48, 8, "eager"),
+    (RAGGED, 40, 17, 6, "graph"),
+    (WIDE_GROUP, 150, 64, 6, "graph"),
+    (MHA, 130, 100, 6, "graph"),
 ])
-def test_prefill_batched_matches_oracle(cfg, plen, chunk, steps):
+def test_prefill_batched_matches_oracle(cfg, plen, chunk, steps, mode):
+    """The decode steps after the batched pass run in the given launch mode."""
     import torch
     from decode_step_05_amd import Decoder
+    from decode_step_05_amd import lfdecode as C
 
-    say(f"[prefill] cfg={cfg.name} prompt={plen} chunk={chunk} steps={steps} seeds=(0,1)")
+    say(f"[prefill] cfg={cfg.name} prompt={plen} chunk={chunk} steps={steps} mode={mode} seeds=(0,1)")
     w = make_weights(cfg, seed=0)
     prompt = make_prompt(cfg, plen, seed=1)
     o = OracleDecoder(cfg, w)
@@ -75,7 +79,9 @@ def test_prefill_batched_matches_oracle(cfg, plen, chunk, steps):
     o.forward_sequence(tokens=prompt, cache=cache)
     ref_z, ref_t = o.generate(prompt, steps)
 
-    dec = Decoder(cfg, w)
+    modes = {"persistent": C.LF_MODE_PERSISTENT, "graph": C.LF_MODE_GRAPH, "eager": C.LF_MODE_EAGER}
+    dec = Decoder(cfg, w, mode=modes[mode])
+    assert dec.mode == modes[mode]
     seq = dec.sequence()
     seq.prefill_batched(prompt, chunk=chunk)
     z, a = seq.logits()
