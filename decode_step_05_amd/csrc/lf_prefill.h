@@ -157,9 +157,10 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
 // S^T = K · Q^T (so lane l owns query l % 32 and 16 of the 32 keys; its
 // partner lane l ^ 32 holds the other 16), applies the mask, updates an online
 // softmax (running max and denominator per query), and adds V^T · P^T into
-// O^T (HD x 32 queries). Q^T and P^T are fed as hi + lo fp16 parts. V is
-// staged transposed in LDS so that each lane reads its keys for one head
-// dimension contiguously.
+// O^T (HD x 32 queries). Q^T and P^T are fed as hi + lo fp16 parts. Each key
+// tile is staged once per workgroup in LDS: K as rows, V transposed (so that a
+// lane reads its keys for one head dimension contiguously); the next tile's
+// loads are in flight meanwhile.
 struct PfAttnArgs {
   const float* q;    // [M][n_q][hd] rotated queries of the chunk
   const half_t* kc;  // this layer's K cache [lanes][max_ctx][kpl][hd], keys 0..pos0+M-1 written
