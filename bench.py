@@ -170,7 +170,8 @@ def main():
     ap.add_argument("--steps", type=int, default=512, help="timed decode steps (<= 512)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event timing pass")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps of the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-steps", type=int, default=96,
+                    help="oracle steps of the CPU baseline, about 10 s on 16 host threads (0 = skip)")
     ap.add_argument("--mode", choices=["default", "persistent", "graph", "eager"], default="default",
                     help="step launch mode (default: the library's choice)")
     ap.add_argument("--synthetic-cache", action="store_true",
