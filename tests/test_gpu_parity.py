@@ -316,6 +316,19 @@ def test_lane_share_full_depth():
     a, r = assert_close(got, want, "lane")
     assert seq.status()[0] == 4096
     say(f"[parity] lane: max|d|={a:.2e} rel={r:.2e}")
+    # the same step in the other two launch modes (the lane's 2 kv heads run
+    # QKV and attention as two kernels; the persistent kernel covers the shape)
+    torch = _torch()
+    dec = seq.dec
+    xin = torch.from_numpy(make_hidden(LANE, seed=2)).cuda()
+    for mode in ("eager", "persistent"):
+        dec.set_mode(_modes()[mode])
+        seq.set_len(4095)
+        xout = torch.empty_like(xin)
+        seq.step_hidden(xin, xout)
+        assert seq.status()[0] == 4096 and seq.status()[2] == 0
+        a, r = assert_close(xout.cpu().numpy(), want, f"lane {mode}")
+        say(f"[parity] lane {mode}: max|d|={a:.2e} rel={r:.2e}")
 
 
 def test_hidden_in_place():
