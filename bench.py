@@ -97,6 +97,84 @@ def lane_share(torch, Decoder):
             "hbm_gbs": round(moved / (us * 1e-6) / 1e9, 1), "roofline_us": round(moved / (PEAK_HBM_GBS * 1e3), 2)}
 
 
+def layer_rate(torch, Decoder, weights):
+    """Per-layer HBM rate of the Laneformer-shaped layer (d 4096, 32 q / 16 kv
+    heads x 128, SwiGLU 7168) at batch 1, cache of 2048 synthetic positions,
+    full causal and with a 1024-key window. Eight copies of the layer (the
+    first eight layers' weights of the full model, 2.2 GB) run as one
+    hidden-state chain so that no copy is still in the 256 MB last-level cache
+    when it is read again; 32 steps from p = 2048, time per layer = step / 8."""
+    from synth import LAYER_FULL, make_hidden, make_kv
+    from synth.gen import weight_names
+    n_copies, start, n = 8, 2048, 32
+    out = {}
+    for name, W in (("full", 0), ("swa1024", 1024)):
+        cfg = LAYER_FULL.replace(n_layers=n_copies, windows=(W,) * n_copies, name=f"layer_x8_{name}")
+        dec = Decoder(cfg, {k: weights[k] for k, _ in weight_names(cfg)})
+        seq = dec.sequence()
+        K_, V_ = make_kv(cfg, start, seed=2)
+        seq.load_cache(K_, V_)
+        xin = torch.from_numpy(make_hidden(cfg, seed=2)).cuda()
+        xout = torch.empty_like(xin)
+        for _ in range(4):
+            seq.step_hidden(xin, xout)
+        best = None
+        for _ in range(3):
+            seq.set_len(start)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                seq.step_hidden(xin, xout)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        moved = sum(step_bytes(cfg, p) for p in range(start, start + n))
+        us_layer = best * 1e3 / (n * n_copies)
+        out[name] = {"us_per_layer": round(us_layer, 2), "bytes_per_layer": moved // (n * n_copies),
+                     "hbm_gbs": round(moved / (best / 1e3) / 1e9, 1),
+                     "roofline_us": round(moved / (n * n_copies) / (PEAK_HBM_GBS * 1e3), 2)}
+        del seq, dec
+        torch.cuda.empty_cache()
+    out["workload"] = ("one Laneformer-shaped layer (d 4096, 32q/16kv x 128, SwiGLU 7168) x 8 weight copies, "
+                       "hidden in/out, cache of 2048 synthetic positions, 32 steps from p 2048; best of 3")
+    return out
+
+
+def ctx1024_rate(torch, dec, P=512, K=512):
+    """tok/s of the full model on the 512-token workload: a 512-token random
+    prompt through the prompt pass, then 512 device-fed greedy steps
+    (positions 512..1023, every window still covers the whole context)."""
+    from synth import make_prompt
+    cfg = dec.cfg
+    seq = dec.sequence()
+    prompt = torch.from_numpy(make_prompt(cfg, P, seed=1)).cuda()
+    seq.prefill_batched(prompt, chunk=PREFILL_CHUNK)
+    seq.step()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(3):
+        seq.set_len(P)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        seq.steps(K)
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1))
+    ms = float(sorted(runs)[1])
+    moved = sum(step_bytes(cfg, p) for p in range(P, P + K))
+    del seq
+    return {"workload": f"ctx1024: the same model, {P}-token random prompt, greedy decode of positions "
+                        f"{P}..{P + K - 1}; median of 3",
+            "tok_s": round(K / (ms / 1e3), 1), "ms_per_step": round(ms / K, 4),
+            "hbm_gbs": round(moved / (ms / 1e3) / 1e9, 1),
+            "roofline_tok_s_avg": round(PEAK_HBM_GBS * 1e9 / (moved / K), 1)}
+
+
 def prefill_flops(cfg, n):
     """Algorithmic flops of the prompt pass over positions 0..n-1: every
     projection as a GEMM of n rows (2 flops per weight per row), attention
@@ -360,6 +438,12 @@ def main():
     lane = lane_share(torch, Decoder)
     log(f"[bench] lane share: {lane['us_per_token']:.1f} us per token")
 
+    # the 512-token workload on the same model, then the single layer
+    ctx1024 = ctx1024_rate(torch, dec)
+    log(f"[bench] ctx1024: {ctx1024['tok_s']:.1f} tok/s")
+    layer = layer_rate(torch, Decoder, weights)
+    log(f"[bench] layer: full {layer['full']['us_per_layer']:.1f} us, swa {layer['swa1024']['us_per_layer']:.1f} us")
+
     cpu = None
     if args.cpu_steps > 0:
         del seq, dec
@@ -402,6 +486,8 @@ def main():
         "qkv_attention_fused": bool(fused),
         "stream_read_ceiling_gbs": round(ceiling, 1),
         "lane_share": lane,
+        "ctx1024": ctx1024,
+        "single_layer": layer,
         "prefill_s": round(prefill_s, 3),
         "prefill": prefill,
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
