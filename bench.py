@@ -175,6 +175,35 @@ def ctx1024_rate(torch, dec, P=512, K=512):
             "roofline_tok_s_avg": round(PEAK_HBM_GBS * 1e9 / (moved / K), 1)}
 
 
+def tiny_latency(torch, Decoder):
+    """Per-step latency of the tiny 2-layer decoder (d 256, 8 q / 4 kv heads x
+    32, SwiGLU 688, vocab 1024, layer 0 window 64): 128-token random prompt,
+    then 32 device-fed greedy steps. Its 3.4 MB of weights stay in cache, so
+    this is the launch-bound floor of a step, not an HBM measurement."""
+    from synth import TINY, make_prompt, make_weights
+    cfg = TINY
+    P, n = 128, 32
+    dec = Decoder(cfg, make_weights(cfg, seed=0))
+    seq = dec.sequence()
+    seq.prefill_batched(torch.from_numpy(make_prompt(cfg, P, seed=1)).cuda(), chunk=P)
+    seq.steps(4)
+    runs = []
+    for _ in range(5):
+        seq.set_len(P)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        seq.steps(n)
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) * 1e3 / n)
+    del seq, dec
+    return {"workload": f"tiny: 2 layers, d 256, 8q/4kv heads x 32, SwiGLU 688, vocab 1024, {P}-token prompt, "
+                        f"{n} greedy steps at positions {P}..{P + n - 1}; median of 5",
+            "us_per_step": round(float(sorted(runs)[2]), 2), "tok_s": round(1e6 / sorted(runs)[2], 1)}
+
+
 def prefill_flops(cfg, n):
     """Algorithmic flops of the prompt pass over positions 0..n-1: every
     projection as a GEMM of n rows (2 flops per weight per row), attention
@@ -443,6 +472,8 @@ def main():
     log(f"[bench] ctx1024: {ctx1024['tok_s']:.1f} tok/s")
     layer = layer_rate(torch, Decoder, weights)
     log(f"[bench] layer: full {layer['full']['us_per_layer']:.1f} us, swa {layer['swa1024']['us_per_layer']:.1f} us")
+    tiny = tiny_latency(torch, Decoder)
+    log(f"[bench] tiny decoder: {tiny['us_per_step']:.1f} us per step")
 
     cpu = None
     if args.cpu_steps > 0:
@@ -488,6 +519,7 @@ def main():
         "lane_share": lane,
         "ctx1024": ctx1024,
         "single_layer": layer,
+        "tiny_latency": tiny,
         "prefill_s": round(prefill_s, 3),
         "prefill": prefill,
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
