@@ -1,0 +1,96 @@
+// Temperature sampling of the next token, one workgroup per row of logits.
+//
+// Stochastic decoding for pass@N (asector.ru summary, "Performance and
+// infrastructure") draws several continuations of one prompt. The pages name
+// no sampler; the one here draws from softmax(z / T) by inverting its
+// cumulative distribution at a uniform u in [0, 1) that the caller supplies:
+// token i covers u in [c_{i-1}, c_i), c_i = p_0 + ... + p_i, so the draw is the
+// smallest i with c_i > u. Unnormalised: with w_i = exp((z_i - max z) / T) and
+// S = sum w, the draw is the smallest i with w_0 + ... + w_i > u * S and
+// w_i > 0; if fp32 rounding leaves none, the last i with w_i > 0.
+//
+// Layout: 1024 threads (16 waves); thread t owns the contiguous index range
+// [t*C, t*C + C), C = ceil(n / 1024), so the partial sums in thread order are
+// the cumulative sums in index order. Three passes over the row (max, sums,
+// search) read it from HBM once and from L2 after.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lf {
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / 64;
+
+__global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restrict__ logits, int n, float inv_t,
+                                                           const float* __restrict__ u,
+                                                           int32_t* __restrict__ tokens) {
+  __shared__ float red[kSampleWaves];
+  __shared__ float wave_off[kSampleWaves];
+  __shared__ int hit, last_pos;
+  const int row = blockIdx.x;
+  const float* z = logits + static_cast<size_t>(row) * n;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int chunk = (n + kSampleThreads - 1) / kSampleThreads;
+  const int i0 = min(t * chunk, n), i1 = min(i0 + chunk, n);
+  if (t == 0) {
+    hit = n;
+    last_pos = -1;
+  }
+
+  // 1. row maximum
+  float m = -INFINITY;
+  for (int i = i0; i < i1; ++i) m = fmaxf(m, z[i]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, red[w]);
+
+  // 2. this thread's weight sum, then an exclusive scan over threads
+  float s = 0.f;
+  for (int i = i0; i < i1; ++i) s += __expf((z[i] - m) * inv_t);
+  float inc = s;
+  for (int d = 1; d < 64; d <<= 1) {
+    const float v = __shfl_up(inc, d);
+    if (lane >= d) inc += v;
+  }
+  __syncthreads();  // every wave has read red[] for the maximum
+  if (lane == 63) red[wave] = inc;
+  __syncthreads();
+  if (t == 0) {
+    float acc = 0.f;
+    for (int w = 0; w < kSampleWaves; ++w) {
+      wave_off[w] = acc;
+      acc += red[w];
+    }
+    red[0] = acc;  // the total S (all waves have read red[] above)
+  }
+  __syncthreads();
+  const float total = red[0];
+  const float off = wave_off[wave] + (inc - s);
+  const float target = u[row] * total;
+
+  // 3. the first index whose cumulative weight passes the target
+  float c = off;
+  int mine = n, pos = -1;
+  for (int i = i0; i < i1; ++i) {
+    const float w = __expf((z[i] - m) * inv_t);
+    c += w;
+    if (w > 0.f) {
+      pos = i;
+      if (c > target) {
+        mine = i;
+        break;
+      }
+    }
+  }
+  // without a hit the loop ran to the end: pos is the range's last positive index
+  if (mine < n) atomicMin(&hit, mine);
+  if (pos >= 0) atomicMax(&last_pos, pos);
+  __syncthreads();
+  if (t == 0) tokens[row] = hit < n ? hit : last_pos;
+}
+
+}  // namespace lf

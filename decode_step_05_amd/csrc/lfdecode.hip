@@ -5,6 +5,7 @@
 #include "lf_kernels.h"
 #include "lf_stream.h"
 #include "lf_prefill.h"
+#include "lf_sample.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -1215,6 +1216,18 @@ int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const f
   kv->len += 1;
   for (int i = 0; i < tm.n; ++i) LF_HIP(hipEventElapsedTime(&ms[i], m->events[2 * i], m->events[2 * i + 1]));
   *n_out = tm.n;
+  return LF_OK;
+}
+
+int lf_sample(const float* d_logits, int32_t rows, int32_t n, float temperature, const float* d_u, int32_t* d_tokens,
+              void* stream) {
+  if (!d_logits || !d_u || !d_tokens) return fail(LF_EINVAL, "null argument");
+  if (rows < 1 || n < 1 || n > (1 << 24)) return fail(LF_EINVAL, "need rows >= 1 and 1 <= n <= 2^24");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(LF_EINVAL, "temperature must be positive and finite");
+  hipLaunchKernelGGL(lf::k_sample, dim3(rows), dim3(lf::kSampleThreads), 0, static_cast<hipStream_t>(stream),
+                     d_logits, n, 1.f / temperature, d_u, d_tokens);
+  LF_HIP(hipPeekAtLastError());
   return LF_OK;
 }
 

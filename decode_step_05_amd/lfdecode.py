@@ -24,7 +24,7 @@ EXPORTS = (
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_prefill_workspace_bytes", "lf_prefill_batched",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
-    "lf_step_kernel_times", "lf_kernel_time", "lf_read_bandwidth", "lf_last_error",
+    "lf_step_kernel_times", "lf_kernel_time", "lf_read_bandwidth", "lf_sample", "lf_last_error",
 )
 
 KERNEL_KINDS = ("qkv", "attn", "o", "gate_up", "down", "lm_head", "qkv_attn")
@@ -88,6 +88,7 @@ def load():
                                          POINTER(c_int32), P]),
         "lf_kernel_time": (c_int, [P, P, c_int32, c_int32, c_int32, c_int32, P, P, POINTER(c_float), P]),
         "lf_read_bandwidth": (c_int, [P, c_size_t, c_int32, P, POINTER(c_float), P]),
+        "lf_sample": (c_int, [P, c_int32, c_int32, c_float, P, P, P]),
         "lf_last_error": (c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -258,6 +259,16 @@ def lf_decode_step_hidden(model, kv, x_in, x_out, stream=None) -> None:
 
 def lf_logits(model, kv, logits, argmax=None, stream=None) -> None:
     _check(load().lf_logits(model, kv, _ptr(logits), _ptr(argmax), _stream(stream)))
+
+
+def lf_sample(logits, temperature, u, tokens, stream=None) -> None:
+    """Temperature draw per row: logits device fp32 [rows, n] (or [n]), u device
+    fp32 [rows], tokens device int32 [rows] (written)."""
+    rows = int(u.numel())
+    n = int(logits.shape[-1])
+    if logits.numel() != rows * n or tokens.numel() != rows:
+        raise ValueError("logits must be [rows, n], u and tokens [rows]")
+    _check(load().lf_sample(_ptr(logits), rows, n, float(temperature), _ptr(u), _ptr(tokens), _stream(stream)))
 
 
 def lf_kv_status(kv, stream=None):

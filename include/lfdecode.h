@@ -303,6 +303,31 @@ int lf_kernel_time(lf_model* m, lf_kv* kv, int32_t kind, int32_t layer, int32_t 
  */
 int lf_read_bandwidth(const void* d_buf, size_t bytes, int32_t iters, void* d_sink, float* gbs, void* stream);
 
+/*
+ * Temperature sampling of the next token, for stochastic (pass@N) decoding,
+ * which the asector.ru summary ("Performance and infrastructure") proposes for
+ * code: several sampled continuations of one prompt. The pages name no
+ * sampler; this one inverts the cumulative distribution of
+ * p = softmax(z / temperature) at a caller-given uniform u: for each row r,
+ * d_tokens[r] = the smallest i with p_0 + ... + p_i > d_u[r] (token i covers
+ * u in [c_{i-1}, c_i)); tokens of probability 0 are never drawn, and if fp32
+ * rounding leaves the total below u the last token of positive probability is
+ * drawn. Computed in fp32 (weights exp((z_i - max z) / T), cumulative sums in
+ * index order), one workgroup per row.
+ *
+ * d_logits: device fp32 [rows, n], row-major, finite values (the logits that
+ * lf_logits copies out, or any others). d_u: device fp32 [rows], each in
+ * [0, 1); a value below 0 draws the first token of positive probability, a
+ * value of 1 or more the last. d_tokens: device int32 [rows], written. All
+ * three are caller-owned; nothing is allocated. Asynchronous on `stream`; to
+ * continue a sequence with the drawn token pass d_tokens + r to lf_decode_step.
+ * LF_EINVAL for null pointers, rows < 1, n < 1 or n > 2^24, or a temperature
+ * that is not positive and finite (greedy decoding is lf_decode_step's own
+ * argmax); LF_EHIP if the launch fails.
+ */
+int lf_sample(const float* d_logits, int32_t rows, int32_t n, float temperature, const float* d_u, int32_t* d_tokens,
+              void* stream);
+
 /* Text of the calling thread's last error ("" if none). */
 const char* lf_last_error(void);
 

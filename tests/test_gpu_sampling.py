@@ -1,0 +1,132 @@
+"""GPU parity of temperature sampling (lf_sample) with the oracle's inverse-CDF
+draw. The logits either come from a seeded generator or from the oracle's own
+decoder; the GPU samples the same fp32 values. Both sides decide the token in
+their own precision (fp32 on the GPU, float64 in the oracle), so a different
+token is accepted only where u lies within EPS of the GPU token's float64
+interval: fp32 rounding of the weights and of the cumulative sums (at most 33
+terms per thread, then a 1024-thread scan) moves an interval end by a few 1e-6
+at most."""
+import numpy as np
+import pytest
+
+from oracle import OracleDecoder, interval_of, sample_token
+from synth import TINY, make_prompt, make_weights
+
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-5
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _C():
+    from decode_step_05_amd import lfdecode as C
+    return C
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _logit_rows(rng, n, rows):
+    # the LM head's logits at random init have std about 0.02 * sqrt(4096) = 1.28
+    return (rng.standard_normal((rows, n)) * 1.28).astype(np.float32)
+
+
+def _check_rows(z, T, u, got):
+    exact = 0
+    for r in range(z.shape[0]):
+        want = sample_token(z[r].astype(np.float64), T, float(u[r]))
+        if got[r] == want:
+            exact += 1
+            continue
+        lo, hi = interval_of(z[r].astype(np.float64), T, int(got[r]))
+        assert lo - EPS <= u[r] < hi + EPS, (r, T, float(u[r]), int(got[r]), want, lo, hi)
+    return exact
+
+
+@pytest.mark.parametrize("n", [1, 7, 1000, 1024, 1025, 32000, 33000])
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
+def test_sample_rows_match_oracle(n, T):
+    torch, C = _torch(), _C()
+    rows = 64
+    rng = np.random.default_rng(1000 * n + int(10 * T))
+    say(f"[sampling] rows={rows} n={n} T={T}")
+    z = _logit_rows(rng, n, rows)
+    u = rng.random(rows).astype(np.float32)
+    u[0], u[1] = 0.0, np.float32(0.99999994)  # both ends of [0, 1)
+    zd, ud = torch.from_numpy(z).cuda(), torch.from_numpy(u).cuda()
+    tok = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    C.lf_sample(zd, T, ud, tok)
+    got = tok.cpu().numpy()
+    assert np.all((got >= 0) & (got < n))
+    exact = _check_rows(z, T, u, got)
+    assert exact >= rows - 2, f"{rows - exact} draws differ"
+
+
+def test_sample_zero_probability_tokens_and_ties():
+    torch, C = _torch(), _C()
+    n, rows = 5000, 256
+    rng = np.random.default_rng(7)
+    z = np.full((rows, n), -1e30, dtype=np.float32)  # probability 0 in both precisions
+    live = rng.choice(n, size=40, replace=False)
+    z[:, live] = np.round(rng.standard_normal(40) * 2).astype(np.float32)  # integer values: many exact ties
+    u = ((np.arange(rows) + 0.5) / rows).astype(np.float32)
+    say(f"[sampling] zero-probability tokens and ties, n={n}")
+    zd, ud = torch.from_numpy(z).cuda(), torch.from_numpy(u).cuda()
+    tok = torch.empty(rows, dtype=torch.int32, device="cuda")
+    C.lf_sample(zd, 1.0, ud, tok)
+    got = tok.cpu().numpy()
+    assert set(got.tolist()) <= set(live.tolist())
+    assert _check_rows(z, 1.0, u, got) >= rows - 2
+    # low temperature: the draw is the greedy token (lowest index among the maxima)
+    C.lf_sample(zd, 1e-4, ud, tok)
+    first_max = int(np.flatnonzero(z[0] == z[0].max())[0])
+    ties = np.flatnonzero(z[0] == z[0].max())
+    assert set(tok.cpu().numpy().tolist()) <= set(ties.tolist())
+    assert int(tok[0].item()) == first_max
+
+
+def test_sampled_decode_matches_oracle():
+    # the tiny decoder: prompt of 24 tokens, then 16 sampled steps at T = 0.8;
+    # the GPU samples its own logits, the oracle its own, with the same u
+    torch, C = _torch(), _C()
+    from decode_step_05_amd import Decoder
+    cfg = TINY
+    w = make_weights(cfg, seed=0)
+    prompt = make_prompt(cfg, 24, seed=1)
+    T, n_steps = 0.8, 16
+    u = np.random.default_rng(3).random(n_steps).astype(np.float32)
+    say(f"[sampling] tiny decoder, {n_steps} sampled steps at T={T}")
+    dec = Decoder(cfg, w)
+    seq = dec.sequence()
+    seq.prefill(prompt)
+    orc = OracleDecoder(cfg, w)
+    cache = orc.new_cache()
+    for t in prompt:
+        zo = orc.step(cache, token=int(t))
+    ud = torch.from_numpy(u).cuda()
+    tok = torch.empty(n_steps, dtype=torch.int32, device="cuda")
+    near = 0
+    for k in range(n_steps):
+        zg, _ = seq.logits()
+        a, _ = assert_close(zg.cpu().numpy(), zo, f"sampled step {k}")
+        C.lf_sample(zg, T, ud[k:k + 1], tok[k:k + 1])
+        g, o = int(tok[k].item()), sample_token(zo, T, float(u[k]))
+        if g != o:
+            # the logits differ by at most a; the cumulative distribution moves by about 2a/T
+            lo, hi = interval_of(zo, T, g)
+            d = 2 * a / T + EPS
+            assert lo - d <= u[k] < hi + d, (k, g, o, float(u[k]), lo, hi)
+            near += 1
+            seq.step(o)
+        else:
+            seq.step(tok[k:k + 1])
+        zo = orc.step(cache, token=o)
+    say(f"[sampling] tiny decoder: {near} near-boundary draws forced to the oracle's token")
+    assert near <= 2
+    assert seq.status()[0] == len(prompt) + n_steps

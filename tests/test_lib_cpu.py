@@ -150,3 +150,16 @@ def test_prefill_workspace_sizes_and_null_checks():
     assert C.lf_prefill_workspace_bytes(C.make_config(TINY), 64) > 0
     assert lib.lf_prefill_batched(None, None, None, 1, 16, None, 0, None) == C.LF_EINVAL
     assert lib.lf_prefill_batched(None, None, 0x1000, 1, 16, 0x1000, 1 << 20, None) == C.LF_EINVAL
+
+
+def test_sample_argument_errors_before_any_device_call():
+    lib = C.load()
+    assert lib.lf_sample(None, 1, 10, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
+    assert lib.lf_sample(0x1000, 1, 10, 1.0, None, 0x1000, None) == C.LF_EINVAL
+    assert lib.lf_sample(0x1000, 1, 10, 1.0, 0x1000, None, None) == C.LF_EINVAL
+    assert lib.lf_sample(0x1000, 0, 10, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
+    assert lib.lf_sample(0x1000, 1, 0, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
+    assert lib.lf_sample(0x1000, 1, (1 << 24) + 1, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
+    for t in (0.0, -1.0, float("nan"), float("inf")):
+        rc = lib.lf_sample(0x1000, 1, 10, t, 0x1000, 0x1000, None)
+        assert rc == C.LF_EINVAL and "temperature" in C.lf_last_error()
