@@ -204,6 +204,31 @@ def tiny_latency(torch, Decoder):
             "us_per_step": round(float(sorted(runs)[2]), 2), "tok_s": round(1e6 / sorted(runs)[2], 1)}
 
 
+def sampling_time(torch, C, vocab=32000):
+    """Microseconds per lf_sample launch (temperature 0.8) over 1 and 8 rows
+    of vocab-wide fp32 logits, seeded N(0, 1.28) like the LM head's output at
+    random init; 100 launches back to back between two events."""
+    import numpy as np
+    out = {}
+    for rows in (1, 8):
+        rng = np.random.default_rng(4)
+        z = torch.from_numpy((rng.standard_normal((rows, vocab)) * 1.28).astype(np.float32)).cuda()
+        u = torch.from_numpy(rng.random(rows).astype(np.float32)).cuda()
+        tok = torch.empty(rows, dtype=torch.int32, device="cuda")
+        C.lf_sample(z, 0.8, u, tok)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(100):
+            C.lf_sample(z, 0.8, u, tok)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"rows{rows}_us"] = round(e0.elapsed_time(e1) * 10, 2)
+    out["workload"] = f"temperature sampling of {vocab}-wide fp32 logits, 1 and 8 rows per launch"
+    return out
+
+
 def prefill_flops(cfg, n):
     """Algorithmic flops of the prompt pass over positions 0..n-1: every
     projection as a GEMM of n rows (2 flops per weight per row), attention
@@ -474,6 +499,8 @@ def main():
     log(f"[bench] layer: full {layer['full']['us_per_layer']:.1f} us, swa {layer['swa1024']['us_per_layer']:.1f} us")
     tiny = tiny_latency(torch, Decoder)
     log(f"[bench] tiny decoder: {tiny['us_per_step']:.1f} us per step")
+    sampling = sampling_time(torch, C)
+    log(f"[bench] sampling: {sampling['rows1_us']:.1f} us (1 row), {sampling['rows8_us']:.1f} us (8 rows)")
 
     cpu = None
     if args.cpu_steps > 0:
@@ -520,6 +547,7 @@ def main():
         "ctx1024": ctx1024,
         "single_layer": layer,
         "tiny_latency": tiny,
+        "sampling": sampling,
         "prefill_s": round(prefill_s, 3),
         "prefill": prefill,
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},

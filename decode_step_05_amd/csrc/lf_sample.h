@@ -11,8 +11,11 @@
 //
 // Layout: 1024 threads (16 waves); thread t owns the contiguous index range
 // [t*C, t*C + C), C = ceil(n / 1024), so the partial sums in thread order are
-// the cumulative sums in index order. Three passes over the row (max, sums,
-// search) read it from HBM once and from L2 after.
+// the cumulative sums in index order. A row that fits in LDS (up to 35,747
+// logits) is first staged there with coalesced loads, one padding word per 32
+// so that the threads' contiguous ranges fall in different banks, and each
+// weight is computed once, in place. A longer row is read three times (max,
+// sums, search) from global memory, the same arithmetic in the same order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,10 +25,17 @@ namespace lf {
 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
+constexpr int kSampleLdsFloats = 36 * 1024;  // 144 KB of the 160 KB per CU
+
+// padded LDS slot of logit i: one spare word after every 32
+__host__ __device__ constexpr int sample_slot(int i) { return i + (i >> 5); }
+// whether a row of n >= 1 logits is staged in LDS
+__host__ __device__ constexpr bool sample_fits_lds(int n) { return sample_slot(n - 1) < kSampleLdsFloats; }
 
 __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restrict__ logits, int n, float inv_t,
                                                            const float* __restrict__ u,
-                                                           int32_t* __restrict__ tokens) {
+                                                           int32_t* __restrict__ tokens, int staged) {
+  extern __shared__ float row_w[];  // staged rows: the logits, then their weights, at sample_slot(i)
   __shared__ float red[kSampleWaves];
   __shared__ float wave_off[kSampleWaves];
   __shared__ int hit, last_pos;
@@ -39,9 +49,17 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restri
     last_pos = -1;
   }
 
-  // 1. row maximum
+  // 1. row maximum (staged rows: while loading them, coalesced)
   float m = -INFINITY;
-  for (int i = i0; i < i1; ++i) m = fmaxf(m, z[i]);
+  if (staged) {
+    for (int i = t; i < n; i += kSampleThreads) {
+      const float v = z[i];
+      row_w[sample_slot(i)] = v;
+      m = fmaxf(m, v);
+    }
+  } else {
+    for (int i = i0; i < i1; ++i) m = fmaxf(m, z[i]);
+  }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (lane == 0) red[wave] = m;
   __syncthreads();
@@ -49,8 +67,17 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restri
   for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, red[w]);
 
   // 2. this thread's weight sum, then an exclusive scan over threads
+  // (the barrier of the maximum also orders the staging stores before these reads)
   float s = 0.f;
-  for (int i = i0; i < i1; ++i) s += __expf((z[i] - m) * inv_t);
+  if (staged) {
+    for (int i = i0; i < i1; ++i) {
+      const float w = __expf((row_w[sample_slot(i)] - m) * inv_t);
+      row_w[sample_slot(i)] = w;
+      s += w;
+    }
+  } else {
+    for (int i = i0; i < i1; ++i) s += __expf((z[i] - m) * inv_t);
+  }
   float inc = s;
   for (int d = 1; d < 64; d <<= 1) {
     const float v = __shfl_up(inc, d);
@@ -76,7 +103,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restri
   float c = off;
   int mine = n, pos = -1;
   for (int i = i0; i < i1; ++i) {
-    const float w = __expf((z[i] - m) * inv_t);
+    const float w = staged ? row_w[sample_slot(i)] : __expf((z[i] - m) * inv_t);
     c += w;
     if (w > 0.f) {
       pos = i;

@@ -1225,8 +1225,14 @@ int lf_sample(const float* d_logits, int32_t rows, int32_t n, float temperature,
   if (rows < 1 || n < 1 || n > (1 << 24)) return fail(LF_EINVAL, "need rows >= 1 and 1 <= n <= 2^24");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(LF_EINVAL, "temperature must be positive and finite");
-  hipLaunchKernelGGL(lf::k_sample, dim3(rows), dim3(lf::kSampleThreads), 0, static_cast<hipStream_t>(stream),
-                     d_logits, n, 1.f / temperature, d_u, d_tokens);
+  const bool staged = lf::sample_fits_lds(n);
+  const size_t lds = staged ? sizeof(float) * (lf::sample_slot(n - 1) + 1) : 0;
+  const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(lf::k_sample),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                sizeof(float) * lf::kSampleLdsFloats);
+  if (lds_ok != hipSuccess) return fail(LF_EHIP, "sampling kernel LDS limit: %s", hipGetErrorString(lds_ok));
+  hipLaunchKernelGGL(lf::k_sample, dim3(rows), dim3(lf::kSampleThreads), lds, static_cast<hipStream_t>(stream),
+                     d_logits, n, 1.f / temperature, d_u, d_tokens, staged ? 1 : 0);
   LF_HIP(hipPeekAtLastError());
   return LF_OK;
 }

@@ -5,7 +5,8 @@ their own precision (fp32 on the GPU, float64 in the oracle), so a different
 token is accepted only where u lies within EPS of the GPU token's float64
 interval: fp32 rounding of the weights and of the cumulative sums (at most 33
 terms per thread, then a 1024-thread scan) moves an interval end by a few 1e-6
-at most."""
+at most. Rows of up to 35,747 logits are staged in LDS, longer ones read
+from global memory: both paths are covered."""
 import numpy as np
 import pytest
 
@@ -49,7 +50,7 @@ def _check_rows(z, T, u, got):
     return exact
 
 
-@pytest.mark.parametrize("n", [1, 7, 1000, 1024, 1025, 32000, 33000])
+@pytest.mark.parametrize("n", [1, 7, 1000, 1024, 1025, 32000, 33000, 35747, 35748, 70000])
 @pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
 def test_sample_rows_match_oracle(n, T):
     torch, C = _torch(), _C()
