@@ -70,10 +70,18 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restri
   // (the barrier of the maximum also orders the staging stores before these reads)
   float s = 0.f;
   if (staged) {
-    for (int i = i0; i < i1; ++i) {
-      const float w = __expf((row_w[sample_slot(i)] - m) * inv_t);
-      row_w[sample_slot(i)] = w;
-      s += w;
+    // eight LDS reads in flight, then the weights in index order
+    for (int b = i0; b < i1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = b + k < i1 ? row_w[sample_slot(b + k)] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (b + k < i1) {
+          const float w = __expf((v[k] - m) * inv_t);
+          row_w[sample_slot(b + k)] = w;
+          s += w;
+        }
     }
   } else {
     for (int i = i0; i < i1; ++i) s += __expf((z[i] - m) * inv_t);
@@ -102,20 +110,31 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restri
   // 3. the first index whose cumulative weight passes the target
   float c = off;
   int mine = n, pos = -1;
-  for (int i = i0; i < i1; ++i) {
-    const float w = staged ? row_w[sample_slot(i)] : __expf((z[i] - m) * inv_t);
-    c += w;
-    if (w > 0.f) {
-      pos = i;
-      if (c > target) {
-        mine = i;
-        break;
+  for (int b = i0; b < i1 && mine == n; b += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = b + k >= i1 ? 0.f : staged ? row_w[sample_slot(b + k)] : __expf((z[b + k] - m) * inv_t);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = v[k];
+      c += w;
+      if (mine == n && b + k < i1 && w > 0.f) {
+        pos = b + k;
+        if (c > target) mine = b + k;
       }
     }
   }
   // without a hit the loop ran to the end: pos is the range's last positive index
-  if (mine < n) atomicMin(&hit, mine);
-  if (pos >= 0) atomicMax(&last_pos, pos);
+  // one LDS atomic per wave: every thread past the hit also hits, on its first index
+  for (int o = 32; o > 0; o >>= 1) {
+    mine = min(mine, __shfl_xor(mine, o));
+    pos = max(pos, __shfl_xor(pos, o));
+  }
+  if (lane == 0) {
+    if (mine < n) atomicMin(&hit, mine);
+    if (pos >= 0) atomicMax(&last_pos, pos);
+  }
   __syncthreads();
   if (t == 0) tokens[row] = hit < n ? hit : last_pos;
 }
