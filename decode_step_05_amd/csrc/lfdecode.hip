@@ -7,6 +7,7 @@
 #include "lf_prefill.h"
 #include "lf_sample.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -1229,16 +1230,16 @@ int lf_sample(const float* d_logits, int32_t rows, int32_t n, float temperature,
   const size_t lds = staged ? sizeof(float) * (lf::sample_slot(n - 1) + 1) : 0;
   // the kernel's LDS limit is raised once per device (two threads racing here set the same value)
   constexpr int kMaxDevices = 64;
-  static bool lds_set[kMaxDevices];
+  static std::atomic<bool> lds_set[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return fail(LF_EHIP, "no usable current device for sampling");
-  if (!lds_set[dev]) {
+  if (!lds_set[dev].load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(lf::k_sample),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              sizeof(float) * lf::kSampleLdsFloats);
     if (e != hipSuccess) return fail(LF_EHIP, "sampling kernel LDS limit: %s", hipGetErrorString(e));
-    lds_set[dev] = true;
+    lds_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL(lf::k_sample, dim3(rows), dim3(lf::kSampleThreads), lds, static_cast<hipStream_t>(stream),
                      d_logits, n, 1.f / temperature, d_u, d_tokens, staged ? 1 : 0);
