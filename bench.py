@@ -229,6 +229,33 @@ def sampling_time(torch, C, vocab=32000):
     return out
 
 
+def sampled_rate(torch, C, dec, seq, P, n=64, T=0.8):
+    """tok/s of sampled decoding on the ctx4096 model: after one greedy step
+    at position P, n steps at P+1 .. P+n, each a copy of the logits, a
+    temperature draw (lf_sample, T = 0.8, seeded u) and the decode step fed
+    with the drawn token; all on the device, between two events."""
+    import numpy as np
+    u = torch.from_numpy(np.random.default_rng(5).random(n).astype(np.float32)).cuda()
+    z = torch.empty(dec.cfg.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.empty(n, dtype=torch.int32, device="cuda")
+    seq.set_len(P)
+    seq.step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(n):
+        C.lf_logits(dec.handle, seq.handle, z)
+        C.lf_sample(z, T, u[k:k + 1], tok[k:k + 1])
+        seq.step(tok[k:k + 1])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    return {"workload": f"sampled decode at T {T} of positions {P + 1}..{P + n}: logits copy, lf_sample, "
+                        "decode step fed with the drawn token",
+            "ms_per_step": round(ms, 4), "tok_s": round(1e3 / ms, 1)}
+
+
 def prefill_flops(cfg, n):
     """Algorithmic flops of the prompt pass over positions 0..n-1: every
     projection as a GEMM of n rows (2 flops per weight per row), attention
@@ -479,6 +506,8 @@ def main():
     torch.cuda.synchronize()
     fixed_ms = e0.elapsed_time(e1) / n_fixed
     fused = dec.fused
+    sampled = sampled_rate(torch, C, dec, seq, P)
+    log(f"[bench] sampled decode: {sampled['tok_s']:.1f} tok/s")
 
     # practical read ceiling: a plain streaming read of 4 GiB
     buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
@@ -548,6 +577,7 @@ def main():
         "single_layer": layer,
         "tiny_latency": tiny,
         "sampling": sampling,
+        "sampled_decode": sampled,
         "prefill_s": round(prefill_s, 3),
         "prefill": prefill,
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
