@@ -318,7 +318,7 @@ int lf_read_bandwidth(const void* d_buf, size_t bytes, int32_t iters, void* d_si
  * d_logits: device fp32 [rows, n], row-major, finite values (the logits that
  * lf_logits copies out, or any others). d_u: device fp32 [rows], each in
  * [0, 1); a value below 0 draws the first token of positive probability, a
- * value of 1 or more the last. d_tokens: device int32 [rows], written. All
+ * value of 1 or more (or NaN) the last. d_tokens: device int32 [rows], written. All
  * three are caller-owned; nothing is allocated. Asynchronous on `stream`; to
  * continue a sequence with the drawn token pass d_tokens + r to lf_decode_step.
  * LF_EINVAL for null pointers, rows < 1, n < 1 or n > 2^24, or a temperature
