@@ -385,3 +385,25 @@ def test_full_model_step_at_ctx4096():
         ma, r = assert_close(got, want, f"full@4096 {mode}")
         assert check_token(tok, want, ma), (mode, tok, greedy_fp32(want))
         say(f"[parity] full@4096 {mode}: max|d|={ma:.2e} rel={r:.2e} token={tok}")
+    # temperature draws from the full-size logits: the GPU samples its own, the
+    # oracle its own, with the same u; a different token only where u lies
+    # within 2 max|d| / T (plus fp32 rounding) of the GPU token's interval
+    from decode_step_05_amd import lfdecode as C
+    from oracle import interval_of, sample_token
+    got, _ = results["graph"]
+    ma = float(np.abs(got - want).max())
+    T, n = 0.8, 16
+    u = np.random.default_rng(6).random(n).astype(np.float32)
+    zd = torch.from_numpy(np.repeat(got[None, :], n, axis=0)).cuda()
+    tok = torch.empty(n, dtype=torch.int32, device="cuda")
+    C.lf_sample(zd, T, torch.from_numpy(u).cuda(), tok)
+    differ = 0
+    for k, g in enumerate(tok.cpu().numpy().tolist()):
+        o = sample_token(want, T, float(u[k]))
+        if g != o:
+            lo, hi = interval_of(want, T, g)
+            d = 2 * ma / T + 1e-5
+            assert lo - d <= u[k] < hi + d, (k, g, o, float(u[k]), lo, hi)
+            differ += 1
+    say(f"[parity] full@4096 sampled at T={T}: {differ} of {n} draws differ (near a boundary)")
+    assert differ <= 2
