@@ -3,13 +3,19 @@
 context 4096 on one MI355X.
 
 Workload: seeded random fp16 weights (N(0, 0.02)), a 3584-token random
-prompt, then greedy decode steps toward 4096 positions (each step reads every
+prompt, then greedy decode steps up to 4096 positions (each step reads every
 weight once plus the visible KV cache: 5 full-attention layers see all
 positions, 10 sliding-window layers at most 1024). The prompt is filled by
 the batched prompt pass on the matrix cores, timed on its own (`prefill`).
-W warm-up steps run first; the sequence is then rewound to the prompt so the
-K timed steps replay the same positions 3584 .. 3584+K-1, device-fed (the
-greedy token never leaves the GPU), as hipGraph replays.
+The whole greedy generation (positions 3584 .. 4095) then runs once untimed,
+device-fed, and its tokens are compared with the oracle's stored tokens of
+the same seeded workload (tests/golden/oracle_ctx4096.npz). The K timed steps
+are the last K of that generation, positions 4096-K .. 4095 (context 4096 at
+the last), replayed after W warm-up steps as hipGraph replays, device-fed
+(the greedy token never leaves the GPU). After every timed region the
+sequence's status word is read: a wait between workgroups that gave up, or a
+token id that had to be clamped, ends the run with an error, and the timed
+region's tokens must equal those of the checked generation.
 
 Prints one JSON line (see the fields below). `--gpus N` with N > 1 is refused:
 this path runs on one GPU.
@@ -65,6 +71,62 @@ def step_bytes(cfg, p):
     return w + kv
 
 
+def golden_tokens(name):
+    """The oracle's greedy tokens of a generation workload, stored by
+    tests/golden/make_golden.py (token s = greedy choice at prompt_len-1+s),
+    with the oracle's top-2 gaps; None if the file is missing."""
+    import numpy as np
+    path = os.path.join(ROOT, "tests", "golden", f"oracle_{name}.npz")
+    if not os.path.exists(path):
+        return None
+    g = np.load(path)
+    return g["tokens"], g["gaps"]
+
+
+def compare_tokens(got, gold, what, near=4e-2):
+    """True if the device-fed chain gives the oracle's tokens. A first
+    difference where the oracle's top-2 gap is at most `near` (twice the
+    parity bound on a logit) is a near-tie: the chains may part there, the
+    run goes on, and the tokens before it matched. Any other difference ends
+    the run."""
+    if gold is None:
+        log(f"[bench] {what}: no stored oracle tokens, not checked")
+        return False
+    toks, gaps = gold
+    n = min(len(got), len(toks))
+    for s in range(n):
+        if int(got[s]) != int(toks[s]):
+            if gaps[s] <= near:
+                log(f"[bench] {what}: near-tie at step {s} (oracle gap {gaps[s]:.2e}); {s} tokens matched")
+                return True
+            log(f"[bench] {what}: token {int(got[s])} != oracle {int(toks[s])} at step {s} (gap {gaps[s]:.3f})")
+            sys.exit(1)
+    log(f"[bench] {what}: all {n} tokens equal the oracle's")
+    return True
+
+
+def check_status(seq, want_len, what):
+    """End the run if a wait between workgroups gave up (status bit 1), a token
+    id was clamped (bit 0), or the sequence is not where it should be."""
+    n, _, flags = seq.status()
+    if flags or n != want_len:
+        log(f"[bench] {what}: sequence status length {n} (expected {want_len}), flags {flags}: results invalid")
+        sys.exit(1)
+
+
+def check_timed(seq, want_len, ref_tokens, first, what):
+    """check_status, and the tokens the timed steps wrote (history entries
+    P+first+1 ..) equal those of the checked generation."""
+    import numpy as np
+    check_status(seq, want_len, what)
+    P = want_len - (len(ref_tokens) - 1)
+    n = len(ref_tokens) - 1 - first
+    got = seq.tokens(P + first + 1, n).cpu().numpy()
+    if not np.array_equal(got, ref_tokens[first + 1:]):
+        log(f"[bench] {what}: tokens differ from the checked generation")
+        sys.exit(1)
+
+
 def lane_share(torch, Decoder):
     """Per-token latency of one lane's share of the decoder (the per-GPU
     slice of the 8-way lane split) at ctx 4096: hidden-state steps, no
@@ -89,6 +151,7 @@ def lane_share(torch, Decoder):
         seq.step_hidden(xin, xout)
     e1.record()
     torch.cuda.synchronize()
+    check_status(seq, start + n, "lane share")
     us = e0.elapsed_time(e1) * 1e3 / n
     moved = sum(step_bytes(cfg, p) for p in range(start, start + n)) / n
     return {"workload": "lane: 15 layers, 4 q / 2 kv heads x 128, QKV 1024x4096, O 4096x512, gate/up 1792x4096, "
@@ -129,6 +192,7 @@ def layer_rate(torch, Decoder, weights):
                 seq.step_hidden(xin, xout)
             e1.record()
             torch.cuda.synchronize()
+            check_status(seq, start + n, f"single layer {name}")
             ms = e0.elapsed_time(e1)
             best = ms if best is None else min(best, ms)
         moved = sum(step_bytes(cfg, p) for p in range(start, start + n))
@@ -164,13 +228,15 @@ def ctx1024_rate(torch, dec, P=512, K=512):
         seq.steps(K)
         e1.record()
         torch.cuda.synchronize()
+        check_status(seq, P + K, "ctx1024")
         runs.append(e0.elapsed_time(e1))
+    checked = compare_tokens(seq.tokens(P, K + 1).cpu().numpy(), golden_tokens("ctx1024"), "ctx1024 generation")
     ms = float(sorted(runs)[1])
     moved = sum(step_bytes(cfg, p) for p in range(P, P + K))
     del seq
     return {"workload": f"ctx1024: the same model, {P}-token random prompt, greedy decode of positions "
                         f"{P}..{P + K - 1}; median of 3",
-            "tok_s": round(K / (ms / 1e3), 1), "ms_per_step": round(ms / K, 4),
+            "tok_s": round(K / (ms / 1e3), 1), "ms_per_step": round(ms / K, 4), "checked": checked,
             "hbm_gbs": round(moved / (ms / 1e3) / 1e9, 1),
             "roofline_tok_s_avg": round(PEAK_HBM_GBS * 1e9 / (moved / K), 1)}
 
@@ -250,6 +316,7 @@ def sampled_rate(torch, C, dec, seq, P, n=64, T=0.8):
         seq.step(tok[k:k + 1])
     e1.record()
     torch.cuda.synchronize()
+    check_status(seq, P + 1 + n, "sampled decode")
     ms = e0.elapsed_time(e1) / n
     return {"workload": f"sampled decode at T {T} of positions {P + 1}..{P + n}: logits copy, lf_sample, "
                         "decode step fed with the drawn token",
@@ -326,12 +393,12 @@ def cpu_baseline(cfg, weights, n_steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512, help="timed decode steps (<= 512)")
+    ap.add_argument("--steps", type=int, default=512, help="timed decode steps, the last of the generation (<= 512)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event timing pass")
     ap.add_argument("--cpu-steps", type=int, default=96,
                     help="oracle steps of the CPU baseline, about 10 s on 16 host threads (0 = skip)")
-    ap.add_argument("--mode", choices=["default", "persistent", "graph", "eager"], default="default",
+    ap.add_argument("--mode", choices=["default", "graph", "eager"], default="default",
                     help="step launch mode (default: the library's choice)")
     ap.add_argument("--synthetic-cache", action="store_true",
                     help="load a seeded random KV cache of the prompt's length instead of prefilling it "
@@ -378,7 +445,7 @@ def main():
     t = time.perf_counter()
     weights = make_weights(cfg, seed=wl.weight_seed, threads=16)
     log(f"[bench] weights generated in {time.perf_counter() - t:.1f}s")
-    modes = {"persistent": C.LF_MODE_PERSISTENT, "graph": C.LF_MODE_GRAPH, "eager": C.LF_MODE_EAGER}
+    modes = {"graph": C.LF_MODE_GRAPH, "eager": C.LF_MODE_EAGER}
     dec = Decoder(cfg, weights, mode=None if args.mode == "default" else modes[args.mode])
     mode_name = {v: k for k, v in modes.items()}[dec.mode]
     log(f"[bench] step launch mode: {mode_name}")
@@ -430,11 +497,26 @@ def main():
     prefill_s = time.perf_counter() - t
     log(f"[bench] {'synthetic cache' if args.synthetic_cache else 'prefill'} {P} positions in {prefill_s:.2f}s")
 
-    # warm-up, then rewind so the timed steps replay positions P .. P+K-1
-    if args.warmup:
-        seq.steps(args.warmup)
+    # the whole generation once, untimed, checked against the oracle's tokens
+    n_gen = cfg.max_ctx - P
+    seq.steps(n_gen)
     torch.cuda.synchronize()
-    seq.set_len(P)
+    check_status(seq, cfg.max_ctx, "untimed generation")
+    gen_tokens = seq.tokens(P, n_gen + 1).cpu().numpy()
+    gold = golden_tokens("ctx4096")
+    checked = compare_tokens(gen_tokens, gold, "ctx4096 generation")
+
+    # warm-up, then the timed region: the last K steps of the generation,
+    # positions start .. 4095, replayed from the same cache
+    start = cfg.max_ctx - K
+    done = 0
+    while done < args.warmup:
+        seq.set_len(start)
+        n = min(K, args.warmup - done)
+        seq.steps(n)
+        done += n
+    torch.cuda.synchronize()
+    seq.set_len(start)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
@@ -443,26 +525,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1)
+    check_timed(seq, cfg.max_ctx, gen_tokens, start - P, "timed region")
     tok_s = K / (ms / 1e3)
-    moved = sum(step_bytes(cfg, p) for p in range(P, P + K))
+    moved = sum(step_bytes(cfg, p) for p in range(start, cfg.max_ctx))
     gbs = moved / (ms / 1e3) / 1e9
     last_bytes = step_bytes(cfg, cfg.max_ctx - 1)
-    log(f"[bench] {K} steps: {ms:.2f} ms (wall {wall * 1e3:.2f} ms) -> {tok_s:.1f} tok/s, {gbs:.0f} GB/s")
+    log(f"[bench] {K} steps at positions {start}..{cfg.max_ctx - 1}: {ms:.2f} ms (wall {wall * 1e3:.2f} ms) -> "
+        f"{tok_s:.1f} tok/s, {gbs:.0f} GB/s; tokens and status checked")
 
     # four more runs of the same timed region (the reported value is the first)
     runs = [tok_s]
     for _ in range(4):
-        seq.set_len(P)
+        seq.set_len(start)
         torch.cuda.synchronize()
         e0.record()
         seq.steps(K)
         e1.record()
         torch.cuda.synchronize()
+        check_timed(seq, cfg.max_ctx, gen_tokens, start - P, "repeated timed region")
         runs.append(K / (e0.elapsed_time(e1) / 1e3))
     log("[bench] runs (tok/s): " + ", ".join(f"{r:.1f}" for r in runs))
 
-    # per-step latency: 64 device-fed steps, each between two events
-    seq.set_len(P)
+    # per-step latency: the last 64 device-fed steps, each between two events
+    seq.set_len(cfg.max_ctx - 64)
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(65)]
     evs[0].record()
@@ -470,6 +555,7 @@ def main():
         seq.step()
         evs[i + 1].record()
     torch.cuda.synchronize()
+    check_status(seq, cfg.max_ctx, "per-step latency")
     lat = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(64))
 
     # per-kernel timing: eager launches of one step (launch gaps included), and
@@ -504,6 +590,7 @@ def main():
         seq.step()
     e1.record()
     torch.cuda.synchronize()
+    check_status(seq, cfg.max_ctx, "fixed context 4096")
     fixed_ms = e0.elapsed_time(e1) / n_fixed
     fused = dec.fused
     sampled = sampled_rate(torch, C, dec, seq, P)
@@ -553,8 +640,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "ctx4096: 15-layer 2.3B-shaped decoder (d 4096, 32q/16kv heads x 128, 8 lanes, "
                                "SwiGLU 7168, vocab 32000, SWA 1024 on 10 layers), random fp16 weights, "
-                               f"{P}-token random prompt, greedy decode of positions {P}..{P + K - 1}, batch 1",
-                   "prompt": P, "decode_steps": K, "max_ctx": cfg.max_ctx},
+                               f"{P}-token random prompt, greedy decode to 4096 positions; timed: the last {K} "
+                               f"steps, positions {start}..{cfg.max_ctx - 1}, batch 1",
+                   "prompt": P, "decode_steps": K, "first_position": start, "last_position": cfg.max_ctx - 1,
+                   "max_ctx": cfg.max_ctx},
+        "checked": checked,
         "hbm_gbs": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step_avg": moved // K,
@@ -568,7 +658,7 @@ def main():
         "runs_tok_s": [round(r, 1) for r in runs],
         "median_tok_s": round(float(np.median(runs)), 1),
         "step_latency_ms": {"p50": round(lat[32], 4), "p90": round(lat[57], 4), "max": round(lat[-1], 4),
-                            "note": "64 device-fed steps at positions 3584..3647, one event pair per step"},
+                            "note": "64 device-fed steps at positions 4032..4095, one event pair per step"},
         "kernels_per_step": n_kernels,
         "qkv_attention_fused": bool(fused),
         "stream_read_ceiling_gbs": round(ceiling, 1),

@@ -94,6 +94,7 @@ __device__ __forceinline__ float wave_total(float v) {
 // Greedy key: larger logit wins, then the lower index; 0 is below every key.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
   unsigned u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0, as better() compares them
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<unsigned long long>(u) << 32) | static_cast<unsigned>(0x7fffffff - i);
 }
@@ -1062,10 +1063,12 @@ __global__ void k_fill_u32(unsigned* p, unsigned v, size_t n) {
 
 // Start a step with an explicit token, or set the length (d_token == null).
 // After a length change the greedy token of position len may be recorded as
-// token len+1 again (positions past len are discarded).
-__global__ void k_set_pos(int32_t* state, int32_t* tokens, int32_t len, const int32_t* d_token) {
+// token len+1 again (positions past len are discarded). abort (if not null):
+// the model's give-up flag, cleared.
+__global__ void k_set_pos(int32_t* state, int32_t* tokens, int32_t len, const int32_t* d_token, unsigned* abort) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   state[kLen] = len;
+  if (abort) *abort = 0u;
   if (d_token) {
     tokens[len] = *d_token;
     state[kFedEnd] = len + 1;

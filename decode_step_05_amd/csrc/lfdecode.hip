@@ -3,7 +3,6 @@
 // declared in include/lfdecode.h.
 #include "lfdecode.h"
 #include "lf_kernels.h"
-#include "lf_stream.h"
 #include "lf_prefill.h"
 #include "lf_sample.h"
 
@@ -76,12 +75,6 @@ int attn_loads_per_lane(int chunk, int head_dim) {
     if (u * per_load >= chunk) return u;
   return 16;
 }
-// The persistent step kernel runs one work item per workgroup: at most
-// nb / n_kv splits per kv head, of at least 32 keys each.
-AttnPlan step_attn_plan(const lf_config& c, int layer, int nb) {
-  const int visible = visible_keys(c, layer);
-  return split_plan(visible, std::min(nb / c.n_kv_heads, (visible + 31) / 32));
-}
 
 // Launch shape of a GEMV: (waves per workgroup, row groups per wave). Each
 // candidate is a compiled variant; the first that gives a balanced grid of at
@@ -146,37 +139,12 @@ Dims dims(const lf_config& c) {
 // Byte offsets of everything in the model workspace.
 struct WsLayout {
   std::vector<size_t> wqkv, wo, wgu, wd, g1, g2;
-  std::vector<size_t> sw;  // stream-order copies of the GEMV weights, per stream phase
-  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, best, counters, bar, attn_epochs, sphases, slayers, total;
-  // tagged exchange buffers of the attention kernel and of the stream step
-  // kernel (one zeroed region)
-  size_t attn_part, xt, qt, kvt, ot, actt, partt, fpart, qkvx, tagged_begin, tagged_end;
+  size_t embed = 0, lm = 0, gf = 0, rope, x, q, o, act, best, counters, abort, attn_epochs, total;
+  // tagged exchange buffers of the attention kernels (one zeroed region)
+  size_t attn_part, fpart, qkvx, tagged_begin, tagged_end;
   size_t class_epochs;  // QKV fused with attention: epoch per XCD class
   int S_max;
 };
-
-// The GEMV phases of the stream step kernel: per layer QKV, O, gate/up,
-// down; then the LM head. Rows are dealt to the launch's compute waves, rpw
-// each (the last ones padded with zero rows); a row is kch 1-KB slots.
-struct StreamPhaseShape {
-  int rows, K, kch, rpw;
-  size_t bytes() const { return static_cast<size_t>(rpw) * kch * lf::kSTW * 1024; }
-};
-
-std::vector<StreamPhaseShape> stream_shapes(const Dims& D) {
-  auto shape = [](int rows, int K) {
-    return StreamPhaseShape{rows, K, (K + 511) / 512, (rows + lf::kSTW - 1) / lf::kSTW};
-  };
-  std::vector<StreamPhaseShape> v;
-  for (int l = 0; l < D.L; ++l) {
-    v.push_back(shape(D.qkv_rows, D.d));
-    v.push_back(shape(D.d, D.qdim));
-    v.push_back(shape(2 * D.ffn, D.d));
-    v.push_back(shape(D.d, D.ffn));
-  }
-  if (D.V) v.push_back(shape(D.V, D.d));
-  return v;
-}
 
 WsLayout ws_layout(const lf_config& c) {
   const Dims D = dims(c);
@@ -205,25 +173,15 @@ WsLayout ws_layout(const lf_config& c) {
   W.S_max = kMaxSplits;
   W.best = take(sizeof(unsigned long long));
   W.counters = take((D.hkv + 4) * sizeof(unsigned));
-  W.bar = take(8 * sizeof(unsigned));
+  W.abort = take(sizeof(unsigned));  // raised when a wait between workgroups gives up
   W.attn_epochs = take(D.hkv * sizeof(unsigned));
   const size_t tw = sizeof(unsigned long long);
   W.tagged_begin = off;
   W.attn_part = take(static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2) * tw);
-  W.xt = take(D.d * tw);
-  W.qt = take(D.qdim * tw);
-  W.kvt = take(static_cast<size_t>(2) * D.hkv * D.hd * tw);
-  W.ot = take(D.qdim * tw);
-  W.actt = take(D.ffn * tw);
-  W.partt = take(static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2) * tw);
   W.fpart = take(static_cast<size_t>(D.hq) * kFusedSplits * (D.hd + 2) * tw);
   W.qkvx = take(static_cast<size_t>(D.qkv_rows) * tw);
   W.tagged_end = off;
   W.class_epochs = take(8 * sizeof(unsigned));
-  const std::vector<StreamPhaseShape> sp = stream_shapes(D);
-  for (const StreamPhaseShape& e : sp) W.sw.push_back(take(e.bytes()));
-  W.sphases = take(sp.size() * sizeof(lf::SPhase));
-  W.slayers = take(static_cast<size_t>(D.L) * sizeof(lf::SLayer));
   W.total = off;
   return W;
 }
@@ -268,9 +226,8 @@ struct lf_model {
   int mode = LF_MODE_GRAPH;
   bool xcd_classes = false;              // workgroups congruent modulo 8 share an XCD (probed at init)
   bool fused_ok = false;                 // QKV and attention can run as one kernel per layer
+  std::vector<char> attn_xcd;            // per layer: k_attn runs with the XCD layout
   bool fused = false;                    // ... and do
-  const void* step_fn = nullptr;         // stream step kernel for this shape (null: unavailable)
-  int step_lds = 0;                      // its LDS bytes per workgroup
   std::vector<GraphEntry> graphs;
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -370,30 +327,34 @@ int set_lds_limit_epi() {
   return LF_OK;
 }
 
+// The attention kernel variant for (head_dim, query heads per kv head, loads
+// per lane, layout). XCD layout: a one-dimensional grid of S * n_kv
+// workgroups in which the splits of a kv head are the workgroups congruent to
+// it modulo 8 (one XCD, exchanges through its L2); else a grid (S, n_kv).
 template <int HD, int G, bool XCD>
-void launch_attn_x(const lf::AttnXArgs& a, int n_kv, hipStream_t st) {
-  const dim3 grid = XCD ? dim3(a.t.S * n_kv) : dim3(a.t.S, n_kv), block(lf::kBlock);
-  switch (attn_loads_per_lane(a.t.chunk, HD)) {
-    case 4: hipLaunchKernelGGL((lf::k_attn<HD, G, 4, XCD>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((lf::k_attn<HD, G, 8, XCD>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((lf::k_attn<HD, G, 16, XCD>), grid, block, 0, st, a); break;
-  }
+const void* attn_fn_u(int u) {
+  return u == 4   ? reinterpret_cast<const void*>(&lf::k_attn<HD, G, 4, XCD>)
+         : u == 8 ? reinterpret_cast<const void*>(&lf::k_attn<HD, G, 8, XCD>)
+                  : reinterpret_cast<const void*>(&lf::k_attn<HD, G, 16, XCD>);
 }
-
-// The splits of each kv head exchange their states through one XCD's L2 when
-// the kv heads divide evenly over the 8 XCD classes of workgroups.
 template <int HD, int G>
-void launch_attn_t(const lf::AttnXArgs& a, int n_kv, bool xcd, hipStream_t st) {
-  if (xcd && n_kv % 8 == 0) return launch_attn_x<HD, G, true>(a, n_kv, st);
-  launch_attn_x<HD, G, false>(a, n_kv, st);
+const void* attn_fn_t(int u, bool xcd) {
+  return xcd ? attn_fn_u<HD, G, true>(u) : attn_fn_u<HD, G, false>(u);
 }
-
-void launch_attn(const lf::AttnXArgs& a, int hd, int G, int n_kv, bool xcd, hipStream_t st) {
-#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return launch_attn_t<H, GG>(a, n_kv, xcd, st);
+const void* attn_kernel(int hd, int G, int u, bool xcd) {
+#define LF_ATTN_CASE(H, GG) if (hd == H && G == GG) return attn_fn_t<H, GG>(u, xcd);
   LF_ATTN_CASE(32, 1) LF_ATTN_CASE(32, 2) LF_ATTN_CASE(32, 4)
   LF_ATTN_CASE(64, 1) LF_ATTN_CASE(64, 2) LF_ATTN_CASE(64, 4)
   LF_ATTN_CASE(128, 1) LF_ATTN_CASE(128, 2) LF_ATTN_CASE(128, 4)
 #undef LF_ATTN_CASE
+  return nullptr;
+}
+
+void launch_attn(const lf::AttnXArgs& a, int hd, int G, int n_kv, bool xcd, hipStream_t st) {
+  const dim3 grid = xcd ? dim3(a.t.S * n_kv) : dim3(a.t.S, n_kv);
+  void* args[] = {const_cast<lf::AttnXArgs*>(&a)};
+  (void)hipLaunchKernel(attn_kernel(hd, G, attn_loads_per_lane(a.t.chunk, hd), xcd), grid, dim3(lf::kBlock), args, 0,
+                        st);
 }
 
 // QKV fused with attention (k_qkv_attn): the decoder shape of 16 kv heads of
@@ -441,54 +402,67 @@ void launch_qkv_attn(const lf::QkvAttnArgs& a, hipStream_t st) {
   (void)hipLaunchKernel(qkv_attn_kernel(ukv, a.g.in_kind), dim3(256), dim3(8 * lf::kWave), args, 0, st);
 }
 
+// Which attention launches a device can run. Workgroups that wait on each
+// other must all be resident at once: a wait on a workgroup that has not been
+// dispatched ends only by giving up (the abort flag), so a plan is chosen
+// from the device's room for each kernel (workgroups per CU x CUs):
+//  * QKV fused with attention: one launch of 16 kv heads x 16 splits = 256
+//    workgroups that wait on their XCD class: needs the fused shape, the XCD
+//    dealing, room for all 256 at once and every split's keys in LDS;
+//  * k_attn with the XCD layout: the splits of a kv head are spread over the
+//    whole grid, so all S * n_kv workgroups must fit at once;
+//  * k_attn with the two-dimensional grid: the S splits of a kv head are
+//    consecutive workgroups, dispatched in order, so S of them must fit; a
+//    configuration that cannot is rejected.
+int plan_attention(const lf_config& c, int n_cu, int attn_per_cu, int fused_per_cu, bool xcd, bool& fused_ok,
+                   std::vector<char>& xcd_layer) {
+  const Dims D = dims(c);
+  fused_ok = xcd && fused_shape(D) && static_cast<long>(fused_per_cu) * n_cu >= D.hkv * kFusedSplits;
+  for (int l = 0; l < D.L && fused_ok; ++l) fused_ok = fused_ukv(fused_plan(c, l).chunk) > 0;
+  const long room = static_cast<long>(attn_per_cu) * n_cu;
+  xcd_layer.assign(D.L, 0);
+  for (int l = 0; l < D.L; ++l) {
+    const AttnPlan P = attn_plan(c, l);
+    if (P.S > room)
+      return fail(LF_EINVAL, "layer %d: %d attention splits cannot be resident at once (room for %ld)", l, P.S, room);
+    xcd_layer[l] = xcd && D.hkv % 8 == 0 && static_cast<long>(P.S) * D.hkv <= room;
+  }
+  return LF_OK;
+}
+
+// Workgroups per CU the device holds of the attention kernels this model
+// launches (the smallest over its layers and both layouts), and of its QKV
+// fused with attention kernels (0 if the shape has none).
+int attention_room(const lf_config& c, int& attn_per_cu, int& fused_per_cu) {
+  const Dims D = dims(c);
+  attn_per_cu = 1 << 20;
+  fused_per_cu = 0;
+  for (int l = 0; l < D.L; ++l) {
+    const int u = attn_loads_per_lane(attn_plan(c, l).chunk, D.hd);
+    for (bool x : {false, true}) {
+      int n = 0;
+      LF_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_kernel(D.hd, D.G, u, x), lf::kBlock, 0));
+      attn_per_cu = std::min(attn_per_cu, n);
+    }
+  }
+  if (!fused_shape(D)) return LF_OK;
+  fused_per_cu = 1 << 20;
+  for (int l = 0; l < D.L; ++l) {
+    const int ukv = fused_ukv(fused_plan(c, l).chunk);
+    if (ukv == 0) return fused_per_cu = 0, LF_OK;
+    int n = 0;
+    const int in = (l == 0 && D.V) ? lf::kInNormEmbed : lf::kInNormF32;
+    LF_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, qkv_attn_kernel(ukv, in), 8 * lf::kWave, 0));
+    fused_per_cu = std::min(fused_per_cu, n);
+  }
+  return LF_OK;
+}
+
 int set_lds_limits() {
   int rc;
   if ((rc = set_lds_limit_epi<lf::kEpiQKV>()) || (rc = set_lds_limit_epi<lf::kEpiSwiGLU>()) ||
       (rc = set_lds_limit_epi<lf::kEpiResid>()) || (rc = set_lds_limit_epi<lf::kEpiLogits>()))
     return rc;
-  return LF_OK;
-}
-
-// Stream step kernels compiled for the shapes in use: (head_dim, query heads
-// per kv head). Other shapes run the per-phase kernels.
-struct StepVariant {
-  int hd, G, lds;
-  const void* fn;
-};
-#define LF_STEP(HD, G) {HD, G, lf::stream_lds_bytes<HD, G>(), reinterpret_cast<const void*>(&lf::k_stream<HD, G>)}
-const StepVariant kStepVariants[] = {LF_STEP(128, 2), LF_STEP(64, 2), LF_STEP(32, 2), LF_STEP(128, 4)};
-#undef LF_STEP
-
-const StepVariant* find_step_kernel(const Dims& D) {
-  for (const StepVariant& v : kStepVariants)
-    if (v.hd == D.hd && v.G == D.G) return &v;
-  return nullptr;
-}
-
-int launch_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
-  const Dims& D = m->D;
-  const WsLayout& W = m->W;
-  lf::StreamArgs a{};
-  a.ph = m->at<lf::SPhase>(W.sphases);
-  a.layers = m->at<lf::SLayer>(W.slayers);
-  a.n_ph = static_cast<int>(W.sw.size());
-  a.L = D.L; a.d = D.d; a.qdim = D.qdim; a.ffn = D.ffn; a.vocab = D.V; a.hd = D.hd;
-  a.qpl = D.qpl; a.kpl = D.kpl; a.n_kv = D.hkv; a.max_ctx = D.ctx; a.S_max = W.S_max;
-  a.eps = m->cfg.rms_eps;
-  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
-  a.embed = D.V ? m->at<half_t>(W.embed) : nullptr;
-  a.gf = D.V ? m->at<half_t>(W.gf) : nullptr;
-  a.rope = m->at<float2>(W.rope);
-  a.xt = m->at<lf::u64>(W.xt); a.qt = m->at<lf::u64>(W.qt); a.kvt = m->at<lf::u64>(W.kvt);
-  a.ot = m->at<lf::u64>(W.ot); a.actt = m->at<lf::u64>(W.actt); a.partt = m->at<lf::u64>(W.partt);
-  a.best = m->at<unsigned long long>(W.best);
-  a.bar = m->at<unsigned>(W.bar);
-  a.state = kv->state(); a.tokens = kv->tokens(); a.logits = kv->logits();
-  a.kc = kv->kc(); a.vc = kv->vc();
-  a.layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
-  a.x_in = xin; a.x_out = xout;
-  void* args[] = {&a};
-  LF_HIP(hipLaunchCooperativeKernel(m->step_fn, dim3(lf::kSGrid), dim3(lf::kSThreads), args, m->step_lds, st));
   return LF_OK;
 }
 
@@ -586,7 +560,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
     t.part = m->at<lf::u64>(W.attn_part);
     t.o = m->at<float>(W.o);
     t.epochs = m->at<unsigned>(W.attn_epochs);
-    t.abort = m->at<unsigned>(W.bar) + 2;
+    t.abort = m->at<unsigned>(W.abort);
     t.S_max = W.S_max;
     t.n_kv = D.hkv;
     if (m->fused) {
@@ -600,7 +574,7 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
       emit_kernel(tm, st, LF_KERNEL_QKV_ATTN, l, [&] { launch_qkv_attn(f, st); });
     } else {
       emit_kernel(tm, st, LF_KERNEL_QKV, l, [&] { launch_gemv<lf::kEpiQKV>(a, st); });
-      emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, m->xcd_classes, st); });
+      emit_kernel(tm, st, LF_KERNEL_ATTN, l, [&] { launch_attn(t, D.hd, D.G, D.hkv, m->attn_xcd[l] != 0, st); });
     }
 
     // O projection + residual
@@ -655,7 +629,6 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
 }
 
 int run_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
-  if (m->mode == LF_MODE_PERSISTENT) return launch_step(m, kv, xin, xout, st);
   if (m->mode == LF_MODE_EAGER) return enqueue_step(m, kv, xin, xout, st);
   hipGraphExec_t exec = nullptr;
   for (const GraphEntry& g : m->graphs)
@@ -882,71 +855,39 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   const int nctr = D.hkv + 4;
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.counters), 0u, size_t(nctr));
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.best), 0u, size_t(2));
-  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar), 0u, size_t(8));
-  // stream kernel: tags start at zero, the launch epoch at 1 (tags of epoch e are >= 512 e)
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.abort), 0u, size_t(1));
+  // tagged exchange words start with tag 0 (no epoch is 0)
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(256), dim3(256), 0, st, m->at<unsigned>(W.tagged_begin), 0u,
                      (W.tagged_end - W.tagged_begin) / sizeof(unsigned));
-  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bar) + 3, 1u, size_t(1));
   // attention: split states are tagged with the kv head's epoch, which starts at 1
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.attn_epochs), 1u, size_t(D.hkv));
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.class_epochs), 1u, size_t(8));
-  // Stream-order copies of the repacked GEMV weights, and the tables of the
-  // stream step kernel (the host copies live until the stream is
-  // synchronized below).
-  const std::vector<StreamPhaseShape> sp = stream_shapes(D);
-  std::vector<lf::SPhase> phases(sp.size());
-  for (size_t i = 0; i < sp.size(); ++i) {
-    const int l = static_cast<int>(i / 4), kind = static_cast<int>(i % 4);
-    const size_t src_off = static_cast<int>(i) == 4 * D.L ? W.lm
-                           : kind == 0                     ? W.wqkv[l]
-                           : kind == 1                     ? W.wo[l]
-                           : kind == 2                     ? W.wgu[l]
-                                                           : W.wd[l];
-    lf::u32x4* dst = m->at<lf::u32x4>(W.sw[i]);
-    hipLaunchKernelGGL(lf::k_stream_repack, dim3(4096), dim3(256), 0, st, m->at<half_t>(src_off), sp[i].rows, sp[i].K,
-                       sp[i].kch, sp[i].rpw, dst, sp[i].bytes() / 16);
-    phases[i] = {dst, sp[i].rows, sp[i].K, sp[i].kch, sp[i].rpw};
-  }
-  std::vector<lf::SLayer> slayers(D.L);
-  for (int l = 0; l < D.L; ++l) {
-    const AttnPlan P = step_attn_plan(*cfg, l, lf::kSGrid);
-    slayers[l] = {m->at<half_t>(W.g1[l]), m->at<half_t>(W.g2[l]), cfg->window[l], P.S, P.chunk};
-  }
-  if (hipMemcpyAsync(m->at<lf::SPhase>(W.sphases), phases.data(), phases.size() * sizeof(lf::SPhase),
-                     hipMemcpyHostToDevice, st) ||
-      hipMemcpyAsync(m->at<lf::SLayer>(W.slayers), slayers.data(), slayers.size() * sizeof(lf::SLayer),
-                     hipMemcpyHostToDevice, st))
-    return bail(fail(LF_EHIP, "stream table upload failed: %s", hipGetErrorString(hipGetLastError())));
-  // The stream step kernel needs cooperative launch and kSGrid co-resident
-  // workgroups. Graph replay stays the default until it is measured faster.
-  {
-    const StepVariant* v = find_step_kernel(D);
-    bool fits = v != nullptr;
-    for (const StreamPhaseShape& e : sp) fits = fits && lf::kSW * e.rpw <= lf::kSResMax && e.K <= lf::kSKMax;
-    int dev = 0, coop = 0, ncu = 0, per_cu = 0;
-    if (fits && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, v->lds) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, lf::kSThreads, v->lds) == hipSuccess &&
-        per_cu * ncu >= lf::kSGrid) {
-      m->step_fn = v->fn;
-      m->step_lds = v->lds;
-    }
-    (void)hipGetLastError();
-  }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
   if ((rc = probe_xcd_classes(m, st))) return bail(rc);
-  int dev = 0, ncu = 0;
-  const bool cus = hipGetDevice(&dev) == hipSuccess &&
-                   hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu >= 256;
-  (void)hipGetLastError();
-  m->fused_ok = m->xcd_classes && cus && fused_shape(D);  // its 256 workgroups wait for each other: one per CU
-  for (int l = 0; l < D.L && m->fused_ok; ++l) m->fused_ok = fused_ukv(fused_plan(*cfg, l).chunk) > 0;
+  int dev = 0, ncu = 0, attn_per_cu = 0, fused_per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return bail(fail(LF_EHIP, "device query: %s", hipGetErrorString(hipGetLastError())));
+  if ((rc = attention_room(*cfg, attn_per_cu, fused_per_cu))) return bail(rc);
+  if ((rc = plan_attention(*cfg, ncu, attn_per_cu, fused_per_cu, m->xcd_classes, m->fused_ok, m->attn_xcd)))
+    return bail(rc);
   m->fused = m->fused_ok;
   *out = m;
+  return LF_OK;
+}
+
+int lf_plan_attention(const lf_config* cfg, int32_t n_cu, int32_t attn_wg_per_cu, int32_t fused_wg_per_cu,
+                      int32_t xcd_classes, int32_t* fused, int32_t* xcd_layers) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!fused || !xcd_layers) return fail(LF_EINVAL, "null argument");
+  if (n_cu < 1 || attn_wg_per_cu < 0 || fused_wg_per_cu < 0) return fail(LF_EINVAL, "need n_cu >= 1 and rooms >= 0");
+  bool f = false;
+  std::vector<char> x;
+  if ((rc = plan_attention(*cfg, n_cu, attn_wg_per_cu, fused_wg_per_cu, xcd_classes != 0, f, x))) return rc;
+  *fused = f ? 1 : 0;
+  for (int l = 0; l < cfg->n_layers; ++l) xcd_layers[l] = x[l];
   return LF_OK;
 }
 
@@ -969,10 +910,7 @@ int lf_model_set_graph(lf_model* m, int enabled) {
 
 int lf_model_set_mode(lf_model* m, int mode) {
   if (!m) return fail(LF_EINVAL, "model is null");
-  if (mode != LF_MODE_EAGER && mode != LF_MODE_GRAPH && mode != LF_MODE_PERSISTENT)
-    return fail(LF_EINVAL, "unknown mode %d", mode);
-  if (mode == LF_MODE_PERSISTENT && !m->step_fn)
-    return fail(LF_EINVAL, "no persistent step kernel for this shape or device");
+  if (mode != LF_MODE_EAGER && mode != LF_MODE_GRAPH) return fail(LF_EINVAL, "unknown mode %d", mode);
   m->mode = mode;
   return LF_OK;
 }
@@ -1046,7 +984,7 @@ int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream) {
   if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");
   if (len < 0 || len > kv->m->D.ctx) return fail(LF_ERANGE, "length %d out of [0, %d]", len, kv->m->D.ctx);
   hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->state(), kv->tokens(), len,
-                     static_cast<const int32_t*>(nullptr));
+                     static_cast<const int32_t*>(nullptr), kv->m->at<unsigned>(kv->m->W.abort));
   LF_HIP(hipPeekAtLastError());
   kv->len = len;
   return LF_OK;
@@ -1132,7 +1070,8 @@ int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream)
   if (!d_token && kv->len == 0) return fail(LF_EINVAL, "no previous position to take a greedy token from");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d_token) {
-    hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, st, kv->state(), kv->tokens(), kv->len, d_token);
+    hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, st, kv->state(), kv->tokens(), kv->len, d_token,
+                       static_cast<unsigned*>(nullptr));
     LF_HIP(hipPeekAtLastError());
   }
   const int rc = run_step(m, kv, nullptr, nullptr, st);
@@ -1179,14 +1118,14 @@ int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream) {
   if (!kv || !out) return fail(LF_EINVAL, "null argument");
   if (!kv->m) return fail(LF_EINVAL, "the sequence's model was freed");
   int32_t s[4];
-  unsigned bar[4];
+  unsigned abort_flag = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   LF_HIP(hipMemcpyAsync(s, kv->state(), sizeof s, hipMemcpyDeviceToHost, st));
-  LF_HIP(hipMemcpyAsync(bar, kv->m->at<unsigned>(kv->m->W.bar), sizeof bar, hipMemcpyDeviceToHost, st));
+  LF_HIP(hipMemcpyAsync(&abort_flag, kv->m->at<unsigned>(kv->m->W.abort), sizeof abort_flag, hipMemcpyDeviceToHost, st));
   LF_HIP(hipStreamSynchronize(st));
   out[0] = s[lf::kLen];
   out[1] = s[lf::kArgmax];
-  out[2] = (s[lf::kBadToken] ? 1 : 0) | (bar[2] ? 2 : 0);
+  out[2] = (s[lf::kBadToken] ? 1 : 0) | (abort_flag ? 2 : 0);
   return LF_OK;
 }
 
@@ -1207,7 +1146,8 @@ int lf_step_kernel_times(lf_model* m, lf_kv* kv, const int32_t* d_token, const f
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d_token) {
-    hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, st, kv->state(), kv->tokens(), kv->len, d_token);
+    hipLaunchKernelGGL(lf::k_set_pos, dim3(1), dim3(64), 0, st, kv->state(), kv->tokens(), kv->len, d_token,
+                       static_cast<unsigned*>(nullptr));
     LF_HIP(hipPeekAtLastError());
   }
   StepTimer tm{m->events.data(), kinds, cap, 0};
@@ -1224,8 +1164,8 @@ int lf_sample(const float* d_logits, int32_t rows, int32_t n, float temperature,
               void* stream) {
   if (!d_logits || !d_u || !d_tokens) return fail(LF_EINVAL, "null argument");
   if (rows < 1 || n < 1 || n > (1 << 24)) return fail(LF_EINVAL, "need rows >= 1 and 1 <= n <= 2^24");
-  if (!(temperature > 0.f) || !std::isfinite(temperature))
-    return fail(LF_EINVAL, "temperature must be positive and finite");
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.f / temperature))
+    return fail(LF_EINVAL, "temperature must be positive and finite, with a finite reciprocal");
   const bool staged = lf::sample_fits_lds(n);
   const size_t lds = staged ? sizeof(float) * (lf::sample_slot(n - 1) + 1) : 0;
   // the kernel's LDS limit is raised once per device (two threads racing here set the same value)

@@ -15,12 +15,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblfdecode
 MAX_LAYERS = 64
 
 LF_OK, LF_EINVAL, LF_ERANGE, LF_EHIP = 0, -1, -2, -3
-LF_MODE_EAGER, LF_MODE_GRAPH, LF_MODE_PERSISTENT = 0, 1, 2
+LF_MODE_EAGER, LF_MODE_GRAPH = 0, 1
 
 # Every symbol include/lfdecode.h declares.
 EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
-    "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused",
+    "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused", "lf_plan_attention",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_prefill_workspace_bytes", "lf_prefill_batched",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
@@ -70,6 +70,8 @@ def load():
         "lf_model_mode": (c_int, [P]),
         "lf_model_set_fused": (c_int, [P, c_int]),
         "lf_model_fused": (c_int, [P]),
+        "lf_plan_attention": (c_int, [POINTER(lf_config), c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
+                                      POINTER(c_int32)]),
         "lf_kv_alloc": (c_int, [P, P, c_size_t, POINTER(P)]),
         "lf_kv_free": (None, [P]),
         "lf_kv_cache_ptrs": (c_int, [P, POINTER(P), POINTER(P)]),
@@ -199,6 +201,15 @@ def lf_model_set_fused(model, enabled: bool) -> None:
 
 def lf_model_fused(model) -> bool:
     return load().lf_model_fused(model) == 1
+
+
+def lf_plan_attention(cfg: lf_config, n_cu: int, attn_wg_per_cu: int, fused_wg_per_cu: int, xcd_classes: bool):
+    """(fused, [xcd layout per layer]) that lf_model_init would choose (host only)."""
+    fused = c_int32()
+    layers = (c_int32 * cfg.n_layers)()
+    _check(load().lf_plan_attention(ctypes.byref(cfg), int(n_cu), int(attn_wg_per_cu), int(fused_wg_per_cu),
+                                    int(bool(xcd_classes)), ctypes.byref(fused), layers))
+    return bool(fused.value), [bool(v) for v in layers]
 
 
 def lf_kv_alloc(model, buf):

@@ -52,7 +52,7 @@ extern "C" {
  * Decoder shape. All sizes in elements.
  *   n_q_heads % n_kv_heads == 0; n_q_heads, n_kv_heads and ffn divisible by n_lanes;
  *   head_dim in {32, 64, 128}; (512 / head_dim) divisible by n_kv_heads / n_lanes;
- *   d_model, ffn multiples of 8 and at most 16384; n_q_heads * head_dim at most 16384;
+ *   d_model, ffn multiples of 8 and at most 8192; n_q_heads * head_dim at most 8192;
  *   1 <= max_ctx <= 4096; 1 <= n_layers <= LF_MAX_LAYERS.
  * vocab == 0 selects hidden-in / hidden-out mode: no embedding, no LM head,
  * lf_decode_step_hidden is the step call.
@@ -95,8 +95,8 @@ typedef struct lf_model lf_model;
 typedef struct lf_kv lf_kv;
 
 /* Bytes of device workspace a model of this shape needs (0 if the config is
- * invalid): the weights twice (row-major for the per-phase kernels, stream
- * order for the persistent kernel) plus activations and exchange buffers. */
+ * invalid): the weights once (repacked, row-major), the rotary table, the
+ * activations and the exchange buffers of the attention kernels. */
 size_t lf_workspace_bytes(const lf_config* cfg);
 
 /* Bytes of the per-sequence device buffer (state, token history, logits, K and V caches). */
@@ -105,7 +105,13 @@ size_t lf_kv_bytes(const lf_config* cfg);
 /*
  * Validate cfg, bind the caller's workspace (d_workspace, >= lf_workspace_bytes,
  * 256-byte aligned), copy and repack the weights into it, build the rotary
- * table, and wait for that setup on `stream`. *out receives the handle.
+ * table, and wait for that setup on `stream` (the stream argument is an
+ * addition to the four calls of the path: the setup copies run on it). It
+ * also reads which XCD each workgroup of three probe launches runs on, and
+ * the device's room for the attention kernels, to choose their layouts
+ * (lf_plan_attention). *out receives the handle.
+ * LF_EINVAL for a bad config, null or misaligned pointers, a small workspace,
+ * or a shape whose attention splits cannot all be resident at once.
  */
 int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspace, size_t ws_bytes,
                   void* stream, lf_model** out);
@@ -115,23 +121,16 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
 void lf_model_free(lf_model* m);
 
 /*
- * How a step is launched. All modes compute the same function.
- *   LF_MODE_PERSISTENT: one cooperative launch of 256 workgroups per step;
- *     the workgroups run the phases (QKV, attention, O, gate/up, down, LM
- *     head) streaming every weight through LDS, and pass data between phases
- *     as tagged words instead of grid barriers. Available when the shape has
- *     a compiled step kernel and the device can hold 256 such workgroups at
- *     once (MI355X: one per compute unit). The workspace holds a second,
- *     stream-ordered copy of the weights for it.
+ * How a step is launched. Both modes compute the same function with the same
+ * kernels (bitwise the same results).
  *   LF_MODE_GRAPH (default): one kernel per phase, captured per (sequence,
  *     in/out pointers) into a hipGraph on first use and replayed.
  *   LF_MODE_EAGER: one kernel per phase, launched one by one.
- * lf_model_set_mode returns LF_EINVAL for a mode the model cannot run.
+ * lf_model_set_mode returns LF_EINVAL for any other value.
  * lf_model_set_graph(m, 1/0) selects LF_MODE_GRAPH / LF_MODE_EAGER.
  */
 #define LF_MODE_EAGER 0
 #define LF_MODE_GRAPH 1
-#define LF_MODE_PERSISTENT 2
 int lf_model_set_mode(lf_model* m, int mode);
 int lf_model_mode(const lf_model* m);
 int lf_model_set_graph(lf_model* m, int enabled);
@@ -153,8 +152,34 @@ int lf_model_set_fused(lf_model* m, int enabled);
 int lf_model_fused(const lf_model* m);
 
 /*
+ * Launch planning of the attention kernels (host only, no device work): what
+ * lf_model_init chooses for a device with n_cu compute units that holds
+ * attn_wg_per_cu workgroups of the split-KV attention kernel and
+ * fused_wg_per_cu of the QKV fused with attention kernel per CU at once, and
+ * deals a launch's workgroups to its 8 XCDs in turn if xcd_classes != 0.
+ * The splits of a kv head wait for each other's partial softmax states, so
+ * every layout is used only where all the workgroups that wait on each other
+ * can be resident at once:
+ *   *fused = 1 if QKV and attention can run as one launch (the fused shape,
+ *     xcd_classes, and room for its 256 workgroups);
+ *   xcd_layers[l] = 1 (host array of n_layers) if layer l's attention launch
+ *     keeps each kv head's splits on one XCD (room for all S * n_kv
+ *     workgroups, n_kv a multiple of 8), else 0 (a grid of S x n_kv in
+ *     which each kv head's S splits are consecutive).
+ * LF_EINVAL for a bad config, null pointers, n_cu < 1, negative rooms, or a
+ * layer whose S splits do not fit at once.
+ */
+int lf_plan_attention(const lf_config* cfg, int32_t n_cu, int32_t attn_wg_per_cu, int32_t fused_wg_per_cu,
+                      int32_t xcd_classes, int32_t* fused, int32_t* xcd_layers);
+
+/*
  * Bind a caller buffer (>= lf_kv_bytes, 256-byte aligned) as one sequence with
- * length 0. Layout of the caches, so a caller can fill them (K holds keys
+ * length 0: the KV cache that every generated token reads (blog, "Designing
+ * the architecture": with grouped-query and sliding-window attention the
+ * cache is what each new token streams besides the weights), for at most
+ * max_ctx <= 4096 positions (asector.ru summary, "Operational risks": a
+ * context of 4,096 tokens). Zeroes the sequence state (synchronously).
+ * Layout of the caches, so a caller can fill them (K holds keys
  * after the rotary embedding):
  *   K[layer][lane][pos][kv_head_in_lane][head_dim] fp16, V likewise,
  * kv head h lives in lane h / (n_kv_heads / n_lanes). lf_kv_cache_ptrs gives
@@ -168,7 +193,10 @@ int lf_kv_cache_ptrs(const lf_kv* kv, void** d_k, void** d_v);
  * Set the sequence length to len (0 <= len <= max_ctx): rewinds, or adopts
  * cache content the caller wrote for positions [0, len). Token len of the
  * history is kept as the input of the next step; greedy tokens of the
- * following steps are recorded from token len+1 on. Enqueued on stream.
+ * following steps are recorded from token len+1 on. Also clears the model's
+ * give-up flag (lf_kv_status bit 1). Enqueued on stream (an argument beyond
+ * the path's four calls: the caller orders it with its own work).
+ * LF_ERANGE if len is outside [0, max_ctx].
  */
 int lf_kv_set_len(lf_kv* kv, int32_t len, void* stream);
 int32_t lf_kv_len(const lf_kv* kv);
@@ -183,10 +211,14 @@ int32_t lf_kv_len(const lf_kv* kv);
 int lf_kv_tokens(const lf_kv* kv, int32_t* d_out, int32_t start, int32_t n, void* stream);
 
 /*
- * Append n positions whose token ids are d_tokens[0..n) (device int32, each in
- * [0, vocab); ids outside are clamped and flagged, see lf_kv_status). Leaves
- * the logits and greedy argmax of the last of them. LF_ERANGE if
- * len + n > max_ctx. Token mode only (vocab > 0).
+ * Prefill: append n positions whose token ids are d_tokens[0..n) (device
+ * int32, each in [0, vocab); ids outside are clamped and flagged, see
+ * lf_kv_status), one decode step per position, so the prompt's keys and
+ * values enter the cache exactly as generated tokens' do (blog, "Designing
+ * the architecture"). Leaves the logits and greedy argmax of the last of
+ * them. LF_EINVAL for null arguments, n < 1 or vocab == 0; LF_ERANGE if
+ * len + n > max_ctx (asector.ru summary, "Operational risks": 4,096-token
+ * context). Enqueued on stream.
  */
 int lf_prefill(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, void* stream);
 
@@ -221,9 +253,16 @@ int lf_prefill_batched(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t 
                        size_t ws_bytes, void* stream);
 
 /*
- * Append one position. d_token (device int32) gives its token id; NULL feeds
- * the greedy argmax of the previous position, which stays on the device.
- * Leaves the logits and argmax of the new position. LF_ERANGE if len == max_ctx.
+ * The decode step: append one position. Every weight of the model is read
+ * once plus the cache keys each layer sees, which is what bounds its speed
+ * at batch 1 (blog, "The idea" and "Designing the architecture"); FP16
+ * weights and cache at batch 1 (asector.ru summary, "Performance and
+ * infrastructure"). d_token (device int32) gives its token id; NULL feeds
+ * the greedy argmax of the previous position (blog, TL;DR: greedy decoding),
+ * which stays on the device. Leaves the logits and argmax of the new
+ * position. LF_EINVAL for null handles, vocab == 0, or d_token NULL at
+ * length 0; LF_ERANGE if len == max_ctx. Enqueued on stream (graph replay or
+ * eager launches, per lf_model_set_mode).
  */
 int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream);
 
@@ -239,17 +278,22 @@ int lf_decode_step_hidden(lf_model* m, lf_kv* kv, const float* d_x_in, float* d_
 
 /*
  * Copy the logits of the most recent position (fp32 [vocab]) to d_logits and,
- * if d_argmax is not NULL, its greedy token (lowest index among maximal
- * logits) to d_argmax (device int32). Token mode only.
+ * if d_argmax is not NULL, its greedy token (blog, TL;DR: greedy decoding;
+ * the lowest index among maximal logits, +0.0 and -0.0 equal) to d_argmax
+ * (device int32). Both buffers caller-owned. LF_EINVAL for null arguments,
+ * vocab == 0 or an empty sequence. Enqueued on stream.
  */
 int lf_logits(const lf_model* m, const lf_kv* kv, float* d_logits, int32_t* d_argmax, void* stream);
 
 /*
  * Read back (synchronously on stream) the device-side sequence state:
  * out[0] = length, out[1] = last argmax, out[2] = flags: bit 0 set if a token
- * id outside [0, vocab) was clamped since lf_kv_alloc; bit 1 set if a
- * persistent step gave up waiting for another workgroup's data (its results
- * are invalid and later persistent steps of the model do nothing).
+ * id outside [0, vocab) was clamped since lf_kv_alloc; bit 1 set if, in a
+ * step of this model (any of its sequences) since lf_model_init or the last
+ * lf_kv_set_len on one of its sequences, an attention workgroup gave up
+ * waiting for another workgroup's data (a bounded poll ran out). The results
+ * of those steps are invalid, and until the flag is cleared every later wait
+ * gives up at once.
  */
 int lf_kv_status(const lf_kv* kv, int32_t out[3], void* stream);
 
@@ -322,8 +366,8 @@ int lf_read_bandwidth(const void* d_buf, size_t bytes, int32_t iters, void* d_si
  * three are caller-owned; nothing is allocated. Asynchronous on `stream`; to
  * continue a sequence with the drawn token pass d_tokens + r to lf_decode_step.
  * LF_EINVAL for null pointers, rows < 1, n < 1 or n > 2^24, or a temperature
- * that is not positive and finite (greedy decoding is lf_decode_step's own
- * argmax); LF_EHIP if the launch fails.
+ * that is not positive and finite or whose reciprocal is not finite (greedy
+ * decoding is lf_decode_step's own argmax); LF_EHIP if the launch fails.
  */
 int lf_sample(const float* d_logits, int32_t rows, int32_t n, float temperature, const float* d_u, int32_t* d_tokens,
               void* stream);

@@ -6,7 +6,8 @@ tokens without re-running a float64 model of 2.3B parameters:
   * the oracle's greedy token (decided on float32-rounded logits),
   * the gap between its two largest logits (for the near-tie rule),
   * the logits at the 8 largest indices and at 128 fixed sampled indices,
-  * the full logits vector at three positions (first, middle, last).
+  * the full logits vector at every 16th position (0, 16, ..., 512), so that
+    whole 32000-wide vectors are compared along each generation.
 
 Workloads: ctx1024 (512-token prompt, 512 greedy steps) and ctx4096
 (3584-token prompt, 512 greedy steps) of the 15-layer decoder.
@@ -28,6 +29,7 @@ from synth import WORKLOADS, make_prompt, make_weights  # noqa: E402
 
 N_TOP = 8
 N_SAMPLE = 128
+FULL_EVERY = 16
 
 
 def sample_indices(vocab, seed=7):
@@ -51,7 +53,7 @@ def run(name):
     top_i = np.zeros((n, N_TOP), np.int32)
     top_v = np.zeros((n, N_TOP), np.float64)
     samp = np.zeros((n, N_SAMPLE), np.float64)
-    full_at = np.array([0, n // 2, n - 1], np.int32)
+    full_at = np.arange(0, n, FULL_EVERY, dtype=np.int32)
     full = np.zeros((len(full_at), cfg.vocab), np.float32)
     for s in range(n):
         if s:

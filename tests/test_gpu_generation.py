@@ -3,14 +3,19 @@
 The float64 oracle runs of the two generation workloads (512-token prompt +
 512 greedy steps, and 3584-token prompt + 512 steps up to context 4096) take
 minutes of CPU time, so tests/golden/make_golden.py stored, per compared
-position, the oracle's greedy token, its top-2 gap, its 8 largest logits,
-128 sampled logits and three full logit vectors. This test regenerates the
-same seeded inputs, runs the HIP path through the C ABI, and compares:
+position, the oracle's greedy token, its top-2 gap, its 8 largest logits and
+128 sampled logits, and the full 32000-wide logit vector at every 16th
+position. This test regenerates the same seeded inputs, runs the HIP path
+through the C ABI, and compares:
   * per position: the stored logits within the tolerances of parity.py;
+  * at every 16th position: all 32000 logits within the same tolerances;
   * per position: the device's greedy token equals the oracle's, or the oracle's
     top-2 gap is within twice the position's max |delta| (near-tie);
   * the device-fed free-running chain reproduces the oracle's tokens up to the
-    first near-tie (there is none in these runs, so: all 513 tokens).
+    first near-tie (there is none in these runs, so: all 513 tokens), and no
+    wait between workgroups gave up on the way (status flags clear).
+A second test runs the float64 oracle itself beside the GPU for the last 32
+positions of the 4096-token context and compares every step's full vector.
 """
 import os
 
@@ -87,9 +92,60 @@ def test_generation_matches_stored_oracle(name):
     # free-running greedy chain on the device (the timed path of the benchmark)
     seq.set_len(wl.prompt_len)
     seq.steps(wl.steps)
-    assert seq.status()[0] == wl.prompt_len + wl.steps
+    st = seq.status()
+    assert st[0] == wl.prompt_len + wl.steps and st[2] == 0, st
     free = seq.tokens(wl.prompt_len, wl.steps + 1).cpu().numpy()
     first_tie = next((s for s in range(wl.steps + 1) if got_a[s] != toks[s]), None)
     upto = wl.steps + 1 if first_tie is None else first_tie
     assert np.array_equal(free[:upto], toks[:upto]), "free-running chain diverged from the oracle's tokens"
     say(f"[generation] {name}: free-running chain matches the oracle's {upto} tokens")
+
+
+@pytest.mark.timeout(600)
+def test_full_vectors_at_every_step_to_ctx4096():
+    """The last 32 positions of the context (4064 .. 4095) of the full model
+    over a synthetic cache of 4064 positions, teacher-forced with the oracle's
+    greedy tokens: all 32000 logits of every step against the float64 oracle,
+    which runs here on the host beside the GPU."""
+    import torch
+    from decode_step_05_amd import Decoder
+    from oracle import OracleDecoder, greedy
+    from synth import FULL, make_kv
+
+    from parity import assert_close, check_token
+
+    cfg, start, n, tok0 = FULL, 4064, 32, 17
+    say(f"[generation] full vectors: cfg={cfg.name} cache {start} (seed 2) + {n} steps from token {tok0}")
+    w = make_weights(cfg, seed=0, threads=16)
+    K, V = make_kv(cfg, start, seed=2)
+    orc = OracleDecoder(cfg, w)
+    cache = orc.new_cache()
+    orc.load_cache(cache, K, V)
+    ref, toks = [], [tok0]
+    for s in range(n):
+        z = orc.step(cache, token=toks[-1])
+        ref.append(z)
+        toks.append(greedy(z))
+    del orc, cache
+    say(f"[generation] full vectors: oracle done, tokens {toks[1:9]}...")
+    dec = Decoder(cfg, w)
+    del w
+    seq = dec.sequence()
+    seq.load_cache(K, V)
+    got, dev_tok = [], []
+    for s in range(n):
+        seq.step(int(toks[s]))
+        z, a = seq.logits()
+        got.append(z)
+        dev_tok.append(a)
+    got = torch.stack(got).cpu().numpy()
+    dev_tok = torch.cat(dev_tok).cpu().numpy()
+    st = seq.status()
+    assert st[0] == 4096 and st[2] == 0, st
+    worst = (0.0, 0.0)
+    for s in range(n):
+        a, r = assert_close(got[s], ref[s], f"position {start + s}")
+        worst = (max(worst[0], a), max(worst[1], r))
+        assert check_token(int(dev_tok[s]), ref[s], a), (start + s, int(dev_tok[s]), toks[s + 1])
+    say(f"[generation] full vectors at positions {start}..{start + n - 1}: worst max|d|={worst[0]:.2e} "
+        f"rel={worst[1]:.2e}")

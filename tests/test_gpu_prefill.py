@@ -59,7 +59,6 @@ def _check_caches(seq, cache, n, what):
     (TINY, 1, 1, 4, "graph"),
     (TINY, 128, 128, 8, "graph"),
     (TINY, 128, 48, 8, "graph"),
-    (TINY, 128, 48, 8, "persistent"),
     (TINY, 128, 48, 8, "eager"),
     (RAGGED, 40, 17, 6, "graph"),
     (WIDE_GROUP, 150, 64, 6, "graph"),
@@ -79,7 +78,7 @@ def test_prefill_batched_matches_oracle(cfg, plen, chunk, steps, mode):
     o.forward_sequence(tokens=prompt, cache=cache)
     ref_z, ref_t = o.generate(prompt, steps)
 
-    modes = {"persistent": C.LF_MODE_PERSISTENT, "graph": C.LF_MODE_GRAPH, "eager": C.LF_MODE_EAGER}
+    modes = {"graph": C.LF_MODE_GRAPH, "eager": C.LF_MODE_EAGER}
     dec = Decoder(cfg, w, mode=modes[mode])
     assert dec.mode == modes[mode]
     seq = dec.sequence()

@@ -28,21 +28,9 @@ def test_library_exports_every_declared_symbol():
     assert sorted(C.EXPORTS) == declared
 
 
-def _stream_copy_bytes(cfg):
-    # the stream step kernel's copy of every GEMV matrix: rows dealt to
-    # 256 workgroups x 8 compute waves (padded to whole rows per wave), each
-    # row a whole number of 1-KB (512-element) slots
-    waves = 256 * 8
-    d, q = cfg.d_model, cfg.n_q_heads * cfg.head_dim
-    mats = [(cfg.qkv_rows, d), (d, q), (2 * cfg.ffn, d), (d, cfg.ffn)] * cfg.n_layers
-    if cfg.vocab:
-        mats.append((cfg.vocab, d))
-    return sum(-(-rows // waves) * -(-k // 512) * waves * 1024 for rows, k in mats)
-
-
 def test_sizes_of_the_workloads():
-    # workspace = weights twice (row-major and stream order) + small
-    # activations; sequence buffer = caches + state
+    # workspace = the weights once + the rotary table, activations and
+    # attention exchange buffers (a few MB); sequence buffer = caches + state
     for cfg in (TINY, LAYER_FULL, FULL, LANE):
         c = C.make_config(cfg)
         ws, kv = C.lf_workspace_bytes(c), C.lf_kv_bytes(c)
@@ -51,11 +39,7 @@ def test_sizes_of_the_workloads():
     cache = 2 * 15 * 4096 * 16 * 128 * 2
     assert cache <= C.lf_kv_bytes(c) < cache + 4096 * 4 + 32000 * 4 + 4096
     weights = 2338451456 * 2
-    stream = _stream_copy_bytes(FULL)
-    # = the weights without the embedding table and the norm gains, with the
-    # LM head's 32000 rows padded to 32768 (16 per wave); everything else divides
-    assert stream == weights - 32000 * 4096 * 2 - (2 * 15 + 1) * 4096 * 2 + 768 * 4096 * 2
-    assert weights + stream <= C.lf_workspace_bytes(c) < weights + stream + 8 * 2 ** 20
+    assert weights <= C.lf_workspace_bytes(c) < weights + 8 * 2 ** 20
 
 
 @pytest.mark.parametrize("field,value,msg", [
@@ -160,6 +144,40 @@ def test_sample_argument_errors_before_any_device_call():
     assert lib.lf_sample(0x1000, 0, 10, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
     assert lib.lf_sample(0x1000, 1, 0, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
     assert lib.lf_sample(0x1000, 1, (1 << 24) + 1, 1.0, 0x1000, 0x1000, None) == C.LF_EINVAL
-    for t in (0.0, -1.0, float("nan"), float("inf")):
+    # 1e-45 is a subnormal fp32 whose reciprocal overflows to inf
+    for t in (0.0, -1.0, float("nan"), float("inf"), 1e-45, -1e-45):
         rc = lib.lf_sample(0x1000, 1, 10, t, 0x1000, 0x1000, None)
-        assert rc == C.LF_EINVAL and "temperature" in C.lf_last_error()
+        assert rc == C.LF_EINVAL and "temperature" in C.lf_last_error(), t
+
+
+def test_attention_plan():
+    """Layouts whose workgroups wait on each other are chosen only where the
+    device holds all of those workgroups at once."""
+    c = C.make_config(FULL)
+    # MI355X: 256 CUs, one fused workgroup per CU (its key copies fill most of
+    # the LDS), several attention workgroups per CU, launches dealt to XCDs in turn
+    fused, xcd = C.lf_plan_attention(c, 256, 8, 1, True)
+    assert fused and xcd == [True] * 15
+    # no room for the fused kernel's 256 workgroups at once, or too few CUs
+    assert C.lf_plan_attention(c, 256, 8, 0, True)[0] is False
+    assert C.lf_plan_attention(c, 128, 8, 1, True)[0] is False
+    # workgroups not dealt to the XCDs in turn: neither the fused kernel nor the XCD layout
+    fused, xcd = C.lf_plan_attention(c, 256, 8, 1, False)
+    assert not fused and not any(xcd)
+    # the XCD layout needs all S * n_kv = 16 * 16 attention workgroups at once
+    assert C.lf_plan_attention(c, 32, 8, 1, True)[1] == [True] * 15
+    assert C.lf_plan_attention(c, 31, 8, 1, True)[1] == [False] * 15
+    # 256 kv heads of 32 dims: 16 splits each, 4096 workgroups; no room for
+    # all of them, so each kv head's splits run as consecutive workgroups
+    big = C.make_config(FULL)
+    big.n_q_heads, big.n_kv_heads, big.head_dim, big.n_lanes = 256, 256, 32, 16
+    fused, xcd = C.lf_plan_attention(big, 256, 8, 1, True)
+    assert not fused and not any(xcd)
+    # a layer whose 16 splits of one kv head cannot be resident together is rejected
+    with pytest.raises(C.LfError, match="cannot be resident"):
+        C.lf_plan_attention(c, 15, 1, 1, True)
+    lib = C.load()
+    one = ctypes.c_int32()
+    layers = (ctypes.c_int32 * 15)()
+    assert lib.lf_plan_attention(ctypes.byref(c), 0, 8, 1, 1, ctypes.byref(one), layers) == C.LF_EINVAL
+    assert lib.lf_plan_attention(ctypes.byref(c), 256, 8, 1, 1, None, layers) == C.LF_EINVAL
