@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -229,6 +230,7 @@ struct lf_model {
   std::vector<char> attn_xcd;            // per layer: k_attn runs with the XCD layout
   bool fused = false;                    // ... and do
   std::vector<GraphEntry> graphs;
+  void* scratch = nullptr;               // this device's address of the static prompt-pass scratch
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
@@ -738,6 +740,106 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
   }
 }
 
+// Arguments shared by both prompt-pass entry points.
+int prefill_check(lf_model* m, lf_kv* kv, int n, int chunk) {
+  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
+  if (m->D.V == 0) return fail(LF_EINVAL, "the prompt pass needs vocab > 0");
+  if (n < 1) return fail(LF_EINVAL, "n = %d < 1", n);
+  if (chunk < 1 || chunk > LF_MAX_PREFILL_CHUNK) return fail(LF_EINVAL, "chunk %d out of [1, %d]", chunk, LF_MAX_PREFILL_CHUNK);
+  if (static_cast<long>(kv->len) + n > m->D.ctx) return fail(LF_ERANGE, "len %d + n %d > max_ctx %d", kv->len, n, m->D.ctx);
+  return LF_OK;
+}
+
+// The prompt pass over n positions in chunks of `chunk`, with its scratch at
+// ws (at least pf_layout(D, chunk).total bytes, 256-byte aligned).
+int prefill_run(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int n, int chunk, char* ws, hipStream_t st) {
+  const Dims& D = m->D;
+  const WsLayout& W = m->W;
+  const PfLayout P = pf_layout(D, chunk);
+  hipLaunchKernelGGL(lf::k_put_tokens, dim3((n + 255) / 256), dim3(256), 0, st, kv->state(), kv->tokens(), kv->len, d_tokens, n);
+  int last = 0;
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    last = std::min(chunk, n - c0);
+    enqueue_pf_chunk(m, kv, ws, P, last, kv->len + c0, st);
+  }
+  hipLaunchKernelGGL(lf::k_pf_finish, dim3(1), dim3(lf::kBlock), 0, st,
+                     reinterpret_cast<const float*>(ws + P.x) + static_cast<size_t>(last - 1) * D.d, m->at<float>(W.x), D.d,
+                     kv->state(), kv->len + n - 1);
+  // final RMSNorm + LM head + greedy argmax of the last position (the decode step's kernel)
+  lf::GemvArgs a{};
+  a.eps = m->cfg.rms_eps;
+  a.vocab = D.V;
+  a.state = kv->state();
+  a.tokens = kv->tokens();
+  a.max_ctx = D.ctx;
+  a.hd = D.hd;
+  a.qpl = D.qpl;
+  a.kpl = D.kpl;
+  a.rope = m->at<float2>(W.rope);
+  a.W = m->at<half_t>(W.lm);
+  a.rows = D.V;
+  a.K = D.d;
+  a.in_kind = lf::kInNormF32;
+  a.x = m->at<float>(W.x);
+  a.gain = m->at<half_t>(W.gf);
+  a.y = kv->logits();
+  a.counter = m->at<unsigned>(W.counters) + D.hkv;
+  a.best = m->at<unsigned long long>(W.best);
+  launch_gemv<lf::kEpiLogits>(a, st);
+  LF_HIP(hipPeekAtLastError());
+  kv->len += n;
+  return LF_OK;
+}
+
+}  // namespace
+
+// Scratch of lf_prefill_batched_static, for callers that cannot allocate
+// device memory. Each device the library runs on holds its own copy until the
+// process ends; every call on a device shares it (calls that overlap on one
+// device race). Host code never uses the name as an address: the device
+// address comes from hipGetSymbolAddress, once per device (static_scratch).
+constexpr size_t kStaticScratchBytes = LF_STATIC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes == size_t(32) << 20, "the header states 32 MiB");
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// The current device's address of `scratch`, looked up on the first call for
+// that device (with it current) and kept.
+int static_scratch(void** out) {
+  int dev = 0;
+  LF_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(LF_EINVAL, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(LF_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LF_OK;
+}
+
+// The largest chunk whose prompt-pass scratch fits the static scratch (0 if
+// not even one position fits).
+int static_chunk_max(const Dims& D) {
+  if (pf_layout(D, 1).total > kStaticScratchBytes) return 0;
+  int lo = 1, hi = LF_MAX_PREFILL_CHUNK;  // the scratch grows with the chunk
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (pf_layout(D, mid).total <= kStaticScratchBytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 }  // namespace
 
 // ===================================================================== C ABI
@@ -866,6 +968,7 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
   if ((rc = probe_xcd_classes(m, st))) return bail(rc);
+  if ((rc = static_scratch(&m->scratch))) return bail(rc);
   int dev = 0, ncu = 0, attn_per_cu = 0, fused_per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return bail(fail(LF_EHIP, "device query: %s", hipGetErrorString(hipGetLastError())));
@@ -1015,51 +1118,26 @@ size_t lf_prefill_workspace_bytes(const lf_config* cfg, int32_t chunk) {
 int lf_prefill_batched(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, int32_t chunk, void* d_workspace,
                        size_t ws_bytes, void* stream) {
   if (!m || !kv || !d_tokens || !d_workspace) return fail(LF_EINVAL, "null argument");
-  if (kv->m != m) return fail(LF_EINVAL, "sequence belongs to another model");
-  if (m->D.V == 0) return fail(LF_EINVAL, "lf_prefill_batched needs vocab > 0");
-  if (n < 1) return fail(LF_EINVAL, "n = %d < 1", n);
-  if (chunk < 1 || chunk > LF_MAX_PREFILL_CHUNK) return fail(LF_EINVAL, "chunk %d out of [1, %d]", chunk, LF_MAX_PREFILL_CHUNK);
+  int rc = prefill_check(m, kv, n, chunk);
+  if (rc) return rc;
   if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign) return fail(LF_EINVAL, "workspace not 256-byte aligned");
-  const PfLayout P = pf_layout(m->D, chunk);
-  if (ws_bytes < P.total) return fail(LF_EINVAL, "workspace %zu bytes < %zu needed for chunk %d", ws_bytes, P.total, chunk);
-  if (static_cast<long>(kv->len) + n > m->D.ctx) return fail(LF_ERANGE, "len %d + n %d > max_ctx %d", kv->len, n, m->D.ctx);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(d_workspace);
-  hipLaunchKernelGGL(lf::k_put_tokens, dim3((n + 255) / 256), dim3(256), 0, st, kv->state(), kv->tokens(), kv->len, d_tokens, n);
-  int last = 0;
-  for (int c0 = 0; c0 < n; c0 += chunk) {
-    last = std::min(chunk, n - c0);
-    enqueue_pf_chunk(m, kv, ws, P, last, kv->len + c0, st);
-  }
-  const Dims& D = m->D;
-  const WsLayout& W = m->W;
-  hipLaunchKernelGGL(lf::k_pf_finish, dim3(1), dim3(lf::kBlock), 0, st,
-                     reinterpret_cast<const float*>(ws + P.x) + static_cast<size_t>(last - 1) * D.d, m->at<float>(W.x), D.d,
-                     kv->state(), kv->len + n - 1);
-  // final RMSNorm + LM head + greedy argmax of the last position (the decode step's kernel)
-  lf::GemvArgs a{};
-  a.eps = m->cfg.rms_eps;
-  a.vocab = D.V;
-  a.state = kv->state();
-  a.tokens = kv->tokens();
-  a.max_ctx = D.ctx;
-  a.hd = D.hd;
-  a.qpl = D.qpl;
-  a.kpl = D.kpl;
-  a.rope = m->at<float2>(W.rope);
-  a.W = m->at<half_t>(W.lm);
-  a.rows = D.V;
-  a.K = D.d;
-  a.in_kind = lf::kInNormF32;
-  a.x = m->at<float>(W.x);
-  a.gain = m->at<half_t>(W.gf);
-  a.y = kv->logits();
-  a.counter = m->at<unsigned>(W.counters) + D.hkv;
-  a.best = m->at<unsigned long long>(W.best);
-  launch_gemv<lf::kEpiLogits>(a, st);
-  LF_HIP(hipPeekAtLastError());
-  kv->len += n;
-  return LF_OK;
+  const size_t need = pf_layout(m->D, chunk).total;
+  if (ws_bytes < need) return fail(LF_EINVAL, "workspace %zu bytes < %zu needed for chunk %d", ws_bytes, need, chunk);
+  return prefill_run(m, kv, d_tokens, n, chunk, static_cast<char*>(d_workspace), static_cast<hipStream_t>(stream));
+}
+
+int lf_prefill_batched_static(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, int32_t chunk, void* stream) {
+  if (!m || !kv || !d_tokens) return fail(LF_EINVAL, "null argument");
+  const int fit = static_chunk_max(m->D);
+  if (fit < 1) return fail(LF_EINVAL, "one position of this shape needs more than the %zu-byte static scratch", kStaticScratchBytes);
+  if (chunk == 0) chunk = std::min(fit, std::max(n, 1));
+  int rc = prefill_check(m, kv, n, chunk);
+  if (rc) return rc;
+  if (chunk > fit)
+    return fail(LF_EINVAL, "chunk %d needs %zu bytes of scratch; the static scratch holds %zu (at most %d positions per chunk)",
+                chunk, pf_layout(m->D, chunk).total, kStaticScratchBytes, fit);
+  if (!m->scratch) return fail(LF_EINVAL, "no static scratch address for the model's device");
+  return prefill_run(m, kv, d_tokens, n, chunk, static_cast<char*>(m->scratch), static_cast<hipStream_t>(stream));
 }
 
 int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream) {

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblfdecode
 MAX_LAYERS = 64
 
 LF_OK, LF_EINVAL, LF_ERANGE, LF_EHIP = 0, -1, -2, -3
+LF_STATIC_SCRATCH_BYTES = 32 << 20
 LF_MODE_EAGER, LF_MODE_GRAPH = 0, 1
 
 # Every symbol include/lfdecode.h declares.
@@ -22,7 +23,7 @@ EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
     "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused", "lf_plan_attention",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
-    "lf_prefill_workspace_bytes", "lf_prefill_batched",
+    "lf_prefill_workspace_bytes", "lf_prefill_batched", "lf_prefill_batched_static",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
     "lf_step_kernel_times", "lf_kernel_time", "lf_read_bandwidth", "lf_sample", "lf_last_error",
 )
@@ -81,6 +82,7 @@ def load():
         "lf_prefill": (c_int, [P, P, P, c_int32, P]),
         "lf_prefill_workspace_bytes": (c_size_t, [POINTER(lf_config), c_int32]),
         "lf_prefill_batched": (c_int, [P, P, P, c_int32, c_int32, P, c_size_t, P]),
+        "lf_prefill_batched_static": (c_int, [P, P, P, c_int32, c_int32, P]),
         "lf_decode_step": (c_int, [P, P, P, P]),
         "lf_decode_steps": (c_int, [P, P, c_int32, P]),
         "lf_decode_step_hidden": (c_int, [P, P, P, P, P]),
@@ -254,6 +256,11 @@ def lf_prefill_batched(model, kv, tokens, chunk: int, workspace, n=None, stream=
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().lf_prefill_batched(model, kv, _ptr(tokens), int(n), int(chunk), _ptr(workspace), nbytes,
                                      _stream(stream)))
+
+
+def lf_prefill_batched_static(model, kv, tokens, chunk: int = 0, n=None, stream=None) -> None:
+    n = tokens.numel() if n is None else n
+    _check(load().lf_prefill_batched_static(model, kv, _ptr(tokens), int(n), int(chunk), _stream(stream)))
 
 
 def lf_decode_step(model, kv, token=None, stream=None) -> None:

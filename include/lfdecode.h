@@ -253,6 +253,25 @@ int lf_prefill_batched(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t 
                        size_t ws_bytes, void* stream);
 
 /*
+ * The batched prompt pass without a caller workspace, for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, result and state as
+ * lf_prefill_batched, with the scratch in an array of LF_STATIC_SCRATCH_BYTES
+ * that the library holds on each device it runs on until the process ends
+ * (its address is looked up once per device, in lf_model_init). Allocates
+ * nothing. Every call on a device shares that array and it keeps the last
+ * call's contents: calls that overlap on one device (on different streams,
+ * or from different threads) race.
+ * chunk: positions per pass, from 1 to the largest whose scratch fits the
+ * array (282 for d_model 4096, 32 q / 16 kv heads of 128 and SwiGLU 7168), or
+ * 0 for that largest. LF_EINVAL for a larger chunk (lf_last_error states the
+ * limit), null arguments, vocab == 0 or n < 1; LF_ERANGE if len + n > max_ctx.
+ * Enqueued on stream.
+ */
+#define LF_STATIC_SCRATCH_BYTES (32u << 20)
+int lf_prefill_batched_static(lf_model* m, lf_kv* kv, const int32_t* d_tokens, int32_t n, int32_t chunk, void* stream);
+
+/*
  * The decode step: append one position. Every weight of the model is read
  * once plus the cache keys each layer sees, which is what bounds its speed
  * at batch 1 (blog, "The idea" and "Designing the architecture"); FP16
