@@ -1,0 +1,462 @@
+// Batched decode step for gfx950: one decode step of up to kMaxBatch
+// sequences of one model, for stochastic decoding of several continuations
+// of one prompt (the asector.ru summary, "Performance and infrastructure",
+// proposes sampling N completions per problem, scored as pass@N). Every
+// weight is read from HBM once per step for all the sequences; each sequence
+// keeps its own cache, position and tokens.
+//
+// Every projection is a skinny GEMM Y[s][row] = sum_k W[row][k] X[s][k] on
+// the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation). The
+// instruction multiplies a 16 x 32 block of fp16 weights (16 rows) by a
+// 32 x 16 block whose 16 columns are the fp16 hi and lo parts of the fp32
+// activations of 8 sequences (hi = fp16(x), lo = fp16(x - hi), about 22
+// significant bits, as in the prompt pass): column s holds sequence s's hi
+// part, column 8 + s its lo part, and the row's result is the sum of the two
+// columns. Lane l holds, of its operands, weight row l % 16 and column
+// l % 16 with the 8 consecutive k of group l / 16; of the result, column
+// l % 16 and rows 4 (l / 16) .. 4 (l / 16) + 3. Each wave builds its
+// activation operand from the fp32 vectors directly (no LDS staging), and
+// the 8 waves of a workgroup split K; their partial results are summed in
+// LDS in a fixed order.
+//
+// RMSNorm: the producer of a normalised input (the embedding gather, the O
+// and down projections) also writes, per workgroup, the partial sums of
+// squares of the new residual; the consumer sums them in a fixed order and
+// applies 1/sqrt(mean + eps) to its outputs, the gain to its inputs.
+#pragma once
+#include "lf_kernels.h"
+
+namespace lf {
+
+constexpr int kMaxBatch = 8;
+constexpr int kSsStride = 1024;  // partial sums of squares per sequence (one per producing workgroup)
+constexpr int kSsMax = 512;      // most partials a consumer reads per sequence
+
+// Per-sequence buffers of one batched step (entries past n unused).
+struct BatchSeqs {
+  int32_t* state[kMaxBatch];
+  int32_t* tokens[kMaxBatch];
+  half_t* kc[kMaxBatch];  // each sequence's K cache (layer 0; layer l at + l * layer_cache)
+  half_t* vc[kMaxBatch];
+  float* logits[kMaxBatch];
+};
+
+// The position of each of the n sequences, read with scalar loads (the state
+// pointers are kernel arguments) before any vector load of the caller.
+__device__ __forceinline__ void batch_positions(const BatchSeqs& q, int n, int (&pos)[kMaxBatch]) {
+#pragma unroll
+  for (int s = 0; s < kMaxBatch; ++s) pos[s] = s < n ? cload(q.state[s] + kLen) : 0;
+}
+
+__device__ __forceinline__ int pick(const int (&v)[kMaxBatch], int s) {
+  int r = v[0];
+#pragma unroll
+  for (int i = 1; i < kMaxBatch; ++i) r = s == i ? v[i] : r;
+  return r;
+}
+
+// ---------------------------------------------------------- skinny GEMM
+
+enum BEpi : int { kBEpiQKV = 0, kBEpiSwiGLU = 1, kBEpiResid = 2, kBEpiLogits = 3 };
+
+struct BGemmArgs {
+  const half_t* W;     // [rows, K] fp16 (QKV and gate/up rows repacked as for the batch-1 kernels)
+  int rows, K;         // K a multiple of 8
+  const float* X;      // input of sequence s: X + s * x_stride, fp32 [K]
+  int x_stride;
+  const half_t* gain;  // RMSNorm gain [K] if the input is normalised
+  const float* ss;     // ... and the partial sums of squares of the input, [kMaxBatch][kSsStride]
+  int ss_n;            // partials per sequence (<= kSsMax)
+  float eps;
+  int n;               // sequences (1 .. kMaxBatch)
+  BatchSeqs seq;
+  size_t layer_cache;  // elements between two layers' caches
+  int layer;
+  float* y;            // QKV: queries [s][q_dim]; residual: x [s][rows] (+=); SwiGLU: [s][rows / 2]
+  int y_stride;
+  float* ss_out;       // residual: partial sums of squares of the new residual [kMaxBatch][kSsStride]
+  const float2* rope;  // (cos, sin) [max_ctx][hd / 2]
+  int hd, qpl, kpl, max_ctx;
+  unsigned* counter;          // logits: workgroups done (the last one ends the step)
+  unsigned long long* best;   // logits: packed greedy key per sequence
+};
+
+// QKV epilogue of one sequence: rotary pair of packed rows (r, r + 1) at
+// position p (as qkv_put; cs: the pair's (cos, sin) at p, loaded early).
+__device__ __forceinline__ void bqkv_put(const BGemmArgs& a, int s, int p, int r, float y0, float y1, float2 cs) {
+  const int half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl;
+  const int u = r / a.hd, c = (r % a.hd) >> 1;
+  const int ln = u / upl, j = u % upl;
+  if (j < a.qpl + a.kpl) {
+    const float t0 = y0 * cs.x - y1 * cs.y;
+    const float t1 = y0 * cs.y + y1 * cs.x;
+    y0 = t0;
+    y1 = t1;
+  }
+  if (j < a.qpl) {
+    float* qh = a.y + static_cast<size_t>(s) * a.y_stride + static_cast<size_t>(ln * a.qpl + j) * a.hd;
+    qh[c] = y0;
+    qh[c + half_hd] = y1;
+  } else {
+    const bool is_k = j < a.qpl + a.kpl;
+    const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
+    half_t* base = (is_k ? a.seq.kc[s] : a.seq.vc[s]) + a.layer_cache * a.layer;
+    half_t* dst = base + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
+    dst[c] = static_cast<half_t>(y0);
+    dst[c + half_hd] = static_cast<half_t>(y1);
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int off) {
+  const unsigned lo = __float_as_uint(lane_xor(__uint_as_float(static_cast<unsigned>(v)), off));
+  const unsigned hi = __float_as_uint(lane_xor(__uint_as_float(static_cast<unsigned>(v >> 32)), off));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Weights and inputs of KB k-steps (32 k each) of one wave.
+template <int KB, int TPW, bool NORM>
+struct BBatch {
+  u32x4 w[KB][TPW];
+  f32x4 x[KB][2];
+  u32x4 gn[NORM ? KB : 1];
+};
+
+// Workgroup: TPW tiles of 16 rows, 8 waves each taking an eighth of the
+// k-steps; a wave's k-steps are loaded KB at a time, two batches in flight.
+template <int EPI, int TPW, bool NORM, int KB>
+__global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
+  constexpr int NW = 8;
+  static_assert(NW == kMaxBatch, "wave w sums sequence w's partial sums of squares");
+  __shared__ float red[NW][TPW][4][kWave];
+  __shared__ float rs[kMaxBatch];
+  __shared__ float ssw[TPW][kMaxBatch];
+  __shared__ unsigned long long wkey[TPW][kMaxBatch];
+  __shared__ int flag;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int g = lane >> 4, col = lane & 15;
+  const int s_in = min(col & 7, a.n - 1);  // the sequence whose input this lane's column holds
+  const bool lo_col = col >= 8;
+  const int nks = (a.K + 31) >> 5;
+  const int per = (nks + NW - 1) / NW;       // k-steps per wave
+  const int ks0 = wave * per, ks1 = min(nks, ks0 + per);
+  const int ntiles = (a.rows + 15) >> 4, tile0 = blockIdx.x * TPW;
+
+  int pos[kMaxBatch];
+  if constexpr (EPI == kBEpiQKV || EPI == kBEpiLogits) batch_positions(a.seq, a.n, pos);
+  // partial sums of squares of sequence `wave`, loaded before the weights
+  // (a wave's loads complete in issue order) and summed at the end
+  float ssv[kSsMax / kWave];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int j = 0; j < kSsMax / kWave; ++j) {
+      const int i = lane + kWave * j;
+      ssv[j] = (wave < a.n && i < a.ss_n) ? a.ss[wave * kSsStride + i] : 0.f;
+    }
+  }
+
+  // what the epilogue reads, loaded before the weights too: wave t < TPW
+  // finishes tile tile0 + t, lane (g, col) rows 16 tile + 4 g + r (r < 4) of
+  // sequence col: their residual values, or their rotary angles
+  const bool epi = wave < TPW && tile0 + wave < ntiles;
+  const int s = col;
+  const bool act = epi && s < a.n;
+  const int row0 = 16 * (tile0 + wave) + 4 * g;
+  f32x4 xres = {0.f, 0.f, 0.f, 0.f};
+  float2 cs[2] = {{1.f, 0.f}, {1.f, 0.f}};
+  if constexpr (EPI == kBEpiResid) {
+    if (act) {
+      const float* xp = a.y + static_cast<size_t>(s) * a.y_stride;
+      if (row0 + 3 < a.rows) {
+        xres = *reinterpret_cast<const f32x4*>(xp + row0);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xres[r] = row0 + r < a.rows ? xp[row0 + r] : 0.f;
+      }
+    }
+  } else if constexpr (EPI == kBEpiQKV) {
+    if (act) {
+      const int p = min(pick(pos, s), a.max_ctx - 1), half_hd = a.hd >> 1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = ((min(row0 + 2 * h, a.rows - 2)) % a.hd) >> 1;
+        cs[h] = a.rope[static_cast<size_t>(p) * half_hd + c];
+      }
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  const half_t* wr[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    wr[t] = a.W + static_cast<size_t>(min(16 * min(tile0 + t, ntiles - 1) + col, a.rows - 1)) * a.K;
+  const float* xr = a.X + static_cast<size_t>(s_in) * a.x_stride;
+
+  // k-steps past this wave's range load the range's last k-step again (an
+  // L2 hit, no new HBM traffic) and are masked where used; so are k-groups
+  // past K (K is a multiple of 8: a group is wholly in or out)
+  auto issue = [&](BBatch<KB, TPW, NORM>& b, int kb) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int ks = min(kb + j, ks1 - 1);
+      const int k = min(ks * 32 + 8 * g, a.K - 8);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) b.w[j][t] = ld_stream(wr[t] + k);
+      b.x[j][0] = *reinterpret_cast<const f32x4*>(xr + k);
+      b.x[j][1] = *reinterpret_cast<const f32x4*>(xr + k + 4);
+      if constexpr (NORM) b.gn[j] = ld16(a.gain + k);
+    }
+  };
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const BBatch<KB, TPW, NORM>& b, int kb) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int ks = kb + j;
+      const bool valid = ks < ks1 && ks * 32 + 8 * g < a.K;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = b.x[j][0][e];
+        v[4 + e] = b.x[j][1][e];
+      }
+      if constexpr (NORM) {
+        float gf[8];
+        unpack8(b.gn[j], gf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= gf[e];
+      }
+      h8 frag;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const half_t hi = static_cast<half_t>(v[e]);
+        const half_t lo = static_cast<half_t>(v[e] - static_cast<float>(hi));
+        frag[e] = valid ? (lo_col ? lo : hi) : static_cast<half_t>(0.f);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, b.w[j][t]), frag, acc[t], 0, 0, 0);
+    }
+  };
+  // two batches in flight, in a loop without any condition on an issue (one
+  // makes the compiler wait for every load before it) and a peeled last pair.
+  // The batch count is rounded up to even: with an odd count the last batch
+  // repeats the range's last k-step (L2 hits, masked); the host picks KB so
+  // that the count is even where it can. The scheduling barriers keep each
+  // batch's loads together, ahead of the other batch's arithmetic (the
+  // scheduler would otherwise move loads next to their uses and leave few in
+  // flight).
+  const int nb = ((per + KB - 1) / KB + 1) & ~1;
+  BBatch<KB, TPW, NORM> b0, b1;
+  issue(b0, ks0);
+  int i = 0;
+  for (; i + 2 < nb; i += 2) {
+    issue(b1, ks0 + (i + 1) * KB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0, ks0 + i * KB);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b0, ks0 + (i + 2) * KB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1, ks0 + (i + 1) * KB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  issue(b1, ks0 + (i + 1) * KB);
+  __builtin_amdgcn_sched_barrier(0);
+  compute(b0, ks0 + i * KB);
+  __builtin_amdgcn_sched_barrier(0);
+  compute(b1, ks0 + (i + 1) * KB);
+
+  // sum the waves' partial results in LDS (fixed order); the norm scale
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t][r][lane] = acc[t][r];
+  if constexpr (NORM) {
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSsMax / kWave; ++j) sum += ssv[j];
+    sum = wave_total(sum);
+    if (lane == 0 && wave < a.n) rs[wave] = 1.0f / sqrtf(sum / static_cast<float>(a.K) + a.eps);
+  }
+  lds_barrier();
+
+  // wave t < TPW finishes tile tile0 + t
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  if (epi) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][wave][r][lane];
+      y[r] = v + lane_xor(v, 8);  // hi column + lo column
+    }
+  }
+  if constexpr (EPI == kBEpiQKV) {
+    if (act) {
+      const float sc = NORM ? rs[s] : 1.f;
+      const int p = pick(pos, s);
+#pragma unroll
+      for (int r = 0; r < 4; r += 2)
+        if (row0 + r < a.rows) bqkv_put(a, s, p, row0 + r, y[r] * sc, y[r + 1] * sc, cs[r >> 1]);
+    }
+  } else if constexpr (EPI == kBEpiSwiGLU) {
+    if (act) {
+      const float sc = NORM ? rs[s] : 1.f;
+#pragma unroll
+      for (int r = 0; r < 4; r += 2)
+        if (row0 + r < a.rows) {
+          const float gt = y[r] * sc, up = y[r + 1] * sc;
+          a.y[static_cast<size_t>(s) * a.y_stride + ((row0 + r) >> 1)] = gt / (1.0f + expf(-gt)) * up;
+        }
+    }
+  } else if constexpr (EPI == kBEpiResid) {
+    float sq = 0.f;
+    if (act) {
+      float* xp = a.y + static_cast<size_t>(s) * a.y_stride + row0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (row0 + r < a.rows) {
+          const float xn = xres[r] + y[r];
+          xp[r] = xn;
+          sq = fmaf(xn, xn, sq);
+        }
+    }
+    if (wave < TPW) {
+      sq += lane_xor(sq, 16);
+      sq += lane_xor(sq, 32);
+      if (lane < kMaxBatch) ssw[wave][lane] = sq;
+    }
+    lds_barrier();
+    if (tid < a.n) {
+      float tot = 0.f;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) tot += ssw[t][tid];
+      a.ss_out[tid * kSsStride + blockIdx.x] = tot;
+    }
+  } else {  // kBEpiLogits
+    unsigned long long key = 0;
+    if (act) {
+      const float sc = NORM ? rs[s] : 1.f;
+      float* z = a.seq.logits[s];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (row0 + r < a.rows) {
+          const float v = y[r] * sc;
+          z[row0 + r] = v;
+          if (v == v) key = max(key, argmax_key(v, row0 + r));  // a NaN logit never wins
+        }
+    }
+    if (wave < TPW) {
+      key = max(key, shfl_xor_u64(key, 16));
+      key = max(key, shfl_xor_u64(key, 32));
+      if (lane < kMaxBatch) wkey[wave][lane] = key;
+    }
+    lds_barrier();
+    if (tid < a.n) {
+      unsigned long long k = 0;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) k = max(k, wkey[t][tid]);
+      if (k) __hip_atomic_fetch_max(a.best + tid, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!arrive(a.counter, gridDim.x, &flag)) return;
+    if (tid < a.n) {
+      const unsigned long long k = __hip_atomic_load(a.best + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int i = k ? argmax_index(k) : 0;  // k == 0 only if every logit is NaN
+      if (i < 0 || i >= a.rows) i = 0;
+      int32_t* st = a.seq.state[tid];
+      const int p = pick(pos, tid);
+      st[kArgmax] = i;
+      if (p + 1 >= st[kFedEnd]) a.seq.tokens[tid][p + 1] = i;
+      st[kLen] = p + 1;
+      __hip_atomic_store(a.best + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// --------------------------------------------------- embedding, attention
+
+struct BEmbedArgs {
+  BatchSeqs seq;
+  const half_t* emb;  // [vocab, d]
+  float* x;           // residual [s][d]
+  float* ss;          // partial sums of squares [kMaxBatch][kSsStride] (one partial per sequence)
+  int d, vocab, max_ctx;
+};
+
+// Workgroup s: the embedding row of sequence s's token at its position, as
+// the fp32 residual, and its sum of squares.
+__global__ __launch_bounds__(kBlock) void k_bembed(BEmbedArgs a) {
+  __shared__ float red[kWavesPerBlock];
+  const int s = blockIdx.x;
+  int32_t* st = a.seq.state[s];
+  const int p = st[kLen];
+  if (p >= a.max_ctx) return;  // the host never launches a step on a full cache
+  int tok = a.seq.tokens[s][p];
+  if (tok < 0 || tok >= a.vocab) {
+    tok = tok < 0 ? 0 : a.vocab - 1;
+    if (threadIdx.x == 0) st[kBadToken] = 1;
+  }
+  const half_t* e = a.emb + static_cast<size_t>(tok) * a.d;
+  float* x = a.x + static_cast<size_t>(s) * a.d;
+  float sq = 0.f;
+  for (int i = threadIdx.x; i < a.d; i += kBlock) {
+    const float v = static_cast<float>(e[i]);
+    x[i] = v;
+    sq = fmaf(v, v, sq);
+  }
+  sq = block_sum(sq, red);
+  if (threadIdx.x == 0) a.ss[s * kSsStride] = sq;
+}
+
+struct AttnBArgs {
+  AttnXArgs a;          // shared fields (t.q, t.kc, t.vc, t.state, part, o, epochs per sequence below)
+  BatchSeqs seq;
+  size_t layer_cache;
+  int layer;
+  const float* q;       // queries [s][q_dim]
+  float* o;             // outputs [s][q_dim]
+  u64* part;            // split states, per sequence part_stride words
+  size_t part_stride;
+  unsigned* epochs;     // [s][n_kv]
+  int q_dim;
+};
+
+// Attention of work item (split blockIdx.x, kv head blockIdx.y) of sequence
+// blockIdx.z: k_attn's two-dimensional layout (the splits of a kv head are
+// consecutive workgroups), with the sequence's cache, position, queries,
+// outputs, split states and epochs.
+template <int HD, int G, int U>
+__global__ __launch_bounds__(kBlock) void k_battn(AttnBArgs b) {
+  __shared__ AttnXSmem<HD, G> sm;
+  const int s = blockIdx.z;
+  AttnXArgs a = b.a;
+  a.t.q = b.q + static_cast<size_t>(s) * b.q_dim;
+  a.t.kc = b.seq.kc[s] + b.layer_cache * b.layer;
+  a.t.vc = b.seq.vc[s] + b.layer_cache * b.layer;
+  a.t.state = b.seq.state[s];
+  a.part = b.part + b.part_stride * s;
+  a.o = b.o + static_cast<size_t>(s) * b.q_dim;
+  a.epochs = b.epochs + static_cast<size_t>(s) * a.n_kv;
+  attn_item<HD, G, U, false>(a, blockIdx.x, blockIdx.y, sm);
+}
+
+// Start a batched step: sequence s's token at its position is d_tokens[s]
+// (each sequence's length is given by the host, as for k_set_pos).
+struct BTokArgs {
+  BatchSeqs seq;
+  int len[kMaxBatch];
+  const int32_t* tokens;
+  int n;
+};
+
+__global__ void k_bset_tokens(BTokArgs a) {
+  const int s = threadIdx.x;
+  if (blockIdx.x != 0 || s >= a.n) return;
+  int32_t* st = a.seq.state[s];
+  st[kLen] = a.len[s];
+  a.seq.tokens[s][a.len[s]] = a.tokens[s];
+  st[kFedEnd] = a.len[s] + 1;
+}
+
+}  // namespace lf

@@ -811,22 +811,14 @@ struct AttnXSmem {
 // of 8) and the splits of a kv head are the workgroups congruent to it
 // modulo 8, so they run on one XCD and exchange their states through its
 // L2; otherwise the grid is (S, n_kv) and the states go through memory.
+// The work item (split si, kv head kvh) of one attention launch, run by a
+// whole workgroup of kBlock threads (see k_attn).
 template <int HD, int G, int U, bool XCD>
-__global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
+__device__ __forceinline__ void attn_item(const AttnXArgs& a, int si, int kvh, AttnXSmem<HD, G>& sm) {
   constexpr int LPR = HD / 8, NW = kWavesPerBlock;
-  __shared__ AttnXSmem<HD, G> sm;
   const int p = a.t.state[kLen];
   if (p >= a.t.max_ctx) return;  // the host never launches a step on a full cache
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  int si, kvh;
-  if constexpr (XCD) {
-    const int b = blockIdx.x, hpc = a.n_kv >> 3, r = b >> 3;  // hpc kv heads per XCD
-    kvh = (b & 7) + 8 * (r % hpc);
-    si = r / hpc;
-  } else {
-    si = blockIdx.x;
-    kvh = blockIdx.y;
-  }
   const int kin = lane / LPR, ch = lane % LPR;
   constexpr int KPW = kWave / LPR;
 
@@ -868,6 +860,21 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
     attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, kvh, si, a.t.S, epoch, epoch, poll, lane);
     if (si == 0 && lane == 0) a.epochs[kvh] = epoch + 1 == 0 ? 1u : epoch + 1;
   }
+}
+
+template <int HD, int G, int U, bool XCD>
+__global__ __launch_bounds__(kBlock) void k_attn(AttnXArgs a) {
+  __shared__ AttnXSmem<HD, G> sm;
+  int si, kvh;
+  if constexpr (XCD) {
+    const int b = blockIdx.x, hpc = a.n_kv >> 3, r = b >> 3;  // hpc kv heads per XCD
+    kvh = (b & 7) + 8 * (r % hpc);
+    si = r / hpc;
+  } else {
+    si = blockIdx.x;
+    kvh = blockIdx.y;
+  }
+  attn_item<HD, G, U, XCD>(a, si, kvh, sm);
 }
 
 // ------------------------------------------- QKV fused with attention

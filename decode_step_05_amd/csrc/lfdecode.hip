@@ -5,6 +5,9 @@
 #include "lf_kernels.h"
 #include "lf_prefill.h"
 #include "lf_sample.h"
+#include "lf_batch.h"
+
+static_assert(LF_MAX_BATCH == lf::kMaxBatch, "the header states the batch limit");
 
 #include <atomic>
 #include <cmath>
@@ -144,6 +147,9 @@ struct WsLayout {
   // tagged exchange buffers of the attention kernels (one zeroed region)
   size_t attn_part, fpart, qkvx, tagged_begin, tagged_end;
   size_t class_epochs;  // QKV fused with attention: epoch per XCD class
+  // batched step (lf_decode_step_batch): per-sequence activations, partial
+  // sums of squares, greedy keys, split states and epochs
+  size_t bx, bq, bo, ba, bss, bbest, bcounter, bpart, bepochs;
   int S_max;
 };
 
@@ -181,8 +187,18 @@ WsLayout ws_layout(const lf_config& c) {
   W.attn_part = take(static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2) * tw);
   W.fpart = take(static_cast<size_t>(D.hq) * kFusedSplits * (D.hd + 2) * tw);
   W.qkvx = take(static_cast<size_t>(D.qkv_rows) * tw);
+  W.bpart = take(static_cast<size_t>(lf::kMaxBatch) * D.hq * W.S_max * (D.hd + 2) * tw);
   W.tagged_end = off;
   W.class_epochs = take(8 * sizeof(unsigned));
+  const size_t B = lf::kMaxBatch;
+  W.bx = take(B * D.d * sizeof(float));
+  W.bq = take(B * D.qdim * sizeof(float));
+  W.bo = take(B * D.qdim * sizeof(float));
+  W.ba = take(B * D.ffn * sizeof(float));
+  W.bss = take(B * lf::kSsStride * sizeof(float));
+  W.bbest = take(B * sizeof(unsigned long long));
+  W.bcounter = take(sizeof(unsigned));
+  W.bepochs = take(B * D.hkv * sizeof(unsigned));
   W.total = off;
   return W;
 }
@@ -209,6 +225,12 @@ KvLayout kv_layout(const lf_config& c) {
 
 }  // namespace
 
+struct BatchGraph {
+  int n;
+  lf_kv* kvs[lf::kMaxBatch];
+  hipGraphExec_t exec;
+};
+
 struct GraphEntry {
   lf_kv* kv;
   const void* xin;
@@ -230,6 +252,7 @@ struct lf_model {
   std::vector<char> attn_xcd;            // per layer: k_attn runs with the XCD layout
   bool fused = false;                    // ... and do
   std::vector<GraphEntry> graphs;
+  std::vector<BatchGraph> batch_graphs;
   void* scratch = nullptr;               // this device's address of the static prompt-pass scratch
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -666,6 +689,202 @@ void drop_graphs(lf_model* m, lf_kv* kv) {
       keep.push_back(g);
   }
   m->graphs.swap(keep);
+  std::vector<BatchGraph> bkeep;
+  for (const BatchGraph& g : m->batch_graphs) {
+    bool hit = kv == nullptr;
+    for (int i = 0; i < g.n; ++i) hit = hit || g.kvs[i] == kv;
+    if (hit)
+      (void)hipGraphExecDestroy(g.exec);
+    else
+      bkeep.push_back(g);
+  }
+  m->batch_graphs.swap(bkeep);
+}
+
+// ------------------------------------------------------------ batched step
+
+// Launch shape of a skinny GEMM: TPW tiles of 16 rows per workgroup (the
+// largest of 4, 2, 1 that still gives 256 workgroups, one per CU), and KB
+// k-steps per batch of loads: 4, or 2 where that makes the number of batches
+// per wave even (the kernel rounds it up to even) or TPW is 4 (registers).
+struct BShape {
+  int tpw, kb, blocks;
+};
+BShape bgemm_shape(int rows, int K) {
+  const int tiles = (rows + 15) / 16;
+  BShape sh{1, 4, tiles};
+  for (int t : {4, 2}) {
+    const int b = (tiles + t - 1) / t;
+    if (b >= 256) {
+      sh = {t, 4, b};
+      break;
+    }
+  }
+  const int per = ((K + 31) / 32 + 7) / 8;  // k-steps per wave (8 waves)
+  if (sh.tpw == 4 || ((per + 3) / 4) % 2) sh.kb = 2;
+  return sh;
+}
+
+template <int EPI, bool NORM, int KB>
+const void* bgemm_fn_kb(int tpw) {
+  if (tpw == 4) return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, 4, NORM, KB>);
+  if (tpw == 2) return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, 2, NORM, KB>);
+  return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, 1, NORM, KB>);
+}
+
+template <int EPI, bool NORM>
+const void* bgemm_fn(const BShape& sh) {
+  if constexpr (EPI == lf::kBEpiResid && NORM) {
+    return nullptr;  // a residual GEMM's input (attention output, SwiGLU) is never normalised
+  } else {
+    if (sh.kb == 2 || sh.tpw == 4) return bgemm_fn_kb<EPI, NORM, 2>(sh.tpw);
+    return bgemm_fn_kb<EPI, NORM, 4>(sh.tpw);
+  }
+}
+
+template <int EPI, bool NORM>
+int launch_bgemm(const lf::BGemmArgs& a, hipStream_t st) {
+  const BShape sh = bgemm_shape(a.rows, a.K);
+  void* args[] = {const_cast<lf::BGemmArgs*>(&a)};
+  (void)hipLaunchKernel(bgemm_fn<EPI, NORM>(sh), dim3(sh.blocks), dim3(8 * lf::kWave), args, 0, st);
+  return sh.blocks;  // partial sums of squares a residual GEMM writes per sequence
+}
+
+template <int HD, int G>
+const void* battn_fn(int u) {
+  return u == 4   ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 4>)
+         : u == 8 ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 8>)
+                  : reinterpret_cast<const void*>(&lf::k_battn<HD, G, 16>);
+}
+const void* battn_kernel(int hd, int G, int u) {
+#define LF_BATTN_CASE(H, GG) if (hd == H && G == GG) return battn_fn<H, GG>(u);
+  LF_BATTN_CASE(32, 1) LF_BATTN_CASE(32, 2) LF_BATTN_CASE(32, 4)
+  LF_BATTN_CASE(64, 1) LF_BATTN_CASE(64, 2) LF_BATTN_CASE(64, 4)
+  LF_BATTN_CASE(128, 1) LF_BATTN_CASE(128, 2) LF_BATTN_CASE(128, 4)
+#undef LF_BATTN_CASE
+  return nullptr;
+}
+
+// Enqueue every kernel of one batched step of the n sequences kvs[0..n).
+int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
+  const Dims& D = m->D;
+  const WsLayout& W = m->W;
+  const lf_config& c = m->cfg;
+  const size_t layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
+  lf::BatchSeqs q{};
+  for (int i = 0; i < n; ++i) {
+    q.state[i] = kvs[i]->state();
+    q.tokens[i] = kvs[i]->tokens();
+    q.kc[i] = kvs[i]->kc();
+    q.vc[i] = kvs[i]->vc();
+    q.logits[i] = kvs[i]->logits();
+  }
+  float* x = m->at<float>(W.bx);
+  float* ss = m->at<float>(W.bss);
+  lf::BEmbedArgs ea{q, m->at<half_t>(W.embed), x, ss, D.d, D.V, D.ctx};
+  hipLaunchKernelGGL(lf::k_bembed, dim3(n), dim3(lf::kBlock), 0, st, ea);
+  int ss_n = 1;
+
+  lf::BGemmArgs base{};
+  base.eps = c.rms_eps;
+  base.n = n;
+  base.seq = q;
+  base.layer_cache = layer_cache;
+  base.rope = m->at<float2>(W.rope);
+  base.hd = D.hd;
+  base.qpl = D.qpl;
+  base.kpl = D.kpl;
+  base.max_ctx = D.ctx;
+  base.ss = ss;
+  base.ss_out = ss;
+  for (int l = 0; l < D.L; ++l) {
+    lf::BGemmArgs a = base;
+    a.layer = l;
+    a.W = m->at<half_t>(W.wqkv[l]);
+    a.rows = D.qkv_rows;
+    a.K = D.d;
+    a.X = x;
+    a.x_stride = D.d;
+    a.gain = m->at<half_t>(W.g1[l]);
+    a.ss_n = ss_n;
+    a.y = m->at<float>(W.bq);
+    a.y_stride = D.qdim;
+    launch_bgemm<lf::kBEpiQKV, true>(a, st);
+
+    const AttnPlan P = attn_plan(c, l);
+    lf::AttnBArgs b{};
+    b.a.t.max_ctx = D.ctx;
+    b.a.t.window = c.window[l];
+    b.a.t.S = P.S;
+    b.a.t.chunk = P.chunk;
+    b.a.t.kpl = D.kpl;
+    b.a.t.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)));
+    b.a.abort = m->at<unsigned>(W.abort);
+    b.a.S_max = W.S_max;
+    b.a.n_kv = D.hkv;
+    b.seq = q;
+    b.layer_cache = layer_cache;
+    b.layer = l;
+    b.q = m->at<float>(W.bq);
+    b.o = m->at<float>(W.bo);
+    b.part = m->at<lf::u64>(W.bpart);
+    b.part_stride = static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2);
+    b.epochs = m->at<unsigned>(W.bepochs);
+    b.q_dim = D.qdim;
+    {
+      void* args[] = {&b};
+      (void)hipLaunchKernel(battn_kernel(D.hd, D.G, attn_loads_per_lane(P.chunk, D.hd)), dim3(P.S, D.hkv, n),
+                            dim3(lf::kBlock), args, 0, st);
+    }
+
+    a = base;
+    a.layer = l;
+    a.W = m->at<half_t>(W.wo[l]);
+    a.rows = D.d;
+    a.K = D.qdim;
+    a.X = m->at<float>(W.bo);
+    a.x_stride = D.qdim;
+    a.y = x;
+    a.y_stride = D.d;
+    ss_n = launch_bgemm<lf::kBEpiResid, false>(a, st);
+
+    a = base;
+    a.layer = l;
+    a.W = m->at<half_t>(W.wgu[l]);
+    a.rows = 2 * D.ffn;
+    a.K = D.d;
+    a.X = x;
+    a.x_stride = D.d;
+    a.gain = m->at<half_t>(W.g2[l]);
+    a.ss_n = ss_n;
+    a.y = m->at<float>(W.ba);
+    a.y_stride = D.ffn;
+    launch_bgemm<lf::kBEpiSwiGLU, true>(a, st);
+
+    a = base;
+    a.layer = l;
+    a.W = m->at<half_t>(W.wd[l]);
+    a.rows = D.d;
+    a.K = D.ffn;
+    a.X = m->at<float>(W.ba);
+    a.x_stride = D.ffn;
+    a.y = x;
+    a.y_stride = D.d;
+    ss_n = launch_bgemm<lf::kBEpiResid, false>(a, st);
+  }
+  lf::BGemmArgs a = base;
+  a.W = m->at<half_t>(W.lm);
+  a.rows = D.V;
+  a.K = D.d;
+  a.X = x;
+  a.x_stride = D.d;
+  a.gain = m->at<half_t>(W.gf);
+  a.ss_n = ss_n;
+  a.counter = m->at<unsigned>(W.bcounter);
+  a.best = m->at<unsigned long long>(W.bbest);
+  launch_bgemm<lf::kBEpiLogits, true>(a, st);
+  LF_HIP(hipPeekAtLastError());
+  return LF_OK;
 }
 
 // Scratch of the batched prompt pass for chunks of mc positions.
@@ -964,6 +1183,12 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   // attention: split states are tagged with the kv head's epoch, which starts at 1
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.attn_epochs), 1u, size_t(D.hkv));
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.class_epochs), 1u, size_t(8));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bepochs), 1u,
+                     size_t(lf::kMaxBatch) * D.hkv);
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bbest), 0u, size_t(2 * lf::kMaxBatch));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bcounter), 0u, size_t(1));
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(64), dim3(256), 0, st, m->at<unsigned>(W.bx), 0u,
+                     (W.bss + lf::kMaxBatch * lf::kSsStride * sizeof(float) - W.bx) / sizeof(unsigned));
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return bail(fail(LF_EHIP, "model setup: %s", hipGetErrorString(e)));
@@ -1155,6 +1380,66 @@ int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream)
   const int rc = run_step(m, kv, nullptr, nullptr, st);
   if (rc) return rc;
   kv->len += 1;
+  return LF_OK;
+}
+
+int lf_decode_step_batch(lf_model* m, lf_kv* const* kvs, int32_t n, const int32_t* d_tokens, void* stream) {
+  if (!m || !kvs) return fail(LF_EINVAL, "null argument");
+  if (m->D.V == 0) return fail(LF_EINVAL, "lf_decode_step_batch needs vocab > 0");
+  if (n < 1 || n > LF_MAX_BATCH) return fail(LF_EINVAL, "n = %d out of [1, %d]", n, LF_MAX_BATCH);
+  for (int i = 0; i < n; ++i) {
+    lf_kv* kv = kvs[i];
+    if (!kv) return fail(LF_EINVAL, "sequence %d is null", i);
+    if (kv->m != m) return fail(LF_EINVAL, "sequence %d belongs to another model", i);
+    for (int j = 0; j < i; ++j)
+      if (kvs[j] == kv) return fail(LF_EINVAL, "sequence %d appears twice", i);
+    if (kv->len >= m->D.ctx) return fail(LF_ERANGE, "sequence %d is full (%d positions)", i, m->D.ctx);
+    if (!d_tokens && kv->len == 0) return fail(LF_EINVAL, "sequence %d has no previous position to take a greedy token from", i);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d_tokens) {
+    lf::BTokArgs t{};
+    for (int i = 0; i < n; ++i) {
+      t.seq.state[i] = kvs[i]->state();
+      t.seq.tokens[i] = kvs[i]->tokens();
+      t.len[i] = kvs[i]->len;
+    }
+    t.tokens = d_tokens;
+    t.n = n;
+    hipLaunchKernelGGL(lf::k_bset_tokens, dim3(1), dim3(64), 0, st, t);
+    LF_HIP(hipPeekAtLastError());
+  }
+  if (m->mode == LF_MODE_EAGER) {
+    const int rc = enqueue_batch_step(m, kvs, n, st);
+    if (rc) return rc;
+  } else {
+    hipGraphExec_t exec = nullptr;
+    for (const BatchGraph& g : m->batch_graphs) {
+      bool same = g.n == n;
+      for (int i = 0; same && i < n; ++i) same = g.kvs[i] == kvs[i];
+      if (same) exec = g.exec;
+    }
+    if (!exec) {
+      hipStream_t cs = m->capture_stream;
+      LF_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+      const int rc = enqueue_batch_step(m, kvs, n, cs);
+      hipGraph_t graph = nullptr;
+      const hipError_t e = hipStreamEndCapture(cs, &graph);
+      if (rc != LF_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+      }
+      if (e != hipSuccess) return fail(LF_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+      const hipError_t ei = hipGraphInstantiateWithFlags(&exec, graph, 0);
+      (void)hipGraphDestroy(graph);
+      if (ei != hipSuccess) return fail(LF_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(ei));
+      BatchGraph g{n, {}, exec};
+      for (int i = 0; i < n; ++i) g.kvs[i] = kvs[i];
+      m->batch_graphs.push_back(g);
+    }
+    LF_HIP(hipGraphLaunch(exec, st));
+  }
+  for (int i = 0; i < n; ++i) kvs[i]->len += 1;
   return LF_OK;
 }
 

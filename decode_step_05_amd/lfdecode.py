@@ -16,6 +16,7 @@ MAX_LAYERS = 64
 
 LF_OK, LF_EINVAL, LF_ERANGE, LF_EHIP = 0, -1, -2, -3
 LF_STATIC_SCRATCH_BYTES = 32 << 20
+LF_MAX_BATCH = 8
 LF_MODE_EAGER, LF_MODE_GRAPH = 0, 1
 
 # Every symbol include/lfdecode.h declares.
@@ -24,7 +25,7 @@ EXPORTS = (
     "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused", "lf_plan_attention",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_prefill_workspace_bytes", "lf_prefill_batched", "lf_prefill_batched_static",
-    "lf_decode_step", "lf_decode_steps", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
+    "lf_decode_step", "lf_decode_steps", "lf_decode_step_batch", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
     "lf_step_kernel_times", "lf_kernel_time", "lf_read_bandwidth", "lf_sample", "lf_last_error",
 )
 
@@ -85,6 +86,7 @@ def load():
         "lf_prefill_batched_static": (c_int, [P, P, P, c_int32, c_int32, P]),
         "lf_decode_step": (c_int, [P, P, P, P]),
         "lf_decode_steps": (c_int, [P, P, c_int32, P]),
+        "lf_decode_step_batch": (c_int, [P, POINTER(P), c_int32, P, P]),
         "lf_decode_step_hidden": (c_int, [P, P, P, P, P]),
         "lf_logits": (c_int, [P, P, P, P, P]),
         "lf_kv_status": (c_int, [P, POINTER(c_int32), P]),
@@ -269,6 +271,12 @@ def lf_decode_step(model, kv, token=None, stream=None) -> None:
 
 def lf_decode_steps(model, kv, n: int, stream=None) -> None:
     _check(load().lf_decode_steps(model, kv, int(n), _stream(stream)))
+
+
+def lf_decode_step_batch(model, kvs, tokens=None, stream=None) -> None:
+    """One step of each sequence handle in kvs (a list); tokens: device int32 [len(kvs)] or None."""
+    arr = (c_void_p * len(kvs))(*kvs)
+    _check(load().lf_decode_step_batch(model, arr, len(kvs), _ptr(tokens), _stream(stream)))
 
 
 def lf_decode_step_hidden(model, kv, x_in, x_out, stream=None) -> None:

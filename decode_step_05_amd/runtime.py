@@ -59,6 +59,15 @@ class Decoder:
     def sequence(self) -> "Sequence":
         return Sequence(self)
 
+    def step_batch(self, seqs, tokens=None, stream=None):
+        """One decode step of each sequence in seqs (lf_decode_step_batch);
+        tokens: None (each its own greedy token), a list of ints, or a device
+        int32 tensor [len(seqs)]."""
+        torch = _torch()
+        if tokens is not None and not torch.is_tensor(tokens):
+            tokens = torch.tensor([int(t) for t in tokens], dtype=torch.int32, device=self.device)
+        C.lf_decode_step_batch(self.handle, [q.handle for q in seqs], tokens, stream)
+
     def close(self):
         if getattr(self, "handle", None):
             C.lf_model_free(self.handle)

@@ -289,6 +289,30 @@ int lf_decode_step(lf_model* m, lf_kv* kv, const int32_t* d_token, void* stream)
 int lf_decode_steps(lf_model* m, lf_kv* kv, int32_t n, void* stream);
 
 /*
+ * Batched decode step: one decode step of each of n sequences of one model
+ * (1 <= n <= LF_MAX_BATCH), with every weight read from HBM once for all of
+ * them. The asector.ru summary ("Performance and infrastructure") proposes
+ * stochastic decoding scored as pass@N: N sampled continuations of one
+ * prompt, which is n sequences that step together. Each sequence keeps its
+ * own cache, length and token history, and after the call holds the logits
+ * and greedy argmax of its new position exactly as after lf_decode_step
+ * (lf_logits, lf_kv_status, lf_kv_tokens per sequence); the lengths may
+ * differ. d_tokens: device int32 [n], the token of each sequence's new
+ * position (e.g. drawn by lf_sample from the rows of lf_logits), or NULL to
+ * feed each sequence its own greedy token of the previous position.
+ * kvs: host array of n distinct sequence handles of model m.
+ * Numerics: the projections run on the matrix cores with each fp32
+ * activation split into two fp16 parts (hi = fp16(a), lo = fp16(a - hi)),
+ * fp32 accumulation; attention, softmax and logits in fp32 as in the
+ * single-sequence step. LF_EINVAL for null or repeated handles, n out of
+ * range, vocab == 0, or d_tokens NULL for an empty sequence; LF_ERANGE if a
+ * sequence is full. Graph mode records one hipGraph per (n, handles) and
+ * replays it. Enqueued on stream.
+ */
+#define LF_MAX_BATCH 8
+int lf_decode_step_batch(lf_model* m, lf_kv* const* kvs, int32_t n, const int32_t* d_tokens, void* stream);
+
+/*
  * Hidden mode (vocab == 0): append one position whose input hidden vector is
  * d_x_in (fp32 [d_model]) and write the last layer's output residual to
  * d_x_out (fp32 [d_model]; may equal d_x_in).

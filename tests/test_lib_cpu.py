@@ -30,7 +30,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_sizes_of_the_workloads():
     # workspace = the weights once + the rotary table, activations and
-    # attention exchange buffers (a few MB); sequence buffer = caches + state
+    # attention exchange buffers (a few MB) + the batched step's buffers for
+    # 8 sequences (activations, partial sums, attention split states: about
+    # 20 MB); sequence buffer = caches + state
     for cfg in (TINY, LAYER_FULL, FULL, LANE):
         c = C.make_config(cfg)
         ws, kv = C.lf_workspace_bytes(c), C.lf_kv_bytes(c)
@@ -39,7 +41,7 @@ def test_sizes_of_the_workloads():
     cache = 2 * 15 * 4096 * 16 * 128 * 2
     assert cache <= C.lf_kv_bytes(c) < cache + 4096 * 4 + 32000 * 4 + 4096
     weights = 2338451456 * 2
-    assert weights <= C.lf_workspace_bytes(c) < weights + 8 * 2 ** 20
+    assert weights <= C.lf_workspace_bytes(c) < weights + 32 * 2 ** 20
 
 
 @pytest.mark.parametrize("field,value,msg", [
@@ -181,3 +183,11 @@ def test_attention_plan():
     layers = (ctypes.c_int32 * 15)()
     assert lib.lf_plan_attention(ctypes.byref(c), 0, 8, 1, 1, ctypes.byref(one), layers) == C.LF_EINVAL
     assert lib.lf_plan_attention(ctypes.byref(c), 256, 8, 1, 1, None, layers) == C.LF_EINVAL
+
+
+def test_batch_step_argument_errors_before_any_device_call():
+    lib = C.load()
+    arr = (ctypes.c_void_p * 9)()
+    assert lib.lf_decode_step_batch(None, arr, 1, None, None) == C.LF_EINVAL
+    assert lib.lf_decode_step_batch(0x1000, None, 1, None, None) == C.LF_EINVAL
+    assert C.LF_MAX_BATCH == 8
