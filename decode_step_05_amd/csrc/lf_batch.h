@@ -14,15 +14,17 @@
 // part, column 8 + s its lo part, and the row's result is the sum of the two
 // columns. Lane l holds, of its operands, weight row l % 16 and column
 // l % 16 with the 8 consecutive k of group l / 16; of the result, column
-// l % 16 and rows 4 (l / 16) .. 4 (l / 16) + 3. Each wave builds its
-// activation operand from the fp32 vectors directly (no LDS staging), and
-// the 8 waves of a workgroup split K; their partial results are summed in
-// LDS in a fixed order.
+// l % 16 and rows 4 (l / 16) .. 4 (l / 16) + 3. Every kernel that produces
+// a projection's input (the embedding gather, attention, the residual and
+// SwiGLU epilogues) writes it already in that operand layout (frag_index),
+// split and, for a normalised input, multiplied by the gain, so each lane of
+// the projection loads one 16-byte operand piece per k-step. The 8 waves of
+// a workgroup split K; their partial results are summed in LDS in a fixed
+// order.
 //
-// RMSNorm: the producer of a normalised input (the embedding gather, the O
-// and down projections) also writes, per workgroup, the partial sums of
-// squares of the new residual; the consumer sums them in a fixed order and
-// applies 1/sqrt(mean + eps) to its outputs, the gain to its inputs.
+// RMSNorm: the producer of a normalised input also writes, per workgroup,
+// the partial sums of squares of the new residual; the consumer sums them in
+// a fixed order and scales its outputs by 1/sqrt(mean + eps).
 #pragma once
 #include "lf_kernels.h"
 
@@ -62,18 +64,18 @@ enum BEpi : int { kBEpiQKV = 0, kBEpiSwiGLU = 1, kBEpiResid = 2, kBEpiLogits = 3
 struct BGemmArgs {
   const half_t* W;     // [rows, K] fp16 (QKV and gate/up rows repacked as for the batch-1 kernels)
   int rows, K;         // K a multiple of 8
-  const float* X;      // input of sequence s: X + s * x_stride, fp32 [K]
-  int x_stride;
-  const half_t* gain;  // RMSNorm gain [K] if the input is normalised
-  const float* ss;     // ... and the partial sums of squares of the input, [kMaxBatch][kSsStride]
-  int ss_n;            // partials per sequence (<= kSsMax)
+  const half_t* B;     // the input as the instruction's operand (frag_index), gain applied; zero past K
+  const float* ss;     // normalised input: partial sums of squares of the raw input, [kMaxBatch][kSsStride]
+  int ss_n;            // partials per sequence (<= kSsMax); 0: the input is not normalised
   float eps;
   int n;               // sequences (1 .. kMaxBatch)
   BatchSeqs seq;
   size_t layer_cache;  // elements between two layers' caches
   int layer;
-  float* y;            // QKV: queries [s][q_dim]; residual: x [s][rows] (+=); SwiGLU: [s][rows / 2]
+  float* y;            // QKV: queries [s][q_dim]; residual: x [s][rows] (+=)
   int y_stride;
+  half_t* frag_out;    // residual, SwiGLU: the output as the next projection's operand
+  const half_t* next_gain;  // residual: RMSNorm gain of the next projection's input [rows]
   float* ss_out;       // residual: partial sums of squares of the new residual [kMaxBatch][kSsStride]
   const float2* rope;  // (cos, sin) [max_ctx][hd / 2]
   int hd, qpl, kpl, max_ctx;
@@ -113,16 +115,17 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
-// Weights and inputs of KB k-steps (32 k each) of one wave.
-template <int KB, int TPW, bool NORM>
+// Weight and operand loads of KB k-step slots of one wave.
+template <int KB, int TPW>
 struct BBatch {
   u32x4 w[KB][TPW];
-  f32x4 x[KB][2];
-  u32x4 gn[NORM ? KB : 1];
+  u32x4 b[KB];
 };
 
-// Workgroup: TPW tiles of 16 rows, 8 waves each taking an eighth of the
-// k-steps; a wave's k-steps are loaded KB at a time, two batches in flight.
+// Workgroup: TPW tiles of 16 rows and all K. Its 8 waves take the k-steps in
+// turn (wave w: k-steps w, w + 8, ...), so the workgroup streams each row as
+// one moving window; a wave loads KB of its k-steps at a time, two batches in
+// flight, and the waves' partial results are summed in LDS.
 template <int EPI, int TPW, bool NORM, int KB>
 __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   constexpr int NW = 8;
@@ -134,17 +137,16 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   __shared__ int flag;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int g = lane >> 4, col = lane & 15;
-  const int s_in = min(col & 7, a.n - 1);  // the sequence whose input this lane's column holds
-  const bool lo_col = col >= 8;
   const int nks = (a.K + 31) >> 5;
-  const int per = (nks + NW - 1) / NW;       // k-steps per wave
-  const int ks0 = wave * per, ks1 = min(nks, ks0 + per);
+  const int J = (nks + NW - 1) / NW;  // k-step slots per wave: slot j is k-step wave + 8 j (if < nks)
   const int ntiles = (a.rows + 15) >> 4, tile0 = blockIdx.x * TPW;
 
   int pos[kMaxBatch];
   if constexpr (EPI == kBEpiQKV || EPI == kBEpiLogits) batch_positions(a.seq, a.n, pos);
-  // partial sums of squares of sequence `wave`, loaded before the weights
-  // (a wave's loads complete in issue order) and summed at the end
+  // Loaded before the weights (a wave's loads complete in issue order): the
+  // partial sums of squares of sequence `wave` (summed at the end), and what
+  // the epilogue reads. Wave t < TPW finishes tile tile0 + t; lane (g, col)
+  // holds rows 16 tile + 4 g + r (r < 4) of sequence col.
   float ssv[kSsMax / kWave];
   if constexpr (NORM) {
 #pragma unroll
@@ -153,24 +155,21 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
       ssv[j] = (wave < a.n && i < a.ss_n) ? a.ss[wave * kSsStride + i] : 0.f;
     }
   }
-
-  // what the epilogue reads, loaded before the weights too: wave t < TPW
-  // finishes tile tile0 + t, lane (g, col) rows 16 tile + 4 g + r (r < 4) of
-  // sequence col: their residual values, or their rotary angles
   const bool epi = wave < TPW && tile0 + wave < ntiles;
   const int s = col;
   const bool act = epi && s < a.n;
   const int row0 = 16 * (tile0 + wave) + 4 * g;
   f32x4 xres = {0.f, 0.f, 0.f, 0.f};
+  float gnext[4] = {0.f, 0.f, 0.f, 0.f};
   float2 cs[2] = {{1.f, 0.f}, {1.f, 0.f}};
   if constexpr (EPI == kBEpiResid) {
     if (act) {
       const float* xp = a.y + static_cast<size_t>(s) * a.y_stride;
-      if (row0 + 3 < a.rows) {
-        xres = *reinterpret_cast<const f32x4*>(xp + row0);
-      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xres[r] = row0 + r < a.rows ? xp[row0 + r] : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(row0 + r, a.rows - 1);
+        xres[r] = xp[row];
+        gnext[r] = static_cast<float>(a.next_gain[row]);
       }
     }
   } else if constexpr (EPI == kBEpiQKV) {
@@ -183,88 +182,65 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
       }
     }
   }
-
   __builtin_amdgcn_sched_barrier(0);
+
   const half_t* wr[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
     wr[t] = a.W + static_cast<size_t>(min(16 * min(tile0 + t, ntiles - 1) + col, a.rows - 1)) * a.K;
-  const float* xr = a.X + static_cast<size_t>(s_in) * a.x_stride;
-
-  // k-steps past this wave's range load the range's last k-step again (an
-  // L2 hit, no new HBM traffic) and are masked where used; so are k-groups
-  // past K (K is a multiple of 8: a group is wholly in or out)
-  auto issue = [&](BBatch<KB, TPW, NORM>& b, int kb) {
+  // slots past this wave's last k-step load that k-step again (an L2 hit)
+  // and are masked where used; k-groups past K load a clamped address, and
+  // the operand is zero there
+  const int ks_last = wave + NW * (J - 1) < nks ? wave + NW * (J - 1) : wave + NW * ((nks - 1 - wave) / NW);
+  auto issue = [&](BBatch<KB, TPW>& b, int j0) {
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      const int ks = min(kb + j, ks1 - 1);
+      const int ks = min(wave + NW * (j0 + j), ks_last);
       const int k = min(ks * 32 + 8 * g, a.K - 8);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) b.w[j][t] = ld_stream(wr[t] + k);
-      b.x[j][0] = *reinterpret_cast<const f32x4*>(xr + k);
-      b.x[j][1] = *reinterpret_cast<const f32x4*>(xr + k + 4);
-      if constexpr (NORM) b.gn[j] = ld16(a.gain + k);
+      b.b[j] = ld16(a.B + (static_cast<size_t>(ks) * kWave + lane) * 8);
     }
   };
   f32x4 acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const BBatch<KB, TPW, NORM>& b, int kb) {
+  auto compute = [&](const BBatch<KB, TPW>& b, int j0) {
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      const int ks = kb + j;
-      const bool valid = ks < ks1 && ks * 32 + 8 * g < a.K;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = b.x[j][0][e];
-        v[4 + e] = b.x[j][1][e];
-      }
-      if constexpr (NORM) {
-        float gf[8];
-        unpack8(b.gn[j], gf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= gf[e];
-      }
-      h8 frag;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const half_t hi = static_cast<half_t>(v[e]);
-        const half_t lo = static_cast<half_t>(v[e] - static_cast<float>(hi));
-        frag[e] = valid ? (lo_col ? lo : hi) : static_cast<half_t>(0.f);
-      }
+      const bool valid = wave + NW * (j0 + j) < nks;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const h8 frag = __builtin_bit_cast(h8, valid ? b.b[j] : z);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, b.w[j][t]), frag, acc[t], 0, 0, 0);
     }
   };
-  // two batches in flight, in a loop without any condition on an issue (one
-  // makes the compiler wait for every load before it) and a peeled last pair.
-  // The batch count is rounded up to even: with an odd count the last batch
-  // repeats the range's last k-step (L2 hits, masked); the host picks KB so
-  // that the count is even where it can. The scheduling barriers keep each
-  // batch's loads together, ahead of the other batch's arithmetic (the
-  // scheduler would otherwise move loads next to their uses and leave few in
-  // flight).
-  const int nb = ((per + KB - 1) / KB + 1) & ~1;
-  BBatch<KB, TPW, NORM> b0, b1;
-  issue(b0, ks0);
+  // Two batches in flight, in a loop without any condition on an issue (one
+  // makes the compiler wait for every load before it) and a peeled last pair;
+  // the batch count is rounded up to even (an extra batch repeats the last
+  // k-step, masked). The scheduling barriers keep each batch's loads
+  // together, ahead of the other batch's arithmetic (the scheduler would
+  // otherwise move loads next to their uses and leave few in flight).
+  const int nb = ((J + KB - 1) / KB + 1) & ~1;
+  BBatch<KB, TPW> b0, b1;
+  issue(b0, 0);
   int i = 0;
   for (; i + 2 < nb; i += 2) {
-    issue(b1, ks0 + (i + 1) * KB);
+    issue(b1, (i + 1) * KB);
     __builtin_amdgcn_sched_barrier(0);
-    compute(b0, ks0 + i * KB);
+    compute(b0, i * KB);
     __builtin_amdgcn_sched_barrier(0);
-    issue(b0, ks0 + (i + 2) * KB);
+    issue(b0, (i + 2) * KB);
     __builtin_amdgcn_sched_barrier(0);
-    compute(b1, ks0 + (i + 1) * KB);
+    compute(b1, (i + 1) * KB);
     __builtin_amdgcn_sched_barrier(0);
   }
-  issue(b1, ks0 + (i + 1) * KB);
+  issue(b1, (i + 1) * KB);
   __builtin_amdgcn_sched_barrier(0);
-  compute(b0, ks0 + i * KB);
+  compute(b0, i * KB);
   __builtin_amdgcn_sched_barrier(0);
-  compute(b1, ks0 + (i + 1) * KB);
+  compute(b1, (i + 1) * KB);
 
   // sum the waves' partial results in LDS (fixed order); the norm scale
 #pragma unroll
@@ -280,7 +256,6 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   }
   lds_barrier();
 
-  // wave t < TPW finishes tile tile0 + t
   float y[4] = {0.f, 0.f, 0.f, 0.f};
   if (epi) {
 #pragma unroll
@@ -291,9 +266,9 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
       y[r] = v + lane_xor(v, 8);  // hi column + lo column
     }
   }
+  const float sc = NORM && act ? rs[s] : 1.f;
   if constexpr (EPI == kBEpiQKV) {
     if (act) {
-      const float sc = NORM ? rs[s] : 1.f;
       const int p = pick(pos, s);
 #pragma unroll
       for (int r = 0; r < 4; r += 2)
@@ -301,25 +276,33 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
     }
   } else if constexpr (EPI == kBEpiSwiGLU) {
     if (act) {
-      const float sc = NORM ? rs[s] : 1.f;
+      float v[2];
 #pragma unroll
-      for (int r = 0; r < 4; r += 2)
-        if (row0 + r < a.rows) {
-          const float gt = y[r] * sc, up = y[r + 1] * sc;
-          a.y[static_cast<size_t>(s) * a.y_stride + ((row0 + r) >> 1)] = gt / (1.0f + expf(-gt)) * up;
-        }
+      for (int h = 0; h < 2; ++h) {
+        const float gt = y[2 * h] * sc, up = y[2 * h + 1] * sc;
+        v[h] = gt / (1.0f + expf(-gt)) * up;
+      }
+      // rows = 2 ffn, a multiple of 16: a lane's four rows exist together
+      if (row0 < a.rows) put_frag2(a.frag_out, row0 >> 1, s, v[0], v[1]);
     }
   } else if constexpr (EPI == kBEpiResid) {
     float sq = 0.f;
     if (act) {
       float* xp = a.y + static_cast<size_t>(s) * a.y_stride + row0;
+      float xn[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        xn[r] = xres[r] + y[r];
         if (row0 + r < a.rows) {
-          const float xn = xres[r] + y[r];
-          xp[r] = xn;
-          sq = fmaf(xn, xn, sq);
+          xp[r] = xn[r];
+          sq = fmaf(xn[r], xn[r], sq);
         }
+      }
+      // rows = d_model, a multiple of 8: a lane's four rows exist together
+      if (row0 < a.rows) {
+        put_frag2(a.frag_out, row0, s, xn[0] * gnext[0], xn[1] * gnext[1]);
+        put_frag2(a.frag_out, row0 + 2, s, xn[2] * gnext[2], xn[3] * gnext[3]);
+      }
     }
     if (wave < TPW) {
       sq += lane_xor(sq, 16);
@@ -336,7 +319,6 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   } else {  // kBEpiLogits
     unsigned long long key = 0;
     if (act) {
-      const float sc = NORM ? rs[s] : 1.f;
       float* z = a.seq.logits[s];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -378,14 +360,17 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
 
 struct BEmbedArgs {
   BatchSeqs seq;
-  const half_t* emb;  // [vocab, d]
-  float* x;           // residual [s][d]
-  float* ss;          // partial sums of squares [kMaxBatch][kSsStride] (one partial per sequence)
+  const half_t* emb;   // [vocab, d]
+  const half_t* gain;  // RMSNorm gain of layer 0's QKV input [d]
+  float* x;            // residual [s][d]
+  half_t* frag;        // layer 0's QKV operand (frag_index)
+  float* ss;           // partial sums of squares [kMaxBatch][kSsStride] (one partial per sequence)
   int d, vocab, max_ctx;
 };
 
 // Workgroup s: the embedding row of sequence s's token at its position, as
-// the fp32 residual, and its sum of squares.
+// the fp32 residual and as the gain-scaled operand of layer 0's QKV
+// projection, and its sum of squares.
 __global__ __launch_bounds__(kBlock) void k_bembed(BEmbedArgs a) {
   __shared__ float red[kWavesPerBlock];
   const int s = blockIdx.x;
@@ -400,10 +385,12 @@ __global__ __launch_bounds__(kBlock) void k_bembed(BEmbedArgs a) {
   const half_t* e = a.emb + static_cast<size_t>(tok) * a.d;
   float* x = a.x + static_cast<size_t>(s) * a.d;
   float sq = 0.f;
-  for (int i = threadIdx.x; i < a.d; i += kBlock) {
-    const float v = static_cast<float>(e[i]);
-    x[i] = v;
-    sq = fmaf(v, v, sq);
+  for (int i = 2 * threadIdx.x; i < a.d; i += 2 * kBlock) {  // d is a multiple of 8
+    const float v0 = static_cast<float>(e[i]), v1 = static_cast<float>(e[i + 1]);
+    x[i] = v0;
+    x[i + 1] = v1;
+    put_frag2(a.frag, i, s, v0 * static_cast<float>(a.gain[i]), v1 * static_cast<float>(a.gain[i + 1]));
+    sq = fmaf(v0, v0, fmaf(v1, v1, sq));
   }
   sq = block_sum(sq, red);
   if (threadIdx.x == 0) a.ss[s * kSsStride] = sq;
@@ -415,7 +402,7 @@ struct AttnBArgs {
   size_t layer_cache;
   int layer;
   const float* q;       // queries [s][q_dim]
-  float* o;             // outputs [s][q_dim]
+  half_t* ofrag;        // outputs, as the O projection's operand (frag_index; column s)
   u64* part;            // split states, per sequence part_stride words
   size_t part_stride;
   unsigned* epochs;     // [s][n_kv]
@@ -425,7 +412,8 @@ struct AttnBArgs {
 // Attention of work item (split blockIdx.x, kv head blockIdx.y) of sequence
 // blockIdx.z: k_attn's two-dimensional layout (the splits of a kv head are
 // consecutive workgroups), with the sequence's cache, position, queries,
-// outputs, split states and epochs.
+// split states and epochs; the outputs go to column s of the O projection's
+// operand.
 template <int HD, int G, int U>
 __global__ __launch_bounds__(kBlock) void k_battn(AttnBArgs b) {
   __shared__ AttnXSmem<HD, G> sm;
@@ -436,7 +424,8 @@ __global__ __launch_bounds__(kBlock) void k_battn(AttnBArgs b) {
   a.t.vc = b.seq.vc[s] + b.layer_cache * b.layer;
   a.t.state = b.seq.state[s];
   a.part = b.part + b.part_stride * s;
-  a.o = b.o + static_cast<size_t>(s) * b.q_dim;
+  a.ofrag = b.ofrag;
+  a.fcol = s;
   a.epochs = b.epochs + static_cast<size_t>(s) * a.n_kv;
   attn_item<HD, G, U, false>(a, blockIdx.x, blockIdx.y, sm);
 }

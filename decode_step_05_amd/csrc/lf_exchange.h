@@ -69,6 +69,24 @@ struct SPoll {
   }
 };
 
+// Operand of the batched projections' matrix instructions (16x16x32): per
+// k-step of 32 k, 64 lanes of 8 fp16; lane 16 g + c holds k-group g (k
+// 8g .. 8g + 7 of the step) of column c, where column s < 8 is the hi part
+// of sequence s's value and column 8 + s its lo part. Half index of
+// (k, column):
+__device__ __forceinline__ int frag_index(int k, int col) {
+  return (((k >> 5) * 64 + ((k >> 3) & 3) * 16 + col) << 3) + (k & 7);
+}
+// Store values v0, v1 at k, k + 1 (k even) of sequence s as hi and lo parts.
+__device__ __forceinline__ void put_frag2(half_t* f, int k, int s, float v0, float v1) {
+  typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+  const half_t h0 = static_cast<half_t>(v0), h1 = static_cast<half_t>(v1);
+  const hh2 hi = {h0, h1};
+  const hh2 lo = {static_cast<half_t>(v0 - static_cast<float>(h0)), static_cast<half_t>(v1 - static_cast<float>(h1))};
+  *reinterpret_cast<hh2*>(f + frag_index(k, s)) = hi;
+  *reinterpret_cast<hh2*>(f + frag_index(k, s + 8)) = lo;
+}
+
 // Fold softmax state (m2, l2, a0, a1) into (M, L, A0, A1): maxima in log2
 // units; a state with maximum -inf holds nothing.
 __device__ __forceinline__ void fold_state(float& M, float& L, float& A0, float& A1, float m2, float l2, float a0,
@@ -93,10 +111,13 @@ __device__ __forceinline__ void fold_state(float& M, float& L, float& A0, float&
 // (max, denominator, outputs) state, and the groups are folded by lane
 // shuffles. Every load of a batch is issued before the first is waited for,
 // so a batch whose states have landed costs one round trip. Returns false if
-// the launch was aborted.
+// the launch was aborted. frag (untagged only): store the outputs instead as
+// column fcol of a matrix-core operand, split into fp16 hi and lo parts
+// (frag_index), for a batched projection.
 template <int HD, int G, bool TAGGED = true>
 __device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int n_kv, int S_max, int kvh, int si,
-                                                 int S, unsigned tag_part, unsigned tag_att, SPoll& poll, int lane) {
+                                                 int S, unsigned tag_part, unsigned tag_att, SPoll& poll, int lane,
+                                                 half_t* frag = nullptr, int fcol = 0) {
   constexpr int ST = HD + 2;  // tagged words per (head, split)
   constexpr int NE = G * HD;  // outputs of the kv head's query heads
   const int per = ((NE + S - 1) / S + 1) & ~1;
@@ -166,6 +187,8 @@ __device__ __forceinline__ bool attn_merge_share(const u64* part, void* out, int
       if constexpr (TAGGED) {
         put_t(ro, head * HD + d, A0 / L, tag_att);
         put_t(ro, head * HD + d + 1, A1 / L, tag_att);
+      } else if (frag) {
+        put_frag2(frag, head * HD + d, fcol, A0 / L, A1 / L);
       } else {
         *reinterpret_cast<float2*>(static_cast<float*>(out) + head * HD + d) = make_float2(A0 / L, A1 / L);
       }

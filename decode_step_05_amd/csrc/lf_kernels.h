@@ -786,6 +786,8 @@ struct AttnXArgs {
   unsigned* epochs;   // [Hkv] launch epoch per kv head (>= 1): the tag of its split states
   unsigned* abort;    // raised when a wait gives up; later waits give up at once
   int S_max, n_kv;
+  half_t* ofrag;      // if set: the outputs go here as column fcol of a batched projection's operand (not to o)
+  int fcol;
 };
 
 template <int HD, int G>
@@ -857,7 +859,8 @@ __device__ __forceinline__ void attn_item(const AttnXArgs& a, int si, int kvh, A
   attn_store_state<HD, G, NW, XCD>(m, l, acc, sm.cb, a.part, a.n_kv, a.S_max, kvh, si, epoch);
   if (wave == 0) {
     SPoll poll{a.abort, 0u};
-    attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, kvh, si, a.t.S, epoch, epoch, poll, lane);
+    attn_merge_share<HD, G, false>(a.part, a.o, a.n_kv, a.S_max, kvh, si, a.t.S, epoch, epoch, poll, lane, a.ofrag,
+                                   a.fcol);
     if (si == 0 && lane == 0) a.epochs[kvh] = epoch + 1 == 0 ? 1u : epoch + 1;
   }
 }

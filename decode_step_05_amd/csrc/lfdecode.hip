@@ -149,7 +149,7 @@ struct WsLayout {
   size_t class_epochs;  // QKV fused with attention: epoch per XCD class
   // batched step (lf_decode_step_batch): per-sequence activations, partial
   // sums of squares, greedy keys, split states and epochs
-  size_t bx, bq, bo, ba, bss, bbest, bcounter, bpart, bepochs;
+  size_t bx, bq, bfd, bfq, bff, bss, bbest, bcounter, bpart, bepochs;
   int S_max;
 };
 
@@ -193,8 +193,11 @@ WsLayout ws_layout(const lf_config& c) {
   const size_t B = lf::kMaxBatch;
   W.bx = take(B * D.d * sizeof(float));
   W.bq = take(B * D.qdim * sizeof(float));
-  W.bo = take(B * D.qdim * sizeof(float));
-  W.ba = take(B * D.ffn * sizeof(float));
+  // projection operands (frag_index): per k-step of 32, 64 lanes of 8 fp16
+  auto frag_bytes = [](int K) { return static_cast<size_t>((K + 31) / 32) * 64 * 8 * sizeof(half_t); };
+  W.bfd = take(frag_bytes(D.d));
+  W.bfq = take(frag_bytes(D.qdim));
+  W.bff = take(frag_bytes(D.ffn));
   W.bss = take(B * lf::kSsStride * sizeof(float));
   W.bbest = take(B * sizeof(unsigned long long));
   W.bcounter = take(sizeof(unsigned));
@@ -704,32 +707,24 @@ void drop_graphs(lf_model* m, lf_kv* kv) {
 // ------------------------------------------------------------ batched step
 
 // Launch shape of a skinny GEMM: TPW tiles of 16 rows per workgroup (the
-// largest of 4, 2, 1 that still gives 256 workgroups, one per CU), and KB
-// k-steps per batch of loads: 4, or 2 where that makes the number of batches
-// per wave even (the kernel rounds it up to even) or TPW is 4 (registers).
+// largest of 4, 2, 1 that still gives 256 workgroups, one per CU) and KB
+// k-steps per batch of loads: 8 KB of weights per wave and batch where the
+// grid fits one workgroup per CU, half that where it is larger, so that two
+// workgroups fit per CU (fewer registers) and the whole grid is resident at
+// once.
 struct BShape {
   int tpw, kb, blocks;
 };
-BShape bgemm_shape(int rows, int K) {
+BShape bgemm_shape(int rows) {
   const int tiles = (rows + 15) / 16;
-  BShape sh{1, 4, tiles};
-  for (int t : {4, 2}) {
-    const int b = (tiles + t - 1) / t;
-    if (b >= 256) {
-      sh = {t, 4, b};
+  int tpw = 1;
+  for (int t : {4, 2})
+    if ((tiles + t - 1) / t >= 256) {
+      tpw = t;
       break;
     }
-  }
-  const int per = ((K + 31) / 32 + 7) / 8;  // k-steps per wave (8 waves)
-  if (sh.tpw == 4 || ((per + 3) / 4) % 2) sh.kb = 2;
-  return sh;
-}
-
-template <int EPI, bool NORM, int KB>
-const void* bgemm_fn_kb(int tpw) {
-  if (tpw == 4) return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, 4, NORM, KB>);
-  if (tpw == 2) return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, 2, NORM, KB>);
-  return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, 1, NORM, KB>);
+  const int blocks = (tiles + tpw - 1) / tpw;
+  return {tpw, (blocks > 256 ? 4 : 8) / tpw, blocks};
 }
 
 template <int EPI, bool NORM>
@@ -737,14 +732,16 @@ const void* bgemm_fn(const BShape& sh) {
   if constexpr (EPI == lf::kBEpiResid && NORM) {
     return nullptr;  // a residual GEMM's input (attention output, SwiGLU) is never normalised
   } else {
-    if (sh.kb == 2 || sh.tpw == 4) return bgemm_fn_kb<EPI, NORM, 2>(sh.tpw);
-    return bgemm_fn_kb<EPI, NORM, 4>(sh.tpw);
+#define LF_BGEMM(T, KB) if (sh.tpw == T && sh.kb == KB) return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, T, NORM, KB>);
+    LF_BGEMM(1, 8) LF_BGEMM(1, 4) LF_BGEMM(2, 4) LF_BGEMM(2, 2) LF_BGEMM(4, 2) LF_BGEMM(4, 1)
+#undef LF_BGEMM
+    return nullptr;
   }
 }
 
 template <int EPI, bool NORM>
 int launch_bgemm(const lf::BGemmArgs& a, hipStream_t st) {
-  const BShape sh = bgemm_shape(a.rows, a.K);
+  const BShape sh = bgemm_shape(a.rows);
   void* args[] = {const_cast<lf::BGemmArgs*>(&a)};
   (void)hipLaunchKernel(bgemm_fn<EPI, NORM>(sh), dim3(sh.blocks), dim3(8 * lf::kWave), args, 0, st);
   return sh.blocks;  // partial sums of squares a residual GEMM writes per sequence
@@ -781,7 +778,10 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
   }
   float* x = m->at<float>(W.bx);
   float* ss = m->at<float>(W.bss);
-  lf::BEmbedArgs ea{q, m->at<half_t>(W.embed), x, ss, D.d, D.V, D.ctx};
+  half_t* fd = m->at<half_t>(W.bfd);
+  half_t* fq = m->at<half_t>(W.bfq);
+  half_t* ff = m->at<half_t>(W.bff);
+  lf::BEmbedArgs ea{q, m->at<half_t>(W.embed), m->at<half_t>(W.g1[0]), x, fd, ss, D.d, D.V, D.ctx};
   hipLaunchKernelGGL(lf::k_bembed, dim3(n), dim3(lf::kBlock), 0, st, ea);
   int ss_n = 1;
 
@@ -803,9 +803,7 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     a.W = m->at<half_t>(W.wqkv[l]);
     a.rows = D.qkv_rows;
     a.K = D.d;
-    a.X = x;
-    a.x_stride = D.d;
-    a.gain = m->at<half_t>(W.g1[l]);
+    a.B = fd;
     a.ss_n = ss_n;
     a.y = m->at<float>(W.bq);
     a.y_stride = D.qdim;
@@ -826,7 +824,7 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     b.layer_cache = layer_cache;
     b.layer = l;
     b.q = m->at<float>(W.bq);
-    b.o = m->at<float>(W.bo);
+    b.ofrag = fq;
     b.part = m->at<lf::u64>(W.bpart);
     b.part_stride = static_cast<size_t>(D.hq) * W.S_max * (D.hd + 2);
     b.epochs = m->at<unsigned>(W.bepochs);
@@ -842,10 +840,11 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     a.W = m->at<half_t>(W.wo[l]);
     a.rows = D.d;
     a.K = D.qdim;
-    a.X = m->at<float>(W.bo);
-    a.x_stride = D.qdim;
+    a.B = fq;
     a.y = x;
     a.y_stride = D.d;
+    a.frag_out = fd;
+    a.next_gain = m->at<half_t>(W.g2[l]);
     ss_n = launch_bgemm<lf::kBEpiResid, false>(a, st);
 
     a = base;
@@ -853,12 +852,9 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     a.W = m->at<half_t>(W.wgu[l]);
     a.rows = 2 * D.ffn;
     a.K = D.d;
-    a.X = x;
-    a.x_stride = D.d;
-    a.gain = m->at<half_t>(W.g2[l]);
+    a.B = fd;
     a.ss_n = ss_n;
-    a.y = m->at<float>(W.ba);
-    a.y_stride = D.ffn;
+    a.frag_out = ff;
     launch_bgemm<lf::kBEpiSwiGLU, true>(a, st);
 
     a = base;
@@ -866,19 +862,18 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     a.W = m->at<half_t>(W.wd[l]);
     a.rows = D.d;
     a.K = D.ffn;
-    a.X = m->at<float>(W.ba);
-    a.x_stride = D.ffn;
+    a.B = ff;
     a.y = x;
     a.y_stride = D.d;
+    a.frag_out = fd;
+    a.next_gain = m->at<half_t>(l + 1 < D.L ? W.g1[l + 1] : W.gf);
     ss_n = launch_bgemm<lf::kBEpiResid, false>(a, st);
   }
   lf::BGemmArgs a = base;
   a.W = m->at<half_t>(W.lm);
   a.rows = D.V;
   a.K = D.d;
-  a.X = x;
-  a.x_stride = D.d;
-  a.gain = m->at<half_t>(W.gf);
+  a.B = fd;
   a.ss_n = ss_n;
   a.counter = m->at<unsigned>(W.bcounter);
   a.best = m->at<unsigned long long>(W.bbest);
@@ -1187,6 +1182,8 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
                      size_t(lf::kMaxBatch) * D.hkv);
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bbest), 0u, size_t(2 * lf::kMaxBatch));
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, st, m->at<unsigned>(W.bcounter), 0u, size_t(1));
+  // batched step buffers zeroed: the operands are zero past K and in the
+  // columns of sequences a batch does not use
   hipLaunchKernelGGL(lf::k_fill_u32, dim3(64), dim3(256), 0, st, m->at<unsigned>(W.bx), 0u,
                      (W.bss + lf::kMaxBatch * lf::kSsStride * sizeof(float) - W.bx) / sizeof(unsigned));
   hipError_t e = hipGetLastError();
