@@ -34,7 +34,8 @@ constexpr int kMaxBatch = 8;
 constexpr int kSsStride = 1024;  // partial sums of squares per sequence (one per producing workgroup)
 constexpr int kSsMax = 512;      // most partials a consumer reads per sequence
 
-// Per-sequence buffers of one batched step (entries past n unused).
+// Per-sequence buffers of one batched step (entries past n repeat entry 0,
+// so that every entry is a valid address: loads need no condition).
 struct BatchSeqs {
   int32_t* state[kMaxBatch];
   int32_t* tokens[kMaxBatch];
@@ -43,11 +44,12 @@ struct BatchSeqs {
   float* logits[kMaxBatch];
 };
 
-// The position of each of the n sequences, read with scalar loads (the state
-// pointers are kernel arguments) before any vector load of the caller.
-__device__ __forceinline__ void batch_positions(const BatchSeqs& q, int n, int (&pos)[kMaxBatch]) {
+// The position of each sequence slot, read with scalar loads (the state
+// pointers are kernel arguments) before any vector load of the caller; no
+// condition on a load, so that all eight are in flight together.
+__device__ __forceinline__ void batch_positions(const BatchSeqs& q, int (&pos)[kMaxBatch]) {
 #pragma unroll
-  for (int s = 0; s < kMaxBatch; ++s) pos[s] = s < n ? cload(q.state[s] + kLen) : 0;
+  for (int s = 0; s < kMaxBatch; ++s) pos[s] = cload(q.state[s] + kLen);
 }
 
 __device__ __forceinline__ int pick(const int (&v)[kMaxBatch], int s) {
@@ -64,7 +66,8 @@ enum BEpi : int { kBEpiQKV = 0, kBEpiSwiGLU = 1, kBEpiResid = 2, kBEpiLogits = 3
 struct BGemmArgs {
   const half_t* W;     // [rows, K] fp16 (QKV and gate/up rows repacked as for the batch-1 kernels)
   int rows, K;         // K a multiple of 8
-  const half_t* B;     // the input as the instruction's operand (frag_index), gain applied; zero past K
+  const half_t* B;     // the input as the instruction's operand (frag_index), gain applied; zero past K,
+                       // and allocated one k-step past the last (all zero)
   const float* ss;     // normalised input: partial sums of squares of the raw input, [kMaxBatch][kSsStride]
   int ss_n;            // partials per sequence (<= kSsMax); 0: the input is not normalised
   float eps;
@@ -135,85 +138,115 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   __shared__ float ssw[TPW][kMaxBatch];
   __shared__ unsigned long long wkey[TPW][kMaxBatch];
   __shared__ int flag;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  __shared__ u32x4 wt[NW][16 * 144 / 16];  // per wave: one 16-row x 64-k weight block (rows 144 B apart)
+  static_assert(KB % 2 == 0, "weights are loaded in pairs of k-steps");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4, col = lane & 15;
   const int nks = (a.K + 31) >> 5;
-  const int J = (nks + NW - 1) / NW;  // k-step slots per wave: slot j is k-step wave + 8 j (if < nks)
+  const int J = 2 * (((nks + 1) / 2 + NW - 1) / NW);  // k-step slots per wave (pairs of k-steps)
   const int ntiles = (a.rows + 15) >> 4, tile0 = blockIdx.x * TPW;
 
   int pos[kMaxBatch];
-  if constexpr (EPI == kBEpiQKV || EPI == kBEpiLogits) batch_positions(a.seq, a.n, pos);
-  // Loaded before the weights (a wave's loads complete in issue order): the
-  // partial sums of squares of sequence `wave` (summed at the end), and what
-  // the epilogue reads. Wave t < TPW finishes tile tile0 + t; lane (g, col)
-  // holds rows 16 tile + 4 g + r (r < 4) of sequence col.
+  if constexpr (EPI == kBEpiQKV || EPI == kBEpiLogits) batch_positions(a.seq, pos);
+  // Loaded before the weights (a wave's loads complete in issue order), all
+  // from clamped in-range addresses without a condition (a condition around
+  // a load makes the compiler wait for it at once): the partial sums of
+  // squares of sequence `wave` (summed at the end), and what the epilogue
+  // reads. Wave t < TPW finishes tile tile0 + t; lane (g, col) holds rows
+  // 16 tile + 4 g + r (r < 4) of sequence col.
   float ssv[kSsMax / kWave];
   if constexpr (NORM) {
+    const float* sp = a.ss + min(wave, a.n - 1) * kSsStride;
+    const int last = max(a.ss_n - 1, 0);
 #pragma unroll
-    for (int j = 0; j < kSsMax / kWave; ++j) {
-      const int i = lane + kWave * j;
-      ssv[j] = (wave < a.n && i < a.ss_n) ? a.ss[wave * kSsStride + i] : 0.f;
-    }
+    for (int j = 0; j < kSsMax / kWave; ++j) ssv[j] = sp[min(lane + kWave * j, last)];
   }
   const bool epi = wave < TPW && tile0 + wave < ntiles;
   const int s = col;
+  const int sl = min(s, a.n - 1);  // the sequence this lane's loads use
   const bool act = epi && s < a.n;
   const int row0 = 16 * (tile0 + wave) + 4 * g;
   f32x4 xres = {0.f, 0.f, 0.f, 0.f};
   float gnext[4] = {0.f, 0.f, 0.f, 0.f};
   float2 cs[2] = {{1.f, 0.f}, {1.f, 0.f}};
   if constexpr (EPI == kBEpiResid) {
-    if (act) {
-      const float* xp = a.y + static_cast<size_t>(s) * a.y_stride;
+    const float* xp = a.y + static_cast<size_t>(sl) * a.y_stride;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = min(row0 + r, a.rows - 1);
-        xres[r] = xp[row];
-        gnext[r] = static_cast<float>(a.next_gain[row]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int row = min(row0 + r, a.rows - 1);
+      xres[r] = xp[row];
+      gnext[r] = static_cast<float>(a.next_gain[row]);
     }
   } else if constexpr (EPI == kBEpiQKV) {
-    if (act) {
-      const int p = min(pick(pos, s), a.max_ctx - 1), half_hd = a.hd >> 1;
+    const int p = min(pick(pos, sl), a.max_ctx - 1), half_hd = a.hd >> 1;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = ((min(row0 + 2 * h, a.rows - 2)) % a.hd) >> 1;
-        cs[h] = a.rope[static_cast<size_t>(p) * half_hd + c];
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int c = ((min(row0 + 2 * h, a.rows - 2)) % a.hd) >> 1;
+      cs[h] = a.rope[static_cast<size_t>(p) * half_hd + c];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  // Weight loads: a 16-row x 64-k block of a tile (k-steps 2p and 2p + 1)
+  // is read as two instructions of 8 rows x 128 bytes, lane l taking row
+  // l / 8 (+ 8) and 16 bytes at chunk l % 8: whole 128-byte lines per
+  // instruction, which streams about a quarter faster than the operand
+  // layout's 16 rows x 64 bytes. compute() passes each block through a
+  // wave-private LDS tile to put it in the operand layout. A wave takes the
+  // k-step pairs in turn with the other waves (pair w, w + 8, ...); slots past
+  // its last pair load its first pair again (an L2 hit) and are masked.
   const half_t* wr[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
-    wr[t] = a.W + static_cast<size_t>(min(16 * min(tile0 + t, ntiles - 1) + col, a.rows - 1)) * a.K;
-  // slots past this wave's last k-step load that k-step again (an L2 hit)
-  // and are masked where used; k-groups past K load a clamped address, and
-  // the operand is zero there
-  const int ks_last = wave + NW * (J - 1) < nks ? wave + NW * (J - 1) : wave + NW * ((nks - 1 - wave) / NW);
+    wr[t] = a.W + static_cast<size_t>(min(16 * min(tile0 + t, ntiles - 1) + (lane >> 3), a.rows - 1)) * a.K;
+  const size_t half_rows = static_cast<size_t>(8) * a.K;  // rows 8 .. 15 of a tile
+  const int npair = (nks + 1) >> 1;
+  const int first_pair = min(wave, npair - 1);
+  auto pair_of = [&](int j) { return wave + NW * (j >> 1); };
   auto issue = [&](BBatch<KB, TPW>& b, int j0) {
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int ks = min(wave + NW * (j0 + j), ks_last);
-      const int k = min(ks * 32 + 8 * g, a.K - 8);
+    for (int j = 0; j < KB; j += 2) {
+      const int p0 = pair_of(j0 + j);
+      const int p = p0 < npair ? p0 : first_pair;
+      const int k = min(64 * p + 8 * (lane & 7), a.K - 8);
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) b.w[j][t] = ld_stream(wr[t] + k);
-      b.b[j] = ld16(a.B + (static_cast<size_t>(ks) * kWave + lane) * 8);
+      for (int t = 0; t < TPW; ++t) {
+        const int rt = 16 * min(tile0 + t, ntiles - 1) + (lane >> 3);
+        b.w[j][t] = ld_stream(wr[t] + k);
+        b.w[j + 1][t] = ld_stream(wr[t] + (rt + 8 < a.rows ? half_rows : 0) + k);
+      }
+      // k-steps past the last (and the slots past the wave's last pair) read
+      // k-step nks of the operand, which is zero
+      const int ks0 = p0 < npair ? 2 * p0 : nks, ks1 = p0 < npair && 2 * p0 + 1 < nks ? 2 * p0 + 1 : nks;
+      b.b[j] = ld16(a.B + (static_cast<size_t>(ks0) * kWave + lane) * 8);
+      b.b[j + 1] = ld16(a.B + (static_cast<size_t>(ks1) * kWave + lane) * 8);
     }
   };
   f32x4 acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kRowB = 144;  // LDS bytes per row of a block (128 + 16: rows 4 banks apart)
+  char* tile_lds = reinterpret_cast<char*>(wt[wave]);
   auto compute = [&](const BBatch<KB, TPW>& b, int j0) {
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const bool valid = wave + NW * (j0 + j) < nks;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const h8 frag = __builtin_bit_cast(h8, valid ? b.b[j] : z);
+    for (int j = 0; j < KB; j += 2) {
+      const h8 f0 = __builtin_bit_cast(h8, b.b[j]), f1 = __builtin_bit_cast(h8, b.b[j + 1]);
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, b.w[j][t]), frag, acc[t], 0, 0, 0);
+      for (int t = 0; t < TPW; ++t) {
+        // lane l wrote row l / 8 (+ 8), chunk l % 8; lane (g, m) reads row m,
+        // chunk g (k-step 2p) and chunk g + 4 (k-step 2p + 1). The same
+        // wave's LDS operations execute in order; the compiler barriers keep
+        // the reads after the writes.
+        *reinterpret_cast<u32x4*>(tile_lds + (lane >> 3) * kRowB + (lane & 7) * 16) = b.w[j][t];
+        *reinterpret_cast<u32x4*>(tile_lds + ((lane >> 3) + 8) * kRowB + (lane & 7) * 16) = b.w[j + 1][t];
+        asm volatile("" ::: "memory");
+        const h8 a0 = *reinterpret_cast<const h8*>(tile_lds + col * kRowB + g * 16);
+        const h8 a1 = *reinterpret_cast<const h8*>(tile_lds + col * kRowB + (g + 4) * 16);
+        asm volatile("" ::: "memory");
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, f0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, f1, acc[t], 0, 0, 0);
+      }
     }
   };
   // Two batches in flight, in a loop without any condition on an issue (one
@@ -250,7 +283,7 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   if constexpr (NORM) {
     float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kSsMax / kWave; ++j) sum += ssv[j];
+    for (int j = 0; j < kSsMax / kWave; ++j) sum += lane + kWave * j < a.ss_n ? ssv[j] : 0.f;
     sum = wave_total(sum);
     if (lane == 0 && wave < a.n) rs[wave] = 1.0f / sqrtf(sum / static_cast<float>(a.K) + a.eps);
   }

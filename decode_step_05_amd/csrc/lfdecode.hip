@@ -193,8 +193,9 @@ WsLayout ws_layout(const lf_config& c) {
   const size_t B = lf::kMaxBatch;
   W.bx = take(B * D.d * sizeof(float));
   W.bq = take(B * D.qdim * sizeof(float));
-  // projection operands (frag_index): per k-step of 32, 64 lanes of 8 fp16
-  auto frag_bytes = [](int K) { return static_cast<size_t>((K + 31) / 32) * 64 * 8 * sizeof(half_t); };
+  // projection operands (frag_index): per k-step of 32, 64 lanes of 8 fp16,
+  // and one more k-step that stays zero (read in place of k-steps past K)
+  auto frag_bytes = [](int K) { return static_cast<size_t>((K + 31) / 32 + 1) * 64 * 8 * sizeof(half_t); };
   W.bfd = take(frag_bytes(D.d));
   W.bfq = take(frag_bytes(D.qdim));
   W.bff = take(frag_bytes(D.ffn));
@@ -711,7 +712,7 @@ void drop_graphs(lf_model* m, lf_kv* kv) {
 // k-steps per batch of loads: 8 KB of weights per wave and batch where the
 // grid fits one workgroup per CU, half that where it is larger, so that two
 // workgroups fit per CU (fewer registers) and the whole grid is resident at
-// once.
+// once; KB is even (k-steps are loaded in pairs) and at least 2.
 struct BShape {
   int tpw, kb, blocks;
 };
@@ -724,7 +725,7 @@ BShape bgemm_shape(int rows) {
       break;
     }
   const int blocks = (tiles + tpw - 1) / tpw;
-  return {tpw, (blocks > 256 ? 4 : 8) / tpw, blocks};
+  return {tpw, std::max(2, (blocks > 256 ? 4 : 8) / tpw), blocks};
 }
 
 template <int EPI, bool NORM>
@@ -733,7 +734,7 @@ const void* bgemm_fn(const BShape& sh) {
     return nullptr;  // a residual GEMM's input (attention output, SwiGLU) is never normalised
   } else {
 #define LF_BGEMM(T, KB) if (sh.tpw == T && sh.kb == KB) return reinterpret_cast<const void*>(&lf::k_bgemm<EPI, T, NORM, KB>);
-    LF_BGEMM(1, 8) LF_BGEMM(1, 4) LF_BGEMM(2, 4) LF_BGEMM(2, 2) LF_BGEMM(4, 2) LF_BGEMM(4, 1)
+    LF_BGEMM(1, 8) LF_BGEMM(1, 4) LF_BGEMM(2, 4) LF_BGEMM(2, 2) LF_BGEMM(4, 2)
 #undef LF_BGEMM
     return nullptr;
   }
@@ -769,12 +770,13 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
   const lf_config& c = m->cfg;
   const size_t layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
   lf::BatchSeqs q{};
-  for (int i = 0; i < n; ++i) {
-    q.state[i] = kvs[i]->state();
-    q.tokens[i] = kvs[i]->tokens();
-    q.kc[i] = kvs[i]->kc();
-    q.vc[i] = kvs[i]->vc();
-    q.logits[i] = kvs[i]->logits();
+  for (int i = 0; i < lf::kMaxBatch; ++i) {  // slots past n repeat sequence 0 (valid addresses)
+    lf_kv* kv = kvs[i < n ? i : 0];
+    q.state[i] = kv->state();
+    q.tokens[i] = kv->tokens();
+    q.kc[i] = kv->kc();
+    q.vc[i] = kv->vc();
+    q.logits[i] = kv->logits();
   }
   float* x = m->at<float>(W.bx);
   float* ss = m->at<float>(W.bss);
