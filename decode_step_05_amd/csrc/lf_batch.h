@@ -446,8 +446,8 @@ struct AttnBArgs {
 // blockIdx.z: k_attn's two-dimensional layout (the splits of a kv head are
 // consecutive workgroups), with the sequence's cache, position, queries,
 // split states and epochs; the outputs go to column s of the O projection's
-// operand.
-template <int HD, int G, int U>
+// operand. DB: splits of several load rounds, double-buffered.
+template <int HD, int G, int U, bool DB>
 __global__ __launch_bounds__(kBlock) void k_battn(AttnBArgs b) {
   __shared__ AttnXSmem<HD, G> sm;
   const int s = blockIdx.z;
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kBlock) void k_battn(AttnBArgs b) {
   a.ofrag = b.ofrag;
   a.fcol = s;
   a.epochs = b.epochs + static_cast<size_t>(s) * a.n_kv;
-  attn_item<HD, G, U, false>(a, blockIdx.x, blockIdx.y, sm);
+  attn_item<HD, G, U, false, DB>(a, blockIdx.x, blockIdx.y, sm);
 }
 
 // Start a batched step: sequence s's token at its position is d_tokens[s]

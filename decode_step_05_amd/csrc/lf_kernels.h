@@ -814,8 +814,11 @@ struct AttnXSmem {
 // modulo 8, so they run on one XCD and exchange their states through its
 // L2; otherwise the grid is (S, n_kv) and the states go through memory.
 // The work item (split si, kv head kvh) of one attention launch, run by a
-// whole workgroup of kBlock threads (see k_attn).
-template <int HD, int G, int U, bool XCD>
+// whole workgroup of kBlock threads (see k_attn). DB: the split spans several
+// load rounds, which are double-buffered (the next round's loads are in
+// flight while a round is computed; rounds past the split re-read its last
+// key, L2 hits, and are masked).
+template <int HD, int G, int U, bool XCD, bool DB = false>
 __device__ __forceinline__ void attn_item(const AttnXArgs& a, int si, int kvh, AttnXSmem<HD, G>& sm) {
   constexpr int LPR = HD / 8, NW = kWavesPerBlock;
   const int p = a.t.state[kLen];
@@ -849,7 +852,21 @@ __device__ __forceinline__ void attn_item(const AttnXArgs& a, int si, int kvh, A
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
   }
   const int nk = sp.nk;
-  if (nk > 0) {
+  if constexpr (DB) {
+    if (nk > 0) {
+      AttnLoads<U> ld1;
+      for (int b0 = wave; b0 * KPW < nk; b0 += 2 * NW * U) {
+        attn_load<HD, U, NW>(ld1, sp, b0 + NW * U);
+        __builtin_amdgcn_sched_barrier(0);
+        attn_step<HD, G, U, NW>(ld, b0, kin, nk, qr, m, l, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        attn_load<HD, U, NW>(ld, sp, b0 + 2 * NW * U);
+        __builtin_amdgcn_sched_barrier(0);
+        attn_step<HD, G, U, NW>(ld1, b0 + NW * U, kin, nk, qr, m, l, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if (nk > 0) {
     attn_step<HD, G, U, NW>(ld, wave, kin, nk, qr, m, l, acc);
     for (int b0 = wave + NW * U; b0 * KPW < nk; b0 += NW * U) {
       attn_load<HD, U, NW>(ld, sp, b0);

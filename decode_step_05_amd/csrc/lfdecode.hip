@@ -748,11 +748,26 @@ int launch_bgemm(const lf::BGemmArgs& a, hipStream_t st) {
   return sh.blocks;  // partial sums of squares a residual GEMM writes per sequence
 }
 
+// The batched attention's splits: as many as keep about two workgroups per CU
+// for the n sequences at once (the whole grid resident), at most kMaxSplits
+// and at least 128 keys each; a split of more than 128 keys is read in
+// double-buffered rounds of 128 (4 waves x 8 loads per lane).
+AttnPlan batch_attn_plan(const lf_config& c, int layer, int n) {
+  const int visible = visible_keys(c, layer);
+  const int want = std::max(1, 512 / (c.n_kv_heads * n));
+  return split_plan(visible, std::min(want, (visible + 127) / 128));
+}
+int batch_attn_u(int chunk, int hd) {
+  const int per8 = lf::kWavesPerBlock * 8 * (512 / hd);  // keys per round at 8 loads per lane
+  return chunk > per8 ? 0 : attn_loads_per_lane(chunk, hd);  // 0: rounds of 8, double-buffered
+}
+
 template <int HD, int G>
 const void* battn_fn(int u) {
-  return u == 4   ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 4>)
-         : u == 8 ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 8>)
-                  : reinterpret_cast<const void*>(&lf::k_battn<HD, G, 16>);
+  return u == 4   ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 4, false>)
+         : u == 8 ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 8, false>)
+         : u == 0 ? reinterpret_cast<const void*>(&lf::k_battn<HD, G, 8, true>)
+                  : reinterpret_cast<const void*>(&lf::k_battn<HD, G, 16, false>);
 }
 const void* battn_kernel(int hd, int G, int u) {
 #define LF_BATTN_CASE(H, GG) if (hd == H && G == GG) return battn_fn<H, GG>(u);
@@ -811,7 +826,7 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     a.y_stride = D.qdim;
     launch_bgemm<lf::kBEpiQKV, true>(a, st);
 
-    const AttnPlan P = attn_plan(c, l);
+    const AttnPlan P = batch_attn_plan(c, l, n);
     lf::AttnBArgs b{};
     b.a.t.max_ctx = D.ctx;
     b.a.t.window = c.window[l];
@@ -833,7 +848,7 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     b.q_dim = D.qdim;
     {
       void* args[] = {&b};
-      (void)hipLaunchKernel(battn_kernel(D.hd, D.G, attn_loads_per_lane(P.chunk, D.hd)), dim3(P.S, D.hkv, n),
+      (void)hipLaunchKernel(battn_kernel(D.hd, D.G, batch_attn_u(P.chunk, D.hd)), dim3(P.S, D.hkv, n),
                             dim3(lf::kBlock), args, 0, st);
     }
 
