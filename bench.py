@@ -58,17 +58,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def step_bytes(cfg, p):
-    """Bytes a step at position p must move: every fp16 weight once (the LM
-    head and one embedding row included, norm gains excluded) plus K and V of
-    the keys each layer sees."""
+def weight_bytes(cfg):
+    """Every fp16 weight a step reads once: the projections, the LM head and
+    one embedding row (norm gains excluded)."""
     d, h = cfg.d_model, 2
     w = cfg.n_layers * h * (cfg.qkv_rows * d + d * cfg.q_dim + 2 * cfg.ffn * d + d * cfg.ffn)
     if cfg.vocab:
         w += h * cfg.vocab * d + h * d
-    per_key = 2 * h * cfg.n_kv_heads * cfg.head_dim
-    kv = sum(per_key * ((p + 1) if W == 0 else min(p + 1, W)) for W in cfg.windows)
-    return w + kv
+    return w
+
+
+def kv_bytes(cfg, p):
+    """K and V of the keys each layer sees at position p."""
+    per_key = 2 * 2 * cfg.n_kv_heads * cfg.head_dim
+    return sum(per_key * ((p + 1) if W == 0 else min(p + 1, W)) for W in cfg.windows)
+
+
+def step_bytes(cfg, p):
+    """Bytes a step at position p must move: every fp16 weight once plus K and
+    V of the keys each layer sees."""
+    return weight_bytes(cfg) + kv_bytes(cfg, p)
 
 
 def golden_tokens(name):
@@ -321,6 +330,65 @@ def sampled_rate(torch, C, dec, seq, P, n=64, T=0.8):
     return {"workload": f"sampled decode at T {T} of positions {P + 1}..{P + n}: logits copy, lf_sample, "
                         "decode step fed with the drawn token",
             "ms_per_step": round(ms, 4), "tok_s": round(1e3 / ms, 1)}
+
+
+def pass_at_n(torch, C, dec, P, prompt_dev, K=32, T=0.8):
+    """Aggregate tok/s of the batched step (lf_decode_step_batch) for N = 1,
+    2, 4, 8 continuations of one prompt: the prompt's cache is filled once by
+    the batched prompt pass and copied to the other N - 1 sequences; each
+    timed region is the last K steps of the context (positions 4096-K ..
+    4095), device-fed greedy, then the same with a temperature draw per
+    sequence per step (logits of the N sequences, one lf_sample launch over
+    the N rows, the batch step fed with the draws). Roofline bytes per step:
+    the weights once plus each sequence's visible cache."""
+    import numpy as np
+    cfg = dec.cfg
+    start = cfg.max_ctx - K
+    seqs = [dec.sequence() for _ in range(8)]
+    seqs[0].prefill_batched(prompt_dev, chunk=PREFILL_CHUNK)
+    seqs[0].steps(start - P)  # greedy up to the timed region
+    torch.cuda.synchronize()
+    for q in seqs[1:]:
+        q.buf.copy_(seqs[0].buf)  # state, history and caches; each handle keeps its own buffer
+        q.set_len(start)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    zbuf = torch.empty((8, cfg.vocab), dtype=torch.float32, device="cuda")
+    tok = torch.empty((K, 8), dtype=torch.int32, device="cuda")
+    u = torch.from_numpy(np.random.default_rng(9).random((K, 8)).astype(np.float32)).cuda()
+    out = {}
+    for n in (1, 2, 4, 8):
+        b = seqs[:n]
+        res = {}
+        for mode in ("greedy", "sampled"):
+            for rep in range(2):  # the first run warms up (and records the graph)
+                for q in b:
+                    q.set_len(start)
+                torch.cuda.synchronize()
+                e0.record()
+                for k in range(K):
+                    if mode == "greedy":
+                        dec.step_batch(b)
+                    else:
+                        for i, q in enumerate(b):
+                            C.lf_logits(dec.handle, q.handle, zbuf[i])
+                        C.lf_sample(zbuf[:n], T, u[k, :n], tok[k, :n])
+                        dec.step_batch(b, tok[k, :n])
+                e1.record()
+                torch.cuda.synchronize()
+                for q in b:
+                    check_status(q, cfg.max_ctx, f"pass@{n} {mode}")
+            ms = e0.elapsed_time(e1) / K
+            moved = sum(weight_bytes(cfg) + n * kv_bytes(cfg, p) for p in range(start, cfg.max_ctx)) / K
+            res[mode] = {"ms_per_step": round(ms, 4), "tok_s": round(n * 1e3 / ms, 1),
+                         "hbm_gbs": round(moved / (ms / 1e3) / 1e9, 1),
+                         "roofline_tok_s": round(n * PEAK_HBM_GBS * 1e9 / moved, 1)}
+        out[f"n{n}"] = res
+    del seqs
+    out["workload"] = (f"N continuations of the {P}-token prompt, the last {K} steps of the context (positions "
+                       f"{start}..{cfg.max_ctx - 1}), batched step; sampled: T {T}, one lf_sample over the N rows "
+                       "per step; roofline bytes = weights once + N visible caches")
+    return out
 
 
 def prefill_flops(cfg, n):
@@ -595,6 +663,10 @@ def main():
     fused = dec.fused
     sampled = sampled_rate(torch, C, dec, seq, P)
     log(f"[bench] sampled decode: {sampled['tok_s']:.1f} tok/s")
+    batch = pass_at_n(torch, C, dec, P, prompt_dev)
+    log("[bench] pass@N batched step (tok/s greedy / sampled): " +
+        ", ".join(f"N={k[1:]} {v['greedy']['tok_s']:.0f} / {v['sampled']['tok_s']:.0f}"
+                  for k, v in batch.items() if k.startswith("n")))
 
     # practical read ceiling: a plain streaming read of 4 GiB
     buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
@@ -668,6 +740,7 @@ def main():
         "tiny_latency": tiny,
         "sampling": sampling,
         "sampled_decode": sampled,
+        "pass_at_n": batch,
         "prefill_s": round(prefill_s, 3),
         "prefill": prefill,
         "kernel_avg_us_eager": {k: round(v * 1e3, 2) for k, v in avg.items()},
