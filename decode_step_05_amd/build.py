@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblfdecode.so")
 SOURCES = [os.path.join(CSRC, "lfdecode.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("lf_device.h", "lf_kernels.h", "lf_exchange.h", "lf_prefill.h", "lf_sample.h")] + [os.path.join(ROOT, "include", "lfdecode.h")]
+HEADERS = [os.path.join(CSRC, f) for f in ("lf_device.h", "lf_kernels.h", "lf_exchange.h", "lf_prefill.h", "lf_sample.h", "lf_batch.h")] + [os.path.join(ROOT, "include", "lfdecode.h")]
 
 
 def hipcc() -> str:

@@ -1410,6 +1410,9 @@ int lf_decode_step_batch(lf_model* m, lf_kv* const* kvs, int32_t n, const int32_
     if (kv->len >= m->D.ctx) return fail(LF_ERANGE, "sequence %d is full (%d positions)", i, m->D.ctx);
     if (!d_tokens && kv->len == 0) return fail(LF_EINVAL, "sequence %d has no previous position to take a greedy token from", i);
   }
+  // one sequence: the single-sequence step is faster (its GEMVs use every
+  // lane; the batched GEMMs would fill 1 of their 16 operand columns)
+  if (n == 1) return lf_decode_step(m, kvs[0], d_tokens, stream);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d_tokens) {
     lf::BTokArgs t{};

@@ -301,10 +301,10 @@ int lf_decode_steps(lf_model* m, lf_kv* kv, int32_t n, void* stream);
  * position (e.g. drawn by lf_sample from the rows of lf_logits), or NULL to
  * feed each sequence its own greedy token of the previous position.
  * kvs: host array of n distinct sequence handles of model m.
- * Numerics: the projections run on the matrix cores with each fp32
- * activation split into two fp16 parts (hi = fp16(a), lo = fp16(a - hi)),
+ * Numerics: for n >= 2 the projections run on the matrix cores with each
+ * fp32 activation split into two fp16 parts (hi = fp16(a), lo = fp16(a - hi)),
  * fp32 accumulation; attention, softmax and logits in fp32 as in the
- * single-sequence step. LF_EINVAL for null or repeated handles, n out of
+ * single-sequence step. n == 1 runs lf_decode_step itself (bitwise the same). LF_EINVAL for null or repeated handles, n out of
  * range, vocab == 0, or d_tokens NULL for an empty sequence; LF_ERANGE if a
  * sequence is full. Graph mode records one hipGraph per (n, handles) and
  * replays it. Enqueued on stream.
