@@ -145,7 +145,14 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   const int g = lane >> 4, col = lane & 15;
   const int nks = (a.K + 31) >> 5;
   const int J = 2 * (((nks + 1) / 2 + NW - 1) / NW);  // k-step slots per wave (pairs of k-steps)
-  const int ntiles = (a.rows + 15) >> 4, tile0 = blockIdx.x * TPW;
+  // Runs of consecutive tiles share an XCD: when the grid is a multiple of 8
+  // (workgroups are dealt to the 8 XCDs in turn), XCD c takes the c-th eighth
+  // of the tiles, so that for the lane-major QKV rows the queries, keys and
+  // values of one lane are computed, and their cache lines assembled, in one
+  // L2 (measured: QKV 16.8 -> 15.8 us, gate/up 22.5 -> 21.7 us per launch at
+  // 8 sequences; the mapping is a permutation either way).
+  const int bx = (gridDim.x & 7) == 0 ? (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int ntiles = (a.rows + 15) >> 4, tile0 = bx * TPW;
 
   int pos[kMaxBatch];
   if constexpr (EPI == kBEpiQKV || EPI == kBEpiLogits) batch_positions(a.seq, pos);
