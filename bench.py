@@ -474,6 +474,7 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only copy a MB-MiB device buffer three times and exit (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--prefill-chunk", type=int, default=PREFILL_CHUNK, help="positions per chunk of the batched prompt pass")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time the batched prompt pass (3 runs) and print its JSON object")
     ap.add_argument("--headline-only", action="store_true",
@@ -527,13 +528,13 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     pseq = dec.sequence()
-    pseq.prefill_batched(prompt_dev, chunk=PREFILL_CHUNK)
+    pseq.prefill_batched(prompt_dev, chunk=args.prefill_chunk)
     pf_ms = []
     for _ in range(3):
         pseq.set_len(0)
         torch.cuda.synchronize()
         e0.record()
-        pseq.prefill_batched(prompt_dev, chunk=PREFILL_CHUNK)
+        pseq.prefill_batched(prompt_dev, chunk=args.prefill_chunk)
         e1.record()
         torch.cuda.synchronize()
         pf_ms.append(e0.elapsed_time(e1))
@@ -542,7 +543,7 @@ def main():
     pf_tflops = prefill_flops(cfg, P) / (pf_med / 1e3) / 1e12
     log(f"[bench] batched prompt pass of {P} positions: {', '.join(f'{x:.2f}' for x in pf_ms)} ms "
         f"-> {pf_tflops:.0f} TFLOP/s")
-    prefill = {"positions": P, "chunk": PREFILL_CHUNK, "runs_ms": [round(x, 3) for x in pf_ms],
+    prefill = {"positions": P, "chunk": args.prefill_chunk, "runs_ms": [round(x, 3) for x in pf_ms],
                "ms": round(pf_med, 3), "tok_s": round(P / (pf_med / 1e3), 1),
                "roofline": {"bound": "mfma", "kernel": "whole batched prompt pass (lf_prefill_batched)",
                             "achieved": round(pf_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
