@@ -332,7 +332,7 @@ def sampled_rate(torch, C, dec, seq, P, n=64, T=0.8):
             "ms_per_step": round(ms, 4), "tok_s": round(1e3 / ms, 1)}
 
 
-def pass_at_n(torch, C, dec, P, prompt_dev, K=32, T=0.8):
+def pass_at_n(torch, C, dec, P, prompt_dev, K=32, T=0.8, ns=(1, 2, 4, 8)):
     """Aggregate tok/s of the batched step (lf_decode_step_batch) for N = 1,
     2, 4, 8 continuations of one prompt: the prompt's cache is filled once by
     the batched prompt pass and copied to the other N - 1 sequences; each
@@ -357,7 +357,7 @@ def pass_at_n(torch, C, dec, P, prompt_dev, K=32, T=0.8):
     tok = torch.empty((K, 8), dtype=torch.int32, device="cuda")
     u = torch.from_numpy(np.random.default_rng(9).random((K, 8)).astype(np.float32)).cuda()
     out = {}
-    for n in (1, 2, 4, 8):
+    for n in ns:
         b = seqs[:n]
         res = {}
         for mode in ("greedy", "sampled"):
@@ -475,6 +475,8 @@ def main():
                     help="only copy a MB-MiB device buffer three times and exit (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     ap.add_argument("--prefill-chunk", type=int, default=PREFILL_CHUNK, help="positions per chunk of the batched prompt pass")
+    ap.add_argument("--pass-at-n-only", type=int, default=0, metavar="N",
+                    help="run only the batched-step measurement for N sequences (for a kernel trace) and exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time the batched prompt pass (3 runs) and print its JSON object")
     ap.add_argument("--headline-only", action="store_true",
@@ -553,6 +555,12 @@ def main():
                                     "instructions as hi + lo parts, so the GEMMs issue twice these flops"}}
     if args.prefill_only:
         print(json.dumps({"prefill": prefill}), flush=True)
+        return
+    if args.pass_at_n_only:
+        if not 1 <= args.pass_at_n_only <= C.LF_MAX_BATCH:
+            raise SystemExit(f"--pass-at-n-only takes 1 .. {C.LF_MAX_BATCH}")
+        batch = pass_at_n(torch, C, dec, P, prompt_dev, ns=(args.pass_at_n_only,))
+        print(json.dumps({"pass_at_n": batch}), flush=True)
         return
 
     seq = dec.sequence()
