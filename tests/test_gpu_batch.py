@@ -183,14 +183,18 @@ def test_batch_sampled_pass_at_n():
 
 
 @pytest.mark.timeout(600)
-def test_batch_full_model_at_ctx4096():
-    """8 sequences of the full model over one synthetic cache, of lengths
-    4088 .. 4095 - 3 s ... (each its own), 3 batched steps each fed its own
-    token: all 32000 logits of every sequence and step against the float64
-    oracle."""
+@pytest.mark.parametrize("n", [8, 3, 2])
+def test_batch_full_model_at_ctx4096(n):
+    """n sequences of the full model over one synthetic cache, of lengths
+    4092, 4087, ... (each its own), 3 batched steps each fed its own token:
+    all 32000 logits of every sequence and step against the float64 oracle.
+    The batch sizes take different attention split plans: at 8 sequences 4
+    splits per sequence and kv head, read in double-buffered rounds on every
+    layer; at 3 and 2, 10 and 16 splits on the full-attention layers (double
+    buffered) and 8 splits of 128 keys, one round each, on the windowed ones."""
     import torch
     from decode_step_05_amd import Decoder
-    cfg, n, steps = FULL, 8, 3
+    cfg, steps = FULL, 3
     lens = [4092 - 5 * s for s in range(n)]
     say(f"[batch] full model n={n} cache lengths {lens} (seed 2) steps={steps}")
     w = make_weights(cfg, seed=0, threads=16)
