@@ -657,11 +657,17 @@ int enqueue_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStrea
   return LF_OK;
 }
 
+// Recorded graphs a model keeps (single-sequence and batched, each): a key
+// past that (a new sequence, hidden-state buffers or batch) runs its kernels
+// eagerly, with the same results, rather than growing the cache without bound.
+constexpr size_t kMaxGraphs = 64;
+
 int run_step(lf_model* m, lf_kv* kv, const float* xin, float* xout, hipStream_t st) {
   if (m->mode == LF_MODE_EAGER) return enqueue_step(m, kv, xin, xout, st);
   hipGraphExec_t exec = nullptr;
   for (const GraphEntry& g : m->graphs)
     if (g.kv == kv && g.xin == xin && g.xout == xout) exec = g.exec;
+  if (!exec && m->graphs.size() >= kMaxGraphs) return enqueue_step(m, kv, xin, xout, st);
   if (!exec) {
     // Record on the library's own stream (the caller's may be the legacy
     // default stream, which cannot be captured); nothing executes here.
@@ -1426,16 +1432,17 @@ int lf_decode_step_batch(lf_model* m, lf_kv* const* kvs, int32_t n, const int32_
     hipLaunchKernelGGL(lf::k_bset_tokens, dim3(1), dim3(64), 0, st, t);
     LF_HIP(hipPeekAtLastError());
   }
-  if (m->mode == LF_MODE_EAGER) {
-    const int rc = enqueue_batch_step(m, kvs, n, st);
-    if (rc) return rc;
-  } else {
-    hipGraphExec_t exec = nullptr;
+  hipGraphExec_t exec = nullptr;
+  if (m->mode != LF_MODE_EAGER)
     for (const BatchGraph& g : m->batch_graphs) {
       bool same = g.n == n;
       for (int i = 0; same && i < n; ++i) same = g.kvs[i] == kvs[i];
       if (same) exec = g.exec;
     }
+  if (m->mode == LF_MODE_EAGER || (!exec && m->batch_graphs.size() >= kMaxGraphs)) {
+    const int rc = enqueue_batch_step(m, kvs, n, st);
+    if (rc) return rc;
+  } else {
     if (!exec) {
       hipStream_t cs = m->capture_stream;
       LF_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));

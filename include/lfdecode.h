@@ -124,7 +124,10 @@ void lf_model_free(lf_model* m);
  * How a step is launched. Both modes compute the same function with the same
  * kernels (bitwise the same results).
  *   LF_MODE_GRAPH (default): one kernel per phase, captured per (sequence,
- *     in/out pointers) into a hipGraph on first use and replayed.
+ *     in/out pointers) into a hipGraph on first use and replayed. A model
+ *     keeps at most 64 such graphs (and 64 of lf_decode_step_batch); a step
+ *     of a key beyond those launches its kernels one by one instead (same
+ *     results). lf_kv_free drops the graphs of its sequence.
  *   LF_MODE_EAGER: one kernel per phase, launched one by one.
  * lf_model_set_mode returns LF_EINVAL for any other value.
  * lf_model_set_graph(m, 1/0) selects LF_MODE_GRAPH / LF_MODE_EAGER.
@@ -304,10 +307,11 @@ int lf_decode_steps(lf_model* m, lf_kv* kv, int32_t n, void* stream);
  * Numerics: for n >= 2 the projections run on the matrix cores with each
  * fp32 activation split into two fp16 parts (hi = fp16(a), lo = fp16(a - hi)),
  * fp32 accumulation; attention, softmax and logits in fp32 as in the
- * single-sequence step. n == 1 runs lf_decode_step itself (bitwise the same). LF_EINVAL for null or repeated handles, n out of
- * range, vocab == 0, or d_tokens NULL for an empty sequence; LF_ERANGE if a
- * sequence is full. Graph mode records one hipGraph per (n, handles) and
- * replays it. Enqueued on stream.
+ * single-sequence step. n == 1 runs lf_decode_step itself (bitwise the
+ * same). LF_EINVAL for null or repeated handles, n out of range, vocab == 0,
+ * or d_tokens NULL for an empty sequence; LF_ERANGE if a sequence is full.
+ * Graph mode records one hipGraph per (n, handles) and replays it (at most 64
+ * per model, as for lf_decode_step). Enqueued on stream.
  */
 #define LF_MAX_BATCH 8
 int lf_decode_step_batch(lf_model* m, lf_kv* const* kvs, int32_t n, const int32_t* d_tokens, void* stream);
