@@ -257,6 +257,7 @@ struct lf_model {
   bool fused = false;                    // ... and do
   std::vector<GraphEntry> graphs;
   std::vector<BatchGraph> batch_graphs;
+  int battn_room = 1;                    // batched attention workgroups the device holds at once
   void* scratch = nullptr;               // this device's address of the static prompt-pass scratch
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -758,10 +759,13 @@ int launch_bgemm(const lf::BGemmArgs& a, hipStream_t st) {
 // for the n sequences at once (the whole grid resident), at most kMaxSplits
 // and at least 128 keys each; a split of more than 128 keys is read in
 // double-buffered rounds of 128 (4 waves x 8 loads per lane).
-AttnPlan batch_attn_plan(const lf_config& c, int layer, int n) {
+// The S splits of one (sequence, kv head) are consecutive workgroups that
+// wait on each other, so S is also capped by the device's room for the
+// attention kernel (room: workgroups per CU x CUs, read at init).
+AttnPlan batch_attn_plan(const lf_config& c, int layer, int n, int room) {
   const int visible = visible_keys(c, layer);
   const int want = std::max(1, 512 / (c.n_kv_heads * n));
-  return split_plan(visible, std::min(want, (visible + 127) / 128));
+  return split_plan(visible, std::min({want, (visible + 127) / 128, std::max(room, 1)}));
 }
 int batch_attn_u(int chunk, int hd) {
   const int per8 = lf::kWavesPerBlock * 8 * (512 / hd);  // keys per round at 8 loads per lane
@@ -832,7 +836,7 @@ int enqueue_batch_step(lf_model* m, lf_kv* const* kvs, int n, hipStream_t st) {
     a.y_stride = D.qdim;
     launch_bgemm<lf::kBEpiQKV, true>(a, st);
 
-    const AttnPlan P = batch_attn_plan(c, l, n);
+    const AttnPlan P = batch_attn_plan(c, l, n, m->battn_room);
     lf::AttnBArgs b{};
     b.a.t.max_ctx = D.ctx;
     b.a.t.window = c.window[l];
@@ -1221,6 +1225,17 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   if ((rc = plan_attention(*cfg, ncu, attn_per_cu, fused_per_cu, m->xcd_classes, m->fused_ok, m->attn_xcd)))
     return bail(rc);
   m->fused = m->fused_ok;
+  if (m->D.V) {  // the batched step's attention kernels (lf_decode_step_batch needs a vocabulary)
+    int per_cu = 1 << 20;
+    for (int u : {4, 8, 16, 0}) {
+      int k = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, battn_kernel(m->D.hd, m->D.G, u), lf::kBlock, 0) != hipSuccess)
+        k = 0;  // then one split per (sequence, kv head): nothing waits on another workgroup
+      per_cu = std::min(per_cu, k);
+    }
+    (void)hipGetLastError();
+    m->battn_room = per_cu * ncu;
+  }
   *out = m;
   return LF_OK;
 }
