@@ -210,6 +210,10 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
   const size_t half_rows = static_cast<size_t>(8) * a.K;  // rows 8 .. 15 of a tile
   const int npair = (nks + 1) >> 1;
   const int first_pair = min(wave, npair - 1);
+  // This lane's operand slot (frag_index): the columns of sequences past n
+  // read those of sequence n - 1 instead (the same bytes, so an instruction
+  // reads 32 n bytes per k-group); their results are never used.
+  const int bslot = (lane & 48) + 2 * min(lane & 7, a.n - 1) + ((lane >> 3) & 1);
   auto pair_of = [&](int j) { return wave + NW * (j >> 1); };
   auto issue = [&](BBatch<KB, TPW>& b, int j0) {
 #pragma unroll
@@ -226,8 +230,8 @@ __global__ __launch_bounds__(8 * kWave) void k_bgemm(BGemmArgs a) {
       // k-steps past the last (and the slots past the wave's last pair) read
       // k-step nks of the operand, which is zero
       const int ks0 = p0 < npair ? 2 * p0 : nks, ks1 = p0 < npair && 2 * p0 + 1 < nks ? 2 * p0 + 1 : nks;
-      b.b[j] = ld16(a.B + (static_cast<size_t>(ks0) * kWave + lane) * 8);
-      b.b[j + 1] = ld16(a.B + (static_cast<size_t>(ks1) * kWave + lane) * 8);
+      b.b[j] = ld16(a.B + (static_cast<size_t>(ks0) * kWave + bslot) * 8);
+      b.b[j + 1] = ld16(a.B + (static_cast<size_t>(ks1) * kWave + bslot) * 8);
     }
   };
   f32x4 acc[TPW];

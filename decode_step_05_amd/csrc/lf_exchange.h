@@ -70,12 +70,14 @@ struct SPoll {
 };
 
 // Operand of the batched projections' matrix instructions (16x16x32): per
-// k-step of 32 k, 64 lanes of 8 fp16; lane 16 g + c holds k-group g (k
+// k-step of 32 k, 64 slots of 8 fp16; lane 16 g + c takes k-group g (k
 // 8g .. 8g + 7 of the step) of column c, where column s < 8 is the hi part
-// of sequence s's value and column 8 + s its lo part. Half index of
+// of sequence s's value and column 8 + s its lo part. In memory a k-group's
+// 16 columns are ordered by sequence, hi then lo (slot 16 g + 2 s + h), so
+// the columns of n sequences are one run of 32 n bytes. Half index of
 // (k, column):
 __device__ __forceinline__ int frag_index(int k, int col) {
-  return (((k >> 5) * 64 + ((k >> 3) & 3) * 16 + col) << 3) + (k & 7);
+  return (((k >> 5) * 64 + ((k >> 3) & 3) * 16 + 2 * (col & 7) + (col >> 3)) << 3) + (k & 7);
 }
 // Store values v0, v1 at k, k + 1 (k even) of sequence s as hi and lo parts.
 __device__ __forceinline__ void put_frag2(half_t* f, int k, int s, float v0, float v1) {
