@@ -43,6 +43,36 @@ struct PfGemmArgs {
   int tiles_m, tiles_n;
 };
 
+// Write, or add to C, a wave's 64 x 64 block of results at (mw, nw): lane l
+// holds columns nw + 32 j + l % 32 and rows mw + 32 i + 8 (r / 4) +
+// 4 (l / 32) + r % 4 of register r of block (i, j). The accumulating form
+// reads a block's 16 old values first, from clamped in-range addresses
+// without a condition (a condition around each load made the compiler wait
+// for each in turn), then adds and stores the elements inside the matrix;
+// one block at a time keeps the registers within two waves per SIMD.
+template <int EPI>
+__device__ __forceinline__ void pf_write(const PfGemmArgs& a, const f32x16 (&acc)[2][2], int mw, int nw, int lane) {
+  auto row = [&](int i, int r) { return mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = nw + j * 32 + (lane & 31);
+      f32x16 old;
+      if constexpr (EPI == kPfAccum) {
+        const int nc = min(n, a.N - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) old[r] = a.C[static_cast<size_t>(min(row(i, r), a.M - 1)) * a.N + nc];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = row(i, r);
+        if (m < a.M && n < a.N)
+          a.C[static_cast<size_t>(m) * a.N + n] = EPI == kPfAccum ? old[r] + acc[i][j][r] : acc[i][j][r];
+      }
+    }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
   __shared__ __attribute__((aligned(16))) half_t As[kPfBM * kPfLd];  // hi parts of the activations
@@ -127,23 +157,147 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
     }
   }
 
+  pf_write<EPI>(a, acc, m0 + wm * 64, n0 + wn * 64, lane);
+}
+
+// The same product on a 128 x 256 workgroup tile of eight 64 x 64 waves, for
+// grids that fill the device (one workgroup per CU: 144 KB of LDS). Measured
+// on the prompt pass's shapes, the single-buffered kernel above waits on its
+// global loads: they are issued one K step ahead, and without them it runs
+// about 40% faster. Here the LDS holds two K steps and the registers two
+// more, so a step's loads have two compute phases to land: K step s is read
+// into a register set during step s - 2, split into hi / lo and written to
+// LDS stage s % 2 at the end of step s - 1, and multiplied during step s,
+// with one barrier per step. The wider tile reads a third fewer bytes of
+// operands from L2 per flop. Loads go through buffer descriptors (one per
+// operand, from the tile's first row) with a 32-bit per-lane offset, which
+// keeps 64-bit addresses out of the vector registers. K steps past the last
+// (an odd count is rounded up to even) and the k past K of the last step
+// load clamped in-range data (the row's last chunk) and are written to LDS
+// as zeros.
+constexpr int kPf2BN = 256, kPf2Threads = 512;
+constexpr int kPf2Stage = (2 * kPfBM + kPf2BN) * kPfLd;  // halves per LDS stage (A hi, A lo, W)
+constexpr int kPf2Lds = 2 * kPf2Stage * static_cast<int>(sizeof(half_t));
+
+template <int EPI>
+__global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) half_t pf2_lds[];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int T = a.tiles_m * a.tiles_n, b = blockIdx.x;
+  const int t = (T & 7) ? b : (b & 7) * (T >> 3) + (b >> 3);  // XCD c: the c-th eighth of the tiles, N-major
+  const int m0 = (t % a.tiles_m) * kPfBM, n0 = (t / a.tiles_m) * kPf2BN;
+
+  // loader: per K step a thread loads NA chunks of 4 activations (rows
+  // arow + ARS i, floats acol ..) and NB chunks of 8 weights (rows lrow + BRS i,
+  // halves lcol ..); rows past the matrix load its last row (results unused)
+  constexpr int ACR = kPfBK / 4, ARS = kPf2Threads / ACR, NA = kPfBM / ARS;
+  constexpr int BCR = kPfBK / 8, BRS = kPf2Threads / BCR, NB = kPf2BN / BRS;
+  const int lrow = tid / BCR, lcol = (tid % BCR) * 8;
+  const int arow = tid / ACR, acol = (tid % ACR) * 4;
+  const size_t abytes = static_cast<size_t>(a.M - m0) * a.K * sizeof(float);
+  const size_t bbytes = static_cast<size_t>(a.N - n0) * a.K * sizeof(half_t);
+  const rsrc_t ar = rsrc_of(a.A + static_cast<size_t>(m0) * a.K, static_cast<int>(min(abytes, size_t(0x7fffffff))));
+  const rsrc_t br = rsrc_of(a.W + static_cast<size_t>(n0) * a.K, static_cast<int>(min(bbytes, size_t(0x7fffffff))));
+  int arow_off[NA], brow_off[NB];  // elements from the descriptor's base to the row
+#pragma unroll
+  for (int i = 0; i < NA; ++i) arow_off[i] = min(arow + ARS * i, a.M - 1 - m0) * a.K;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) brow_off[i] = min(lrow + BRS * i, a.N - 1 - n0) * a.K;
+  const int nsteps = (a.K + kPfBK - 1) / kPfBK;
+
+  f32x4 ra0[NA], ra1[NA];
+  u32x4 rb0[NB], rb1[NB];
+  auto load = [&](f32x4 (&ra)[NA], u32x4 (&rb)[NB], int step) {
+    const int k0 = min(step, nsteps - 1) * kPfBK;
+    const int ka = min(k0 + acol, a.K - 4), kb = min(k0 + lcol, a.K - 8);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      ra[i] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, (arow_off[i] + ka) * static_cast<int>(sizeof(float)), 0, 0));
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, (brow_off[i] + kb) * static_cast<int>(sizeof(half_t)), 0, 0);
+  };
+  auto store = [&](const f32x4 (&ra)[NA], const u32x4 (&rb)[NB], int step, half_t* stage) {
+    half_t* As = stage;
+    half_t* Al = As + kPfBM * kPfLd;
+    half_t* Bs = Al + kPfBM * kPfLd;
+    const int k0 = step * kPfBK;
+    const bool ina = k0 + acol < a.K, inb = k0 + lcol < a.K;  // K is a multiple of 8
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      h4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = ina ? ra[i][e] : 0.f;
+        hi[e] = static_cast<half_t>(v);
+        lo[e] = static_cast<half_t>(v - static_cast<float>(hi[e]));
+      }
+      *reinterpret_cast<h4*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
+      *reinterpret_cast<h4*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
+    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4*>(&Bs[(lrow + BRS * i) * kPfLd + lcol]) = inb ? rb[i] : z;
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < a.M && n < a.N) {
-          float* c = a.C + static_cast<size_t>(m) * a.N + n;
-          if constexpr (EPI == kPfAccum)
-            *c += acc[i][j][r];
-          else
-            *c = acc[i][j][r];
-        }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto compute = [&](const half_t* stage) {
+    const half_t* As = stage;
+    const half_t* Al = As + kPfBM * kPfLd;
+    const half_t* Bs = Al + kPfBM * kPfLd;
+#pragma unroll
+    for (int kk = 0; kk < kPfBK / 16; ++kk) {
+      h8 af[2], al[2], bf[2];
+      const int col = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const h8*>(&As[(wm * 64 + i * 32 + (lane & 31)) * kPfLd + col]);
+        al[i] = *reinterpret_cast<const h8*>(&Al[(wm * 64 + i * 32 + (lane & 31)) * kPfLd + col]);
+        bf[i] = *reinterpret_cast<const h8*>(&Bs[(wn * 64 + i * 32 + (lane & 31)) * kPfLd + col]);
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bf[j], acc[i][j], 0, 0, 0);
+        }
     }
+  };
+
+  half_t* st0 = pf2_lds;
+  half_t* st1 = pf2_lds + kPf2Stage;
+  load(ra0, rb0, 0);
+  load(ra1, rb1, 1);
+  store(ra0, rb0, 0, st0);
+  __syncthreads();
+  // Each step issues its loads first (the scheduling barriers keep them
+  // there), then multiplies its stage, then writes the next step's stage
+  // (free since the barrier that ended the step before).
+  for (int s = 0; s < nsteps; s += 2) {
+    load(ra0, rb0, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st0);
+    __builtin_amdgcn_sched_barrier(0);
+    store(ra1, rb1, s + 1, st1);
+    __syncthreads();
+    load(ra1, rb1, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(ra0, rb0, s + 2, st0);
+    __syncthreads();
+  }
+
+  pf_write<EPI>(a, acc, m0 + wm * 64, n0 + wn * 64, lane);
 }
 
 // ---------------------------------------------------------- attention

@@ -258,6 +258,7 @@ struct lf_model {
   std::vector<GraphEntry> graphs;
   std::vector<BatchGraph> batch_graphs;
   int battn_room = 1;                    // batched attention workgroups the device holds at once
+  int ncu = 256;                         // compute units of the device (read at init)
   void* scratch = nullptr;               // this device's address of the static prompt-pass scratch
 
   template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -493,6 +494,10 @@ int set_lds_limits() {
   if ((rc = set_lds_limit_epi<lf::kEpiQKV>()) || (rc = set_lds_limit_epi<lf::kEpiSwiGLU>()) ||
       (rc = set_lds_limit_epi<lf::kEpiResid>()) || (rc = set_lds_limit_epi<lf::kEpiLogits>()))
     return rc;
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_pf_gemm_db<lf::kPfStore>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lf::kPf2Lds));
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_pf_gemm_db<lf::kPfAccum>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lf::kPf2Lds));
   return LF_OK;
 }
 
@@ -927,9 +932,17 @@ PfLayout pf_layout(const Dims& D, int mc) {
   return P;
 }
 
+// The double-buffered 128 x 256 kernel where its grid gives every CU a
+// workgroup (it holds one per CU), else the 128 x 128 one (two per CU).
 template <int EPI>
-void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int K, hipStream_t st) {
-  lf::PfGemmArgs g{A, W, C, M, N, K, (M + lf::kPfBM - 1) / lf::kPfBM, (N + lf::kPfBN - 1) / lf::kPfBN};
+void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int K, int ncu, hipStream_t st) {
+  const int tm = (M + lf::kPfBM - 1) / lf::kPfBM, tn2 = (N + lf::kPf2BN - 1) / lf::kPf2BN;
+  if (tm * tn2 >= ncu) {
+    lf::PfGemmArgs g{A, W, C, M, N, K, tm, tn2};
+    hipLaunchKernelGGL(lf::k_pf_gemm_db<EPI>, dim3(tm * tn2), dim3(lf::kPf2Threads), lf::kPf2Lds, st, g);
+    return;
+  }
+  lf::PfGemmArgs g{A, W, C, M, N, K, tm, (N + lf::kPfBN - 1) / lf::kPfBN};
   hipLaunchKernelGGL(lf::k_pf_gemm<EPI>, dim3(g.tiles_m * g.tiles_n), dim3(lf::kPfThreads), 0, st, g);
 }
 
@@ -964,20 +977,20 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
     lf::PfNormArgs na{x, h, m->at<half_t>(W.g1[l]), l == 0 ? m->at<half_t>(W.embed) : nullptr, kv->tokens(), kv->state(),
                       M, D.d, D.V, pos0, c.rms_eps};
     hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
-    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wqkv[l]), y, M, D.qkv_rows, D.d, st);
+    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wqkv[l]), y, M, D.qkv_rows, D.d, m->ncu, st);
     lf::PfQkvArgs qa{y, q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, m->at<float2>(W.rope),
                      M, D.qkv_rows, D.hd, D.qpl, D.kpl, D.hq, D.ctx, pos0};
     hipLaunchKernelGGL(lf::k_pf_qkv, dim3((D.qkv_rows / 2 + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, qa);
     lf::PfAttnArgs aa{q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, h, M, pos0, D.ctx, c.window[l], D.kpl,
                       D.hq, static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)))};
     launch_pf_attn(aa, D.hd, D.G, D.hkv, st);
-    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wo[l]), x, M, D.d, D.qdim, st);
+    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wo[l]), x, M, D.d, D.qdim, m->ncu, st);
     na.gain = m->at<half_t>(W.g2[l]);
     na.emb = nullptr;
     hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
-    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, st);
+    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, m->ncu, st);
     hipLaunchKernelGGL(lf::k_pf_swiglu, dim3((D.ffn + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, y, h, D.ffn);
-    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, st);
+    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, st);
   }
 }
 
@@ -1225,6 +1238,7 @@ int lf_model_init(const lf_config* cfg, const lf_weight_ptrs* w, void* d_workspa
   if ((rc = plan_attention(*cfg, ncu, attn_per_cu, fused_per_cu, m->xcd_classes, m->fused_ok, m->attn_xcd)))
     return bail(rc);
   m->fused = m->fused_ok;
+  m->ncu = ncu;
   if (m->D.V) {  // the batched step's attention kernels (lf_decode_step_batch needs a vocabulary)
     int per_cu = 1 << 20;
     for (int u : {4, 8, 16, 0}) {
