@@ -30,6 +30,15 @@ MHA = DecoderConfig("mha", n_layers=2, d_model=384, n_q_heads=3, n_kv_heads=3, h
                     vocab=600, n_lanes=3, max_ctx=200, windows=(0, 45))
 
 
+# Projections wide enough, over a prompt long enough, that the 128 x 256
+# double-buffered GEMM runs (its grid fills the device) on ragged tiles: 4000
+# positions in one chunk (the last 128-row tile holds 32 rows), gate/up 2000
+# rows and O / down 2056 rows (part-filled last 256-row tiles), K = 2056 and
+# 1000 (a part-filled last K step, and an odd number of K steps).
+WIDE_RAGGED = DecoderConfig("wide_ragged", n_layers=2, d_model=2056, n_q_heads=8, n_kv_heads=4, head_dim=64,
+                            ffn=1000, vocab=1000, n_lanes=4, max_ctx=4096, windows=(0, 300))
+
+
 def say(*a):
     print(*a, flush=True)
 
@@ -161,6 +170,39 @@ def test_prefill_batched_argument_errors():
         C.lf_prefill_batched(dec.handle, seq.handle, toks, 8, ws)
     assert e.value.code == C.LF_ERANGE
     assert seq.len == cfg.max_ctx - 4
+
+
+@pytest.mark.timeout(600)
+def test_prefill_batched_wide_ragged_tiles():
+    """WIDE_RAGGED: a 4000-position prompt as one chunk, then 2 decode steps:
+    the last position's logits, the caches and the steps against the oracle."""
+    import torch
+    from decode_step_05_amd import Decoder
+
+    cfg, plen, steps = WIDE_RAGGED, 4000, 2
+    say(f"[prefill] cfg={cfg.name} prompt={plen} chunk={plen} steps={steps} seeds=(0,1)")
+    w = make_weights(cfg, seed=0)
+    prompt = make_prompt(cfg, plen, seed=1)
+    o = OracleDecoder(cfg, w)
+    cache = o.new_cache()
+    o.forward_sequence(tokens=prompt, cache=cache)
+    ref_z, ref_t = o.generate(prompt, steps)
+    say(f"[prefill] {cfg.name}: oracle done")
+    dec = Decoder(cfg, w)
+    seq = dec.sequence()
+    seq.prefill_batched(prompt, chunk=plen)
+    z, a = seq.logits()
+    z = z.cpu().numpy()
+    amax, rel = assert_close(z, ref_z[0], f"{cfg.name} last prompt position")
+    assert check_token(int(a.item()), ref_z[0], amax)
+    assert seq.status()[0] == plen
+    crel = _check_caches(seq, cache, plen, cfg.name)
+    for s in range(steps):
+        seq.step(int(ref_t[s]))
+        zs, _ = seq.logits()
+        assert_close(zs.cpu().numpy(), ref_z[s + 1], f"{cfg.name} decode step {s} after the batched pass")
+    torch.cuda.synchronize()
+    say(f"[prefill] {cfg.name}: logits max|d|={amax:.2e} rel={rel:.2e}, worst cache rel={crel:.2e}")
 
 
 @pytest.mark.timeout(600)
