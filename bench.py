@@ -38,10 +38,10 @@ PREFILL_CHUNK = 2048
 # WRITE_SIZE (a 512 MiB device copy reads as 0.5x FETCH_SIZE, writes as 1.0x
 # WRITE_SIZE; both factors applied), for the GEMV kernel sources whose sha256
 # is given: reported only while the sources are unchanged.
-GATE_UP_TRAFFIC = {"bytes": 118176004,
+GATE_UP_TRAFFIC = {"bytes": 118175985,
                    "sources": ("decode_step_05_amd/csrc/lf_device.h", "decode_step_05_amd/csrc/lf_exchange.h",
                                "decode_step_05_amd/csrc/lf_kernels.h"),
-                   "sha256": "54a1e459c99b8ebc62a8bfbc7afb5065b3d5c20b7ee4b4876a1b8ff4cea849ac"}
+                   "sha256": "82b47b42a3e7bfc227dcd168b563167ab7f5b027f59c82fc2067a8d4abb33779"}
 
 
 def measured_traffic(entry):
