@@ -227,3 +227,50 @@ def test_batch_full_model_at_ctx4096(n):
         st = q.status()
         assert st[0] == L + steps and st[2] == 0, st
     say(f"[batch] full model n={n}: worst max|d|={worst[0]:.2e} rel={worst[1]:.2e}")
+
+
+@pytest.mark.timeout(300)
+def test_batch_edge_positions():
+    """One batch whose sequences sit at the edges of the context: an empty
+    sequence (its first position attends to itself only), one cached key,
+    63, 64 and 65 cached keys around the 64-key window of the tiny decoder's
+    first layer, and the last position of the context (4095 cached keys):
+    each sequence's logits and greedy token against the oracle; then a step
+    of the batch, which now holds a full sequence, is refused."""
+    import torch
+    from decode_step_05_amd import Decoder
+    from decode_step_05_amd import lfdecode as C
+    cfg = TINY
+    lens = [0, 1, 63, 64, 65, cfg.max_ctx - 1]
+    toks = [5 + 37 * s for s in range(len(lens))]
+    say(f"[batch] edge positions cfg={cfg.name} cache lengths {lens} (seed 2) tokens {toks}")
+    w = make_weights(cfg, seed=0)
+    K, V = make_kv(cfg, max(lens), seed=2)
+    orc = OracleDecoder(cfg, w)
+    refs = []
+    for L, t in zip(lens, toks):
+        c = orc.new_cache()
+        if L:
+            orc.load_cache(c, K[:, :L], V[:, :L])
+        refs.append(orc.step(c, token=t))
+    dec = Decoder(cfg, w)
+    seqs = [dec.sequence() for _ in lens]
+    for q, L in zip(seqs, lens):
+        if L:
+            q.load_cache(K[:, :L], V[:, :L])
+        else:
+            q.set_len(0)
+    dec.step_batch(seqs, toks)
+    worst = (0.0, 0.0)
+    for s, q in enumerate(seqs):
+        z, a = q.logits()
+        ma, r = assert_close(z.cpu().numpy(), refs[s], f"edge seq {s} (p={lens[s]})")
+        worst = (max(worst[0], ma), max(worst[1], r))
+        assert check_token(int(a.item()), refs[s], ma), s
+        st = q.status()
+        assert st[0] == lens[s] + 1 and st[2] == 0, (s, st)
+    with pytest.raises(C.LfError) as e:
+        dec.step_batch(seqs, toks)
+    assert e.value.code == C.LF_ERANGE
+    torch.cuda.synchronize()
+    say(f"[batch] edge positions: worst max|d|={worst[0]:.2e} rel={worst[1]:.2e}")
