@@ -1304,6 +1304,14 @@ int lf_model_set_fused(lf_model* m, int enabled) {
 
 int lf_model_fused(const lf_model* m) { return m ? (m->fused ? 1 : 0) : -1; }
 
+int lf_model_raise_give_up(lf_model* m, void* stream) {
+  if (!m) return fail(LF_EINVAL, "model is null");
+  hipLaunchKernelGGL(lf::k_fill_u32, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), m->at<unsigned>(m->W.abort),
+                     1u, size_t(1));
+  LF_HIP(hipPeekAtLastError());
+  return LF_OK;
+}
+
 int lf_kv_alloc(lf_model* m, void* d_buf, size_t bytes, lf_kv** out) {
   if (!m || !d_buf || !out) return fail(LF_EINVAL, "null argument");
   *out = nullptr;

@@ -22,7 +22,8 @@ LF_MODE_EAGER, LF_MODE_GRAPH = 0, 1
 # Every symbol include/lfdecode.h declares.
 EXPORTS = (
     "lf_workspace_bytes", "lf_kv_bytes", "lf_model_init", "lf_model_free", "lf_model_set_graph",
-    "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused", "lf_plan_attention",
+    "lf_model_set_mode", "lf_model_mode", "lf_model_set_fused", "lf_model_fused", "lf_model_raise_give_up",
+    "lf_plan_attention",
     "lf_kv_alloc", "lf_kv_free", "lf_kv_cache_ptrs", "lf_kv_set_len", "lf_kv_len", "lf_kv_tokens", "lf_prefill",
     "lf_prefill_workspace_bytes", "lf_prefill_batched", "lf_prefill_batched_static",
     "lf_decode_step", "lf_decode_steps", "lf_decode_step_batch", "lf_decode_step_hidden", "lf_logits", "lf_kv_status",
@@ -72,6 +73,7 @@ def load():
         "lf_model_mode": (c_int, [P]),
         "lf_model_set_fused": (c_int, [P, c_int]),
         "lf_model_fused": (c_int, [P]),
+        "lf_model_raise_give_up": (c_int, [P, P]),
         "lf_plan_attention": (c_int, [POINTER(lf_config), c_int32, c_int32, c_int32, c_int32, POINTER(c_int32),
                                       POINTER(c_int32)]),
         "lf_kv_alloc": (c_int, [P, P, c_size_t, POINTER(P)]),
@@ -205,6 +207,10 @@ def lf_model_set_fused(model, enabled: bool) -> None:
 
 def lf_model_fused(model) -> bool:
     return load().lf_model_fused(model) == 1
+
+
+def lf_model_raise_give_up(model, stream=None) -> None:
+    _check(load().lf_model_raise_give_up(model, _stream(stream)))
 
 
 def lf_plan_attention(cfg: lf_config, n_cu: int, attn_wg_per_cu: int, fused_wg_per_cu: int, xcd_classes: bool):

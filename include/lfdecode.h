@@ -155,6 +155,16 @@ int lf_model_set_fused(lf_model* m, int enabled);
 int lf_model_fused(const lf_model* m);
 
 /*
+ * Raise the model's give-up flag (lf_kv_status bit 1) on stream, as an
+ * attention wait that ran out of polls would: every wait of the following
+ * steps gives up at once, their results are invalid, and the flag reads set
+ * until lf_kv_set_len on one of the model's sequences clears it. For callers
+ * and tests that check how an invalid step is reported and recovered from;
+ * no kernel faults or hangs. LF_EINVAL for a null model.
+ */
+int lf_model_raise_give_up(lf_model* m, void* stream);
+
+/*
  * Launch planning of the attention kernels (host only, no device work): what
  * lf_model_init chooses for a device with n_cu compute units that holds
  * attn_wg_per_cu workgroups of the split-KV attention kernel and

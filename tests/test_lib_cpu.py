@@ -108,6 +108,7 @@ def test_null_handles_rejected():
     lib.lf_kv_free(None)
     assert lib.lf_model_set_fused(None, 1) == C.LF_EINVAL
     assert lib.lf_model_fused(None) == -1
+    assert lib.lf_model_raise_give_up(None, None) == C.LF_EINVAL
 
 
 def test_read_bandwidth_argument_errors_before_any_device_call():
