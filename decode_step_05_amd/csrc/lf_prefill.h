@@ -33,7 +33,10 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kPfBM = 128, kPfBN = 128, kPfBK = 64, kPfThreads = 256;
 constexpr int kPfLd = kPfBK + 8;  // LDS row stride in halves (144 B: rows 4 banks apart)
 
-enum PfEpi : int { kPfStore = 0, kPfAccum = 1 };
+// kPfStore: C = A W^T; kPfAccum: C += A W^T; kPfSwiGLU: the gate/up product
+// (gate f and up f in weight rows 2f, 2f + 1) goes through SwiGLU into C
+// [M][N / 2]: C[m][f] = silu(gate) * up.
+enum PfEpi : int { kPfStore = 0, kPfAccum = 1, kPfSwiGLU = 2 };
 
 struct PfGemmArgs {
   const float* A;
@@ -49,10 +52,29 @@ struct PfGemmArgs {
 // reads a block's 16 old values first, from clamped in-range addresses
 // without a condition (a condition around each load made the compiler wait
 // for each in turn), then adds and stores the elements inside the matrix;
-// one block at a time keeps the registers within two waves per SIMD.
+// one block at a time keeps the registers within two waves per SIMD. The
+// SwiGLU form pairs column n (gate, even lanes) with column n + 1 (up, the
+// next lane) and stores one value per pair.
 template <int EPI>
 __device__ __forceinline__ void pf_write(const PfGemmArgs& a, const f32x16 (&acc)[2][2], int mw, int nw, int lane) {
   auto row = [&](int i, int r) { return mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
+  if constexpr (EPI == kPfSwiGLU) {
+    const int half = a.N >> 1;  // N even
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = nw + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float g = acc[i][j][r], up = lane_xor(g, 1);
+          const int m = row(i, r);
+          if ((lane & 1) == 0 && m < a.M && n < a.N)
+            a.C[static_cast<size_t>(m) * half + (n >> 1)] = g / (1.0f + expf(-g)) * up;
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -568,14 +590,6 @@ __global__ __launch_bounds__(kBlock) void k_pf_qkv(PfQkvArgs a) {
     dst[c] = static_cast<half_t>(y0);
     dst[c + half_hd] = static_cast<half_t>(y1);
   }
-}
-
-// SwiGLU over the gate/up GEMM's output (gate f and up f in columns 2f, 2f+1).
-__global__ __launch_bounds__(kBlock) void k_pf_swiglu(const float* y, float* act, int ffn) {
-  const int f = blockIdx.x * kBlock + threadIdx.x, t = blockIdx.y;
-  if (f >= ffn) return;
-  const float2 gu = reinterpret_cast<const float2*>(y + static_cast<size_t>(t) * 2 * ffn)[f];
-  act[static_cast<size_t>(t) * ffn + f] = gu.x / (1.0f + expf(-gu.x)) * gu.y;
 }
 
 // Hand the last prompt position's residual to the decode step's LM head and

@@ -498,6 +498,8 @@ int set_lds_limits() {
                              hipFuncAttributeMaxDynamicSharedMemorySize, lf::kPf2Lds));
   LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_pf_gemm_db<lf::kPfAccum>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, lf::kPf2Lds));
+  LF_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&lf::k_pf_gemm_db<lf::kPfSwiGLU>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lf::kPf2Lds));
   return LF_OK;
 }
 
@@ -988,9 +990,9 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
     na.gain = m->at<half_t>(W.g2[l]);
     na.emb = nullptr;
     hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
-    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, m->ncu, st);
-    hipLaunchKernelGGL(lf::k_pf_swiglu, dim3((D.ffn + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, y, h, D.ffn);
-    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, st);
+    // gate/up with SwiGLU in its epilogue: the activations [M][ffn] land in y
+    launch_pf_gemm<lf::kPfSwiGLU>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, m->ncu, st);
+    launch_pf_gemm<lf::kPfAccum>(y, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, st);
   }
 }
 
