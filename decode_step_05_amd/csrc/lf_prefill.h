@@ -534,24 +534,54 @@ struct PfNormArgs {
   float eps;
 };
 
+// One workgroup per row; a thread holds 4 consecutive elements per step in
+// registers between the sum of squares and the scaled store (d <= 8192 and
+// a multiple of 8: 16-byte loads and stores).
 __global__ __launch_bounds__(kBlock) void k_pf_norm(PfNormArgs a) {
+  constexpr int NV = 8192 / (4 * kBlock);
   __shared__ float red[kWavesPerBlock];
   const int t = blockIdx.x;
   float* x = a.x + static_cast<size_t>(t) * a.d;
+  const half_t* e = nullptr;
   if (a.emb) {
     int tok = a.tokens[a.tok0 + t];
     if (tok < 0 || tok >= a.vocab) {
       tok = tok < 0 ? 0 : a.vocab - 1;
       if (threadIdx.x == 0) a.state[kBadToken] = 1;
     }
-    const half_t* e = a.emb + static_cast<size_t>(tok) * a.d;
-    for (int i = threadIdx.x; i < a.d; i += kBlock) x[i] = static_cast<float>(e[i]);
+    e = a.emb + static_cast<size_t>(tok) * a.d;
   }
+  f32x4 v[NV];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < a.d; i += kBlock) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int i = (threadIdx.x + k * kBlock) * 4;
+    if (i < a.d) {
+      if (e) {
+        const h4 eh = *reinterpret_cast<const h4*>(e + i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[k][c] = static_cast<float>(eh[c]);
+        *reinterpret_cast<f32x4*>(x + i) = v[k];
+      } else {
+        v[k] = *reinterpret_cast<const f32x4*>(x + i);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ss = fmaf(v[k][c], v[k][c], ss);
+    }
+  }
   const float inv = rsqrtf(block_sum(ss, red) / a.d + a.eps);
   float* h = a.h + static_cast<size_t>(t) * a.d;
-  for (int i = threadIdx.x; i < a.d; i += kBlock) h[i] = x[i] * inv * static_cast<float>(a.gain[i]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int i = (threadIdx.x + k * kBlock) * 4;
+    if (i < a.d) {
+      const h4 g = *reinterpret_cast<const h4*>(a.gain + i);
+      f32x4 o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = v[k][c] * inv * static_cast<float>(g[c]);
+      *reinterpret_cast<f32x4*>(h + i) = o;
+    }
+  }
 }
 
 // Rotary embedding and cache append for the QKV GEMM's output, whose columns
