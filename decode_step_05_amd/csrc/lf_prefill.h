@@ -44,6 +44,11 @@ struct PfGemmArgs {
   float* C;
   int M, N, K;  // K a multiple of 8
   int tiles_m, tiles_n;
+  // k_pf_gemm_db only: tiles [full, tiles_m * tiles_n) are each computed as
+  // `split` pieces over equal runs of K steps (split 0: none), whose raw sums
+  // go to part ([piece][kPfBM][kPf2BN] fp32) for k_pf_fixup
+  int full, split;
+  float* part;
 };
 
 // Write, or add to C, a wave's 64 x 64 block of results at (mw, nw): lane l
@@ -201,12 +206,34 @@ constexpr int kPf2BN = 256, kPf2Threads = 512;
 constexpr int kPf2Stage = (2 * kPfBM + kPf2BN) * kPfLd;  // halves per LDS stage (A hi, A lo, W)
 constexpr int kPf2Lds = 2 * kPf2Stage * static_cast<int>(sizeof(half_t));
 
+//
+// The last, partly filled round of tiles would leave CUs idle (one
+// workgroup per CU, all tiles alike): those tiles can instead be split into
+// pieces over K steps, which fill the round, with their sums added by
+// k_pf_fixup. Workgroup b runs on XCD b mod 8; each XCD takes its eighth of
+// the whole tiles as a contiguous run (N-major, so the M tiles that share a
+// weight tile share an L2), then the pieces, dealt in turn, last.
 template <int EPI>
 __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) half_t pf2_lds[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int T = a.tiles_m * a.tiles_n, b = blockIdx.x;
-  const int t = (T & 7) ? b : (b & 7) * (T >> 3) + (b >> 3);  // XCD c: the c-th eighth of the tiles, N-major
+  const int nsteps_all = (a.K + kPfBK - 1) / kPfBK;
+  int t, piece = -1, s_begin = 0, s_end = nsteps_all;
+  if (a.split == 0) {
+    t = (T & 7) ? b : (b & 7) * (T >> 3) + (b >> 3);
+  } else {  // full and the number of pieces are multiples of 8
+    const int c = b & 7, r = b >> 3, per = a.full >> 3;
+    if (r < per) {
+      t = c * per + r;
+    } else {
+      piece = (r - per) * 8 + c;
+      t = a.full + piece / a.split;
+      const int q = (nsteps_all + a.split - 1) / a.split, j = piece % a.split;
+      s_begin = min(j * q, nsteps_all);
+      s_end = min(s_begin + q, nsteps_all);
+    }
+  }
   const int m0 = (t % a.tiles_m) * kPfBM, n0 = (t / a.tiles_m) * kPf2BN;
 
   // loader: per K step a thread loads NA chunks of 4 activations (rows
@@ -225,12 +252,12 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   for (int i = 0; i < NA; ++i) arow_off[i] = min(arow + ARS * i, a.M - 1 - m0) * a.K;
 #pragma unroll
   for (int i = 0; i < NB; ++i) brow_off[i] = min(lrow + BRS * i, a.N - 1 - n0) * a.K;
-  const int nsteps = (a.K + kPfBK - 1) / kPfBK;
+  const int kend = min(a.K, s_end * kPfBK);  // k past this are zero (a piece's K run ends here)
 
   f32x4 ra0[NA], ra1[NA];
   u32x4 rb0[NB], rb1[NB];
   auto load = [&](f32x4 (&ra)[NA], u32x4 (&rb)[NB], int step) {
-    const int k0 = min(step, nsteps - 1) * kPfBK;
+    const int k0 = max(min(step, s_end - 1), 0) * kPfBK;
     const int ka = min(k0 + acol, a.K - 4), kb = min(k0 + lcol, a.K - 8);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
@@ -245,7 +272,7 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
     half_t* Al = As + kPfBM * kPfLd;
     half_t* Bs = Al + kPfBM * kPfLd;
     const int k0 = step * kPfBK;
-    const bool ina = k0 + acol < a.K, inb = k0 + lcol < a.K;  // K is a multiple of 8
+    const bool ina = k0 + acol < kend, inb = k0 + lcol < kend;  // K is a multiple of 8
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       h4 hi, lo;
@@ -297,14 +324,14 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
 
   half_t* st0 = pf2_lds;
   half_t* st1 = pf2_lds + kPf2Stage;
-  load(ra0, rb0, 0);
-  load(ra1, rb1, 1);
-  store(ra0, rb0, 0, st0);
+  load(ra0, rb0, s_begin);
+  load(ra1, rb1, s_begin + 1);
+  store(ra0, rb0, s_begin, st0);
   __syncthreads();
   // Each step issues its loads first (the scheduling barriers keep them
   // there), then multiplies its stage, then writes the next step's stage
   // (free since the barrier that ended the step before).
-  for (int s = 0; s < nsteps; s += 2) {
+  for (int s = s_begin; s < s_end; s += 2) {
     load(ra0, rb0, s + 2);
     __builtin_amdgcn_sched_barrier(0);
     compute(st0);
@@ -319,7 +346,44 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
     __syncthreads();
   }
 
+  if (piece >= 0) {  // raw sums of the piece, tile-local [kPfBM][kPf2BN]
+    float* pp = a.part + static_cast<size_t>(piece) * kPfBM * kPf2BN;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          pp[row * kPf2BN + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][r];
+        }
+    return;
+  }
   pf_write<EPI>(a, acc, m0 + wm * 64, n0 + wn * 64, lane);
+}
+
+// The split tiles of a k_pf_gemm_db launch: the sum of each element's
+// pieces in a fixed order, then the launch's epilogue as pf_write applies
+// it. Workgroup (u, y): tile full + u, tile rows 8 y .. 8 y + 7; thread c
+// column c of the tile (for SwiGLU, gate and up columns in adjacent lanes).
+template <int EPI>
+__global__ __launch_bounds__(kPf2BN) void k_pf_fixup(PfGemmArgs a) {
+  const int u = blockIdx.x, t = a.full + u, c = threadIdx.x;
+  const int m0 = (t % a.tiles_m) * kPfBM, n = (t / a.tiles_m) * kPf2BN + c;
+  const float* pp = a.part + static_cast<size_t>(u) * a.split * kPfBM * kPf2BN + c;
+  for (int rr = 0; rr < 8; ++rr) {
+    const int row = blockIdx.y * 8 + rr, m = m0 + row;
+    float v = 0.f;
+    for (int j = 0; j < a.split; ++j) v += pp[(static_cast<size_t>(j) * kPfBM + row) * kPf2BN];
+    if constexpr (EPI == kPfSwiGLU) {
+      const float up = lane_xor(v, 1);
+      if ((c & 1) == 0 && m < a.M && n < a.N)
+        a.C[static_cast<size_t>(m) * (a.N >> 1) + (n >> 1)] = v / (1.0f + expf(-v)) * up;
+    } else if (m < a.M && n < a.N) {
+      float* dst = a.C + static_cast<size_t>(m) * a.N + n;
+      *dst = EPI == kPfAccum ? *dst + v : v;
+    }
+  }
 }
 
 // ---------------------------------------------------------- attention

@@ -934,14 +934,68 @@ PfLayout pf_layout(const Dims& D, int mc) {
   return P;
 }
 
+// Device scratch that a prompt-pass GEMM may use for the sums of split
+// tiles: `pieces` blocks of kPfBM x kPf2BN fp32 at p (none if p is null).
+struct PfPart {
+  float* p;
+  int pieces;
+};
+constexpr size_t kPfPieceBytes = static_cast<size_t>(lf::kPfBM) * lf::kPf2BN * sizeof(float);
+
+// The free bytes [from, to) of the chunk scratch as a PfPart.
+PfPart pf_part(char* ws, size_t from, size_t to) {
+  from = align_up(from);
+  if (to <= from) return {nullptr, 0};
+  const size_t n = std::min<size_t>((to - from) / kPfPieceBytes, 1 << 20);
+  return {n ? reinterpret_cast<float*>(ws + from) : nullptr, static_cast<int>(n)};
+}
+
+// How many K pieces to cut each tile of the last, partly filled round into
+// (0: none). With one workgroup per CU and T tiles of equal work the launch
+// takes ceil(T / ncu) rounds; splitting the R = T mod ncu tail tiles into s
+// pieces makes it floor(T / ncu) + ceil(R s / ncu) / s rounds, plus a fixup
+// pass that reads the pieces once. Taken where it saves at least a quarter of
+// a round; each piece keeps at least 4 K steps, and the XCD mapping of
+// k_pf_gemm_db wants the whole tiles and the pieces in multiples of 8.
+int pf_split(int T, int K, int ncu, int cap) {
+  const int R = T % ncu, nsteps = (K + lf::kPfBK - 1) / lf::kPfBK;
+  if (R == 0 || (T - R) % 8) return 0;
+  const double whole = T / ncu + 1;
+  double best = whole - 0.25;
+  int pick = 0;
+  for (int s = 2; s <= 8; ++s) {
+    if ((R * s) % 8 || R * s > cap || nsteps < 4 * s) continue;
+    const double rounds = T / ncu + static_cast<double>((R * s + ncu - 1) / ncu) / s;
+    if (rounds < best - 1e-9) {
+      best = rounds;
+      pick = s;
+    }
+  }
+  return pick;
+}
+
 // The double-buffered 128 x 256 kernel where its grid gives every CU a
-// workgroup (it holds one per CU), else the 128 x 128 one (two per CU).
+// workgroup (it holds one per CU), its tail tiles split over K where that
+// shortens the launch (part: scratch for their sums); else the 128 x 128
+// kernel (two per CU).
 template <int EPI>
-void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int K, int ncu, hipStream_t st) {
+void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int K, int ncu, PfPart part,
+                    hipStream_t st) {
   const int tm = (M + lf::kPfBM - 1) / lf::kPfBM, tn2 = (N + lf::kPf2BN - 1) / lf::kPf2BN;
-  if (tm * tn2 >= ncu) {
+  const int T = tm * tn2;
+  if (T >= ncu) {
     lf::PfGemmArgs g{A, W, C, M, N, K, tm, tn2};
-    hipLaunchKernelGGL(lf::k_pf_gemm_db<EPI>, dim3(tm * tn2), dim3(lf::kPf2Threads), lf::kPf2Lds, st, g);
+    const int s = part.p ? pf_split(T, K, ncu, part.pieces) : 0;
+    if (s == 0) {
+      hipLaunchKernelGGL(lf::k_pf_gemm_db<EPI>, dim3(T), dim3(lf::kPf2Threads), lf::kPf2Lds, st, g);
+      return;
+    }
+    const int R = T % ncu;
+    g.full = T - R;
+    g.split = s;
+    g.part = part.p;
+    hipLaunchKernelGGL(lf::k_pf_gemm_db<EPI>, dim3(g.full + R * s), dim3(lf::kPf2Threads), lf::kPf2Lds, st, g);
+    hipLaunchKernelGGL(lf::k_pf_fixup<EPI>, dim3(R, lf::kPfBM / 8), dim3(lf::kPf2BN), 0, st, g);
     return;
   }
   lf::PfGemmArgs g{A, W, C, M, N, K, tm, (N + lf::kPfBN - 1) / lf::kPfBN};
@@ -975,24 +1029,30 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
   float* y = reinterpret_cast<float*>(ws + P.y);
   float* h = reinterpret_cast<float*>(ws + P.h);
   float* q = reinterpret_cast<float*>(ws + P.q);
+  // Scratch free during each GEMM, for split-tile sums: past the normed
+  // input in h through q (QKV, gate/up), y (O: its QKV rows are consumed),
+  // h through q (down: its input is y).
+  const size_t rows = static_cast<size_t>(M);
+  const PfPart past_norm = pf_part(ws, P.h + rows * D.d * sizeof(float), P.total);
+  const PfPart in_y = pf_part(ws, P.y, P.h), from_h = pf_part(ws, P.h, P.total);
   for (int l = 0; l < D.L; ++l) {
     lf::PfNormArgs na{x, h, m->at<half_t>(W.g1[l]), l == 0 ? m->at<half_t>(W.embed) : nullptr, kv->tokens(), kv->state(),
                       M, D.d, D.V, pos0, c.rms_eps};
     hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
-    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wqkv[l]), y, M, D.qkv_rows, D.d, m->ncu, st);
+    launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wqkv[l]), y, M, D.qkv_rows, D.d, m->ncu, past_norm, st);
     lf::PfQkvArgs qa{y, q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, m->at<float2>(W.rope),
                      M, D.qkv_rows, D.hd, D.qpl, D.kpl, D.hq, D.ctx, pos0};
     hipLaunchKernelGGL(lf::k_pf_qkv, dim3((D.qkv_rows / 2 + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, qa);
     lf::PfAttnArgs aa{q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, h, M, pos0, D.ctx, c.window[l], D.kpl,
                       D.hq, static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)))};
     launch_pf_attn(aa, D.hd, D.G, D.hkv, st);
-    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wo[l]), x, M, D.d, D.qdim, m->ncu, st);
+    launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wo[l]), x, M, D.d, D.qdim, m->ncu, in_y, st);
     na.gain = m->at<half_t>(W.g2[l]);
     na.emb = nullptr;
     hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
     // gate/up with SwiGLU in its epilogue: the activations [M][ffn] land in y
-    launch_pf_gemm<lf::kPfSwiGLU>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, m->ncu, st);
-    launch_pf_gemm<lf::kPfAccum>(y, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, st);
+    launch_pf_gemm<lf::kPfSwiGLU>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, m->ncu, past_norm, st);
+    launch_pf_gemm<lf::kPfAccum>(y, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, from_h, st);
   }
 }
 
