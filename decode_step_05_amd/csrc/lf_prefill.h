@@ -9,7 +9,10 @@
 // sliding-window attention on some layers). Activations stay fp32 as in the
 // decode step: an fp32 operand of a matrix instruction is fed as the sum of
 // two fp16 parts (hi = fp16(a), lo = fp16(a - hi), about 22 significant bits),
-// each multiplied with the fp16 weights or values, fp32 accumulation.
+// each multiplied with the fp16 weights or values, fp32 accumulation. The
+// kernels that produce a GEMM's activations store them already split (see
+// split4), so that the split is done once per element rather than once per
+// weight tile that reads it.
 #pragma once
 #include "lf_device.h"
 #include "lf_kernels.h"  // lds_barrier
@@ -20,10 +23,32 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// Split activations: a row of K fp32 values a[k] is stored as K / 4 groups
+// of 16 bytes, group g holding fp16 hi parts of a[4g .. 4g + 3], then their
+// lo parts (hi = fp16(a), lo = fp16(a - hi)), so a row takes the bytes of its
+// fp32 values and a GEMM's loader copies hi and lo straight into LDS.
+__device__ __forceinline__ u32x4 split4(f32x4 v) {
+  h8 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = static_cast<half_t>(v[e]);
+    o[e + 4] = static_cast<half_t>(v[e] - static_cast<float>(o[e]));
+  }
+  return __builtin_bit_cast(u32x4, o);
+}
+
+// Element k of a split row (2 K halves from row).
+__device__ __forceinline__ void put_split(half_t* row, int k, float v) {
+  const half_t hi = static_cast<half_t>(v);
+  half_t* g = row + (k >> 2) * 8 + (k & 3);
+  g[0] = hi;
+  g[4] = static_cast<half_t>(v - static_cast<float>(hi));
+}
+
 // ---------------------------------------------------------------- GEMM
-// C[M][N] (=, +=) A[M][K] · W[N][K]^T. A: activations, fp32 row-major, split
-// into hi and lo fp16 parts on the way into LDS; W: a weight matrix as the
-// model stores it, fp16 row-major [out][in]; C fp32.
+// C[M][N] (=, +=) A[M][K] · W[N][K]^T. A: activations, split rows (above);
+// W: a weight matrix as the model stores it, fp16 row-major [out][in]; C
+// fp32 (split rows of N / 2 for SwiGLU).
 // Workgroup tile 128 x 128, K step 64, four waves of 64 x 64 (2 x 2 blocks of
 // 32 x 32). A 32x32x16 matrix instruction takes, in lane l, row l % 32 of its
 // A block and column l % 32 of its B block with 8 consecutive k each (k group
@@ -35,11 +60,11 @@ constexpr int kPfLd = kPfBK + 8;  // LDS row stride in halves (144 B: rows 4 ban
 
 // kPfStore: C = A W^T; kPfAccum: C += A W^T; kPfSwiGLU: the gate/up product
 // (gate f and up f in weight rows 2f, 2f + 1) goes through SwiGLU into C
-// [M][N / 2]: C[m][f] = silu(gate) * up.
+// [M][N / 2] as split rows: C[m][f] = silu(gate) * up.
 enum PfEpi : int { kPfStore = 0, kPfAccum = 1, kPfSwiGLU = 2 };
 
 struct PfGemmArgs {
-  const float* A;
+  const half_t* A;  // split rows: 2 K halves each
   const half_t* W;
   float* C;
   int M, N, K;  // K a multiple of 8
@@ -64,7 +89,7 @@ template <int EPI>
 __device__ __forceinline__ void pf_write(const PfGemmArgs& a, const f32x16 (&acc)[2][2], int mw, int nw, int lane) {
   auto row = [&](int i, int r) { return mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
   if constexpr (EPI == kPfSwiGLU) {
-    const int half = a.N >> 1;  // N even
+    half_t* C = reinterpret_cast<half_t*>(a.C);  // split rows of N / 2 (N even): N halves each
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -75,7 +100,7 @@ __device__ __forceinline__ void pf_write(const PfGemmArgs& a, const f32x16 (&acc
           const float g = acc[i][j][r], up = lane_xor(g, 1);
           const int m = row(i, r);
           if ((lane & 1) == 0 && m < a.M && n < a.N)
-            a.C[static_cast<size_t>(m) * half + (n >> 1)] = g / (1.0f + expf(-g)) * up;
+            put_split(C + static_cast<size_t>(m) * a.N, n >> 1, g / (1.0f + expf(-g)) * up);
         }
       }
     return;
@@ -119,20 +144,19 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
   constexpr int BCR = kPfBK / 8, BRS = kPfThreads / BCR, NB = kPfBN / BRS;
   const int lrow = tid / BCR, lcol = (tid % BCR) * 8;
   const int arow = tid / ACR, acol = (tid % ACR) * 4;
-  const float* ap[NA];
+  const half_t* ap[NA];  // split rows: 4 activations in 8 halves
   const half_t* bp[NB];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) ap[i] = a.A + static_cast<size_t>(min(m0 + arow + ARS * i, a.M - 1)) * a.K + acol;
+  for (int i = 0; i < NA; ++i) ap[i] = a.A + (static_cast<size_t>(min(m0 + arow + ARS * i, a.M - 1)) * a.K + acol) * 2;
 #pragma unroll
   for (int i = 0; i < NB; ++i) bp[i] = a.W + static_cast<size_t>(min(n0 + lrow + BRS * i, a.N - 1)) * a.K + lcol;
-  f32x4 ra[NA];
+  u32x4 ra[NA];
   u32x4 rb[NB];
   auto load = [&](int k0) {
     const bool ina = k0 + acol < a.K, inb = k0 + lcol < a.K;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ra[i] = ina ? *reinterpret_cast<const f32x4*>(ap[i] + k0) : zf;
+    for (int i = 0; i < NA; ++i) ra[i] = ina ? ld16(ap[i] + 2 * k0) : z;
 #pragma unroll
     for (int i = 0; i < NB; ++i) rb[i] = inb ? ld16(bp[i] + k0) : z;
   };
@@ -151,14 +175,9 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
     __syncthreads();  // every wave is done reading the previous K step
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      h4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = static_cast<half_t>(ra[i][e]);
-        lo[e] = static_cast<half_t>(ra[i][e] - static_cast<float>(hi[e]));
-      }
-      *reinterpret_cast<h4*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
-      *reinterpret_cast<h4*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
+      const u32x2 hi = {ra[i][0], ra[i][1]}, lo = {ra[i][2], ra[i][3]};
+      *reinterpret_cast<u32x2*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
+      *reinterpret_cast<u32x2*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4*>(&Bs[(lrow + BRS * i) * kPfLd + lcol]) = rb[i];
@@ -243,9 +262,9 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   constexpr int BCR = kPfBK / 8, BRS = kPf2Threads / BCR, NB = kPf2BN / BRS;
   const int lrow = tid / BCR, lcol = (tid % BCR) * 8;
   const int arow = tid / ACR, acol = (tid % ACR) * 4;
-  const size_t abytes = static_cast<size_t>(a.M - m0) * a.K * sizeof(float);
+  const size_t abytes = static_cast<size_t>(a.M - m0) * a.K * 4;  // split rows: 4 bytes per activation
   const size_t bbytes = static_cast<size_t>(a.N - n0) * a.K * sizeof(half_t);
-  const rsrc_t ar = rsrc_of(a.A + static_cast<size_t>(m0) * a.K, static_cast<int>(min(abytes, size_t(0x7fffffff))));
+  const rsrc_t ar = rsrc_of(a.A + static_cast<size_t>(m0) * a.K * 2, static_cast<int>(min(abytes, size_t(0x7fffffff))));
   const rsrc_t br = rsrc_of(a.W + static_cast<size_t>(n0) * a.K, static_cast<int>(min(bbytes, size_t(0x7fffffff))));
   int arow_off[NA], brow_off[NB];  // elements from the descriptor's base to the row
 #pragma unroll
@@ -254,20 +273,19 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   for (int i = 0; i < NB; ++i) brow_off[i] = min(lrow + BRS * i, a.N - 1 - n0) * a.K;
   const int kend = min(a.K, s_end * kPfBK);  // k past this are zero (a piece's K run ends here)
 
-  f32x4 ra0[NA], ra1[NA];
+  u32x4 ra0[NA], ra1[NA];
   u32x4 rb0[NB], rb1[NB];
-  auto load = [&](f32x4 (&ra)[NA], u32x4 (&rb)[NB], int step) {
+  auto load = [&](u32x4 (&ra)[NA], u32x4 (&rb)[NB], int step) {
     const int k0 = max(min(step, s_end - 1), 0) * kPfBK;
     const int ka = min(k0 + acol, a.K - 4), kb = min(k0 + lcol, a.K - 8);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      ra[i] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, (arow_off[i] + ka) * static_cast<int>(sizeof(float)), 0, 0));
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, (arow_off[i] + ka) * 4, 0, 0);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, (brow_off[i] + kb) * static_cast<int>(sizeof(half_t)), 0, 0);
   };
-  auto store = [&](const f32x4 (&ra)[NA], const u32x4 (&rb)[NB], int step, half_t* stage) {
+  auto store = [&](const u32x4 (&ra)[NA], const u32x4 (&rb)[NB], int step, half_t* stage) {
     half_t* As = stage;
     half_t* Al = As + kPfBM * kPfLd;
     half_t* Bs = Al + kPfBM * kPfLd;
@@ -275,15 +293,9 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
     const bool ina = k0 + acol < kend, inb = k0 + lcol < kend;  // K is a multiple of 8
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      h4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = ina ? ra[i][e] : 0.f;
-        hi[e] = static_cast<half_t>(v);
-        lo[e] = static_cast<half_t>(v - static_cast<float>(hi[e]));
-      }
-      *reinterpret_cast<h4*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
-      *reinterpret_cast<h4*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
+      const u32x2 hi = {ina ? ra[i][0] : 0u, ina ? ra[i][1] : 0u}, lo = {ina ? ra[i][2] : 0u, ina ? ra[i][3] : 0u};
+      *reinterpret_cast<u32x2*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
+      *reinterpret_cast<u32x2*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
     }
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(kPf2BN) void k_pf_fixup(PfGemmArgs a) {
     if constexpr (EPI == kPfSwiGLU) {
       const float up = lane_xor(v, 1);
       if ((c & 1) == 0 && m < a.M && n < a.N)
-        a.C[static_cast<size_t>(m) * (a.N >> 1) + (n >> 1)] = v / (1.0f + expf(-v)) * up;
+        put_split(reinterpret_cast<half_t*>(a.C) + static_cast<size_t>(m) * a.N, n >> 1, v / (1.0f + expf(-v)) * up);
     } else if (m < a.M && n < a.N) {
       float* dst = a.C + static_cast<size_t>(m) * a.N + n;
       *dst = EPI == kPfAccum ? *dst + v : v;
@@ -405,7 +417,7 @@ struct PfAttnArgs {
   const float* q;    // [M][n_q][hd] rotated queries of the chunk
   const half_t* kc;  // this layer's K cache [lanes][max_ctx][kpl][hd], keys 0..pos0+M-1 written
   const half_t* vc;
-  float* o;          // [M][n_q * hd] attention outputs (input of the O projection)
+  half_t* o;         // [M][n_q * hd] attention outputs as split rows (input of the O projection)
   int M, pos0, max_ctx, window, kpl, n_q;
   float scale_log2;  // log2(e) / sqrt(hd)
 };
@@ -574,13 +586,16 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  if (qrow < a.M) {
+  if (qrow < a.M) {  // registers 4 u .. 4 u + 3: head dimensions th 32 + 8 u + 4 grp + 0..3, one split group
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = a.o + static_cast<size_t>(qrow) * a.n_q * HD + head * HD;
+    half_t* op = a.o + (static_cast<size_t>(qrow) * a.n_q * HD + head * HD) * 2;
 #pragma unroll
     for (int th = 0; th < HD / 32; ++th)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) op[th * 32 + 8 * (r >> 2) + 4 * grp + (r & 3)] = ot[th][r] * inv;
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 v = {ot[th][4 * u] * inv, ot[th][4 * u + 1] * inv, ot[th][4 * u + 2] * inv, ot[th][4 * u + 3] * inv};
+        *reinterpret_cast<u32x4*>(op + (th * 32 + 8 * u + 4 * grp) * 2) = split4(v);
+      }
   }
 }
 
@@ -589,7 +604,7 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
 // with emb set, the row is first loaded from the embedding of its token.
 struct PfNormArgs {
   float* x;            // [M][d] residual
-  float* h;            // [M][d]
+  half_t* h;           // [M][d] split rows (the GEMMs' input)
   const half_t* gain;
   const half_t* emb;   // [vocab][d], or null
   const int32_t* tokens;
@@ -634,7 +649,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(PfNormArgs a) {
     }
   }
   const float inv = rsqrtf(block_sum(ss, red) / a.d + a.eps);
-  float* h = a.h + static_cast<size_t>(t) * a.d;
+  half_t* h = a.h + static_cast<size_t>(t) * a.d * 2;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int i = (threadIdx.x + k * kBlock) * 4;
@@ -643,7 +658,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(PfNormArgs a) {
       f32x4 o;
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[c] = v[k][c] * inv * static_cast<float>(g[c]);
-      *reinterpret_cast<f32x4*>(h + i) = o;
+      *reinterpret_cast<u32x4*>(h + 2 * i) = split4(o);
     }
   }
 }

@@ -979,7 +979,7 @@ int pf_split(int T, int K, int ncu, int cap) {
 // shortens the launch (part: scratch for their sums); else the 128 x 128
 // kernel (two per CU).
 template <int EPI>
-void launch_pf_gemm(const float* A, const half_t* W, float* C, int M, int N, int K, int ncu, PfPart part,
+void launch_pf_gemm(const half_t* A, const half_t* W, float* C, int M, int N, int K, int ncu, PfPart part,
                     hipStream_t st) {
   const int tm = (M + lf::kPfBM - 1) / lf::kPfBM, tn2 = (N + lf::kPf2BN - 1) / lf::kPf2BN;
   const int T = tm * tn2;
@@ -1027,7 +1027,8 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
   const size_t layer_cache = static_cast<size_t>(D.lanes) * D.ctx * D.kpl * D.hd;
   float* x = reinterpret_cast<float*>(ws + P.x);
   float* y = reinterpret_cast<float*>(ws + P.y);
-  float* h = reinterpret_cast<float*>(ws + P.h);
+  half_t* h = reinterpret_cast<half_t*>(ws + P.h);  // GEMM inputs: split rows (4 bytes per activation)
+  half_t* ys = reinterpret_cast<half_t*>(ws + P.y);  // the SwiGLU output, split rows
   float* q = reinterpret_cast<float*>(ws + P.q);
   // Scratch free during each GEMM, for split-tile sums: past the normed
   // input in h through q (QKV, gate/up), y (O: its QKV rows are consumed),
@@ -1050,9 +1051,9 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
     na.gain = m->at<half_t>(W.g2[l]);
     na.emb = nullptr;
     hipLaunchKernelGGL(lf::k_pf_norm, dim3(M), dim3(lf::kBlock), 0, st, na);
-    // gate/up with SwiGLU in its epilogue: the activations [M][ffn] land in y
+    // gate/up with SwiGLU in its epilogue: the activations [M][ffn] land in y as split rows
     launch_pf_gemm<lf::kPfSwiGLU>(h, m->at<half_t>(W.wgu[l]), y, M, 2 * D.ffn, D.d, m->ncu, past_norm, st);
-    launch_pf_gemm<lf::kPfAccum>(y, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, from_h, st);
+    launch_pf_gemm<lf::kPfAccum>(ys, m->at<half_t>(W.wd[l]), x, M, D.d, D.ffn, m->ncu, from_h, st);
   }
 }
 
