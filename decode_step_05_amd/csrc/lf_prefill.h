@@ -230,8 +230,19 @@ constexpr int kPf2Lds = 2 * kPf2Stage * static_cast<int>(sizeof(half_t));
 // workgroup per CU, all tiles alike): those tiles can instead be split into
 // pieces over K steps, which fill the round, with their sums added by
 // k_pf_fixup. Workgroup b runs on XCD b mod 8; each XCD takes its eighth of
-// the whole tiles as a contiguous run (N-major, so the M tiles that share a
-// weight tile share an L2), then the pieces, dealt in turn, last.
+// the whole tiles as a contiguous run in pf_tile's order (tiles that share
+// operands share an L2), then the pieces, dealt in turn, last.
+//
+// Tile t of a k_pf_gemm_db launch: N-major in blocks of 4 weight tiles, so
+// that 32 consecutive tiles (one XCD's share of a round) are 8 activation
+// tiles x 4 weight tiles rather than 16 x 2 (a third fewer operand bytes
+// into that XCD's L2 per K step).
+__device__ __forceinline__ void pf_tile(int t, int tm, int tn, int& m0, int& n0) {
+  const int blk = t / (4 * tm), w = t % (4 * tm), nb = min(4, tn - 4 * blk);
+  m0 = (w / nb) * kPfBM;
+  n0 = (4 * blk + w % nb) * kPf2BN;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) half_t pf2_lds[];
@@ -253,7 +264,8 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
       s_end = min(s_begin + q, nsteps_all);
     }
   }
-  const int m0 = (t % a.tiles_m) * kPfBM, n0 = (t / a.tiles_m) * kPf2BN;
+  int m0, n0;
+  pf_tile(t, a.tiles_m, a.tiles_n, m0, n0);
 
   // loader: per K step a thread loads NA chunks of 4 activations (rows
   // arow + ARS i, floats acol ..) and NB chunks of 8 weights (rows lrow + BRS i,
@@ -380,8 +392,10 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
 // column c of the tile (for SwiGLU, gate and up columns in adjacent lanes).
 template <int EPI>
 __global__ __launch_bounds__(kPf2BN) void k_pf_fixup(PfGemmArgs a) {
-  const int u = blockIdx.x, t = a.full + u, c = threadIdx.x;
-  const int m0 = (t % a.tiles_m) * kPfBM, n = (t / a.tiles_m) * kPf2BN + c;
+  const int u = blockIdx.x, c = threadIdx.x;
+  int m0, n0;
+  pf_tile(a.full + u, a.tiles_m, a.tiles_n, m0, n0);
+  const int n = n0 + c;
   const float* pp = a.part + static_cast<size_t>(u) * a.split * kPfBM * kPf2BN + c;
   for (int rr = 0; rr < 8; ++rr) {
     const int row = blockIdx.y * 8 + rr, m = m0 + row;
