@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak, vendor figure
-PREFILL_CHUNK = 2048
+PREFILL_CHUNK = 3584
 
 # HBM bytes per gate/up GEMV launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (a 512 MiB device copy reads as 0.5x FETCH_SIZE, writes as 1.0x

@@ -388,27 +388,25 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
 
 // The split tiles of a k_pf_gemm_db launch: the sum of each element's
 // pieces in a fixed order, then the launch's epilogue as pf_write applies
-// it. Workgroup (u, y): tile full + u, tile rows 8 y .. 8 y + 7; thread c
-// column c of the tile (for SwiGLU, gate and up columns in adjacent lanes).
+// it. Workgroup (u, row): tile full + u, that row of it; thread c column c of
+// the tile (for SwiGLU, gate and up columns in adjacent lanes). A row per
+// workgroup keeps enough loads in flight over few split tiles.
 template <int EPI>
 __global__ __launch_bounds__(kPf2BN) void k_pf_fixup(PfGemmArgs a) {
-  const int u = blockIdx.x, c = threadIdx.x;
+  const int u = blockIdx.x, row = blockIdx.y, c = threadIdx.x;
   int m0, n0;
   pf_tile(a.full + u, a.tiles_m, a.tiles_n, m0, n0);
-  const int n = n0 + c;
-  const float* pp = a.part + static_cast<size_t>(u) * a.split * kPfBM * kPf2BN + c;
-  for (int rr = 0; rr < 8; ++rr) {
-    const int row = blockIdx.y * 8 + rr, m = m0 + row;
-    float v = 0.f;
-    for (int j = 0; j < a.split; ++j) v += pp[(static_cast<size_t>(j) * kPfBM + row) * kPf2BN];
-    if constexpr (EPI == kPfSwiGLU) {
-      const float up = lane_xor(v, 1);
-      if ((c & 1) == 0 && m < a.M && n < a.N)
-        put_split(reinterpret_cast<half_t*>(a.C) + static_cast<size_t>(m) * a.N, n >> 1, v / (1.0f + expf(-v)) * up);
-    } else if (m < a.M && n < a.N) {
-      float* dst = a.C + static_cast<size_t>(m) * a.N + n;
-      *dst = EPI == kPfAccum ? *dst + v : v;
-    }
+  const int m = m0 + row, n = n0 + c;
+  const float* pp = a.part + static_cast<size_t>(u) * a.split * kPfBM * kPf2BN + row * kPf2BN + c;
+  float v = 0.f;
+  for (int j = 0; j < a.split; ++j) v += pp[static_cast<size_t>(j) * kPfBM * kPf2BN];
+  if constexpr (EPI == kPfSwiGLU) {
+    const float up = lane_xor(v, 1);
+    if ((c & 1) == 0 && m < a.M && n < a.N)
+      put_split(reinterpret_cast<half_t*>(a.C) + static_cast<size_t>(m) * a.N, n >> 1, v / (1.0f + expf(-v)) * up);
+  } else if (m < a.M && n < a.N) {
+    float* dst = a.C + static_cast<size_t>(m) * a.N + n;
+    *dst = EPI == kPfAccum ? *dst + v : v;
   }
 }
 

@@ -995,7 +995,7 @@ void launch_pf_gemm(const half_t* A, const half_t* W, float* C, int M, int N, in
     g.split = s;
     g.part = part.p;
     hipLaunchKernelGGL(lf::k_pf_gemm_db<EPI>, dim3(g.full + R * s), dim3(lf::kPf2Threads), lf::kPf2Lds, st, g);
-    hipLaunchKernelGGL(lf::k_pf_fixup<EPI>, dim3(R, lf::kPfBM / 8), dim3(lf::kPf2BN), 0, st, g);
+    hipLaunchKernelGGL(lf::k_pf_fixup<EPI>, dim3(R, lf::kPfBM), dim3(lf::kPf2BN), 0, st, g);
     return;
   }
   lf::PfGemmArgs g{A, W, C, M, N, K, tm, (N + lf::kPfBN - 1) / lf::kPfBN};

@@ -206,11 +206,11 @@ def test_prefill_batched_wide_ragged_tiles():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,chunk", [("ctx1024", 200), ("ctx4096", 1024), ("ctx4096", 2048)])
+@pytest.mark.parametrize("name,chunk", [("ctx1024", 200), ("ctx4096", 1024), ("ctx4096", 2048), ("ctx4096", 3584)])
 def test_prefill_batched_full_size_matches_stored_oracle(name, chunk):
     """The 15-layer decoder's prompt (512 positions in chunks of 200, 200, 112;
     3584 in chunks of 1024, the last one 512; 3584 in chunks of 2048 and 1536,
-    where the tail tiles of the gate/up and QKV GEMMs are split over K), then
+    and as one chunk, where the tail tiles of the GEMMs are split over K), then
     32 teacher-forced decode steps over the cache it wrote, against the stored
     oracle results of the generation workload."""
     import torch
