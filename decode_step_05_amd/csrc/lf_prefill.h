@@ -212,8 +212,9 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
 // global loads: they are issued one K step ahead, and without them it runs
 // about 40% faster. Here the LDS holds two K steps and the registers two
 // more, so a step's loads have two compute phases to land: K step s is read
-// into a register set during step s - 2, split into hi / lo and written to
-// LDS stage s % 2 at the end of step s - 1, and multiplied during step s,
+// into a register set during step s - 2, written to LDS stage s % 2 (A's
+// hi and lo parts to their own arrays) at the end of step s - 1, and
+// multiplied during step s,
 // with one barrier per step. The wider tile reads a third fewer bytes of
 // operands from L2 per flop. Loads go through buffer descriptors (one per
 // operand, from the tile's first row) with a 32-bit per-lane offset, which
