@@ -431,7 +431,7 @@ struct PfAttnArgs {
   const half_t* kc;  // this layer's K cache [lanes][max_ctx][kpl][hd], keys 0..pos0+M-1 written
   const half_t* vc;
   half_t* o;         // [M][n_q * hd] attention outputs as split rows (input of the O projection)
-  int M, pos0, max_ctx, window, kpl, n_q;
+  int M, pos0, max_ctx, window, kpl, n_q, n_kv;
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
@@ -452,12 +452,21 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(16))) half_t Vt[HD * VLD];
   __shared__ __attribute__((aligned(16))) half_t Ks[32 * KLD];  // the tile's keys, staged once for all waves
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int kvh = blockIdx.y;
+  // Workgroup b runs on XCD b mod 8. With n_kv a multiple of 8, the query
+  // blocks of kv head kvh all go to XCD kvh / (n_kv / 8), so a kv head's keys
+  // and values are read through one L2 (2 heads of a 3584-position cache:
+  // 3.7 MB); the query blocks come in order, kv heads innermost.
+  int kvh, qb;
+  {
+    const int b = blockIdx.x, r = b % a.n_kv;
+    qb = b / a.n_kv;
+    kvh = (a.n_kv & 7) ? r : (r & 7) * (a.n_kv >> 3) + (r >> 3);
+  }
   const int head = kvh * G + w % G;
   const int ln = kvh / a.kpl, hk = kvh % a.kpl;
-  const int q_first = a.pos0 + blockIdx.x * QB * 32;  // the workgroup's query range
+  const int q_first = a.pos0 + qb * QB * 32;  // the workgroup's query range
   const int q_last = min(q_first + QB * 32 - 1, a.pos0 + a.M - 1);
-  const int qrow = (blockIdx.x * QB + w / G) * 32 + (lane & 31);  // chunk row of this lane's query (may pass M)
+  const int qrow = (qb * QB + w / G) * 32 + (lane & 31);  // chunk row of this lane's query (may pass M)
   const int qpos = a.pos0 + qrow;
   const int grp = lane >> 5;
 

@@ -1008,7 +1008,7 @@ void launch_pf_attn(const lf::PfAttnArgs& a, int hd, int G, int n_kv, hipStream_
 #define LF_PF_ATTN(HD, GG)                                                                          \
   if (hd == HD && G == GG) {                                                                        \
     constexpr int QB = GG <= 2 ? 2 : 1;                                                             \
-    hipLaunchKernelGGL((lf::k_pf_attn<HD, GG, QB>), dim3((a.M + 32 * QB - 1) / (32 * QB), n_kv),    \
+    hipLaunchKernelGGL((lf::k_pf_attn<HD, GG, QB>), dim3((a.M + 32 * QB - 1) / (32 * QB) * n_kv),    \
                        dim3(QB * GG * lf::kWave), 0, st, a);                                        \
     return;                                                                                         \
   }
@@ -1045,7 +1045,7 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
                      M, D.qkv_rows, D.hd, D.qpl, D.kpl, D.hq, D.ctx, pos0};
     hipLaunchKernelGGL(lf::k_pf_qkv, dim3((D.qkv_rows / 2 + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, qa);
     lf::PfAttnArgs aa{q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, h, M, pos0, D.ctx, c.window[l], D.kpl,
-                      D.hq, static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)))};
+                      D.hq, D.hkv, static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)))};
     launch_pf_attn(aa, D.hd, D.G, D.hkv, st);
     launch_pf_gemm<lf::kPfAccum>(h, m->at<half_t>(W.wo[l]), x, M, D.d, D.qdim, m->ncu, in_y, st);
     na.gain = m->at<half_t>(W.g2[l]);
