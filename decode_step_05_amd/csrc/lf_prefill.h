@@ -355,17 +355,23 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   __syncthreads();
   // Each step issues its loads first (the scheduling barriers keep them
   // there), then multiplies its stage, then writes the next step's stage
-  // (free since the barrier that ended the step before).
+  // (free since the barrier that ended the step before). A wave raises its
+  // priority while it multiplies, so that of the two waves on a SIMD the one
+  // with matrix work ready issues first (35.45 -> 34.95 ms per prompt pass).
   for (int s = s_begin; s < s_end; s += 2) {
     load(ra0, rb0, s + 2);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     compute(st0);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     store(ra1, rb1, s + 1, st1);
     __syncthreads();
     load(ra1, rb1, s + 3);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     compute(st1);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     store(ra0, rb0, s + 2, st0);
     __syncthreads();
