@@ -6,7 +6,7 @@ do. It shares no code with the HIP library: both sides receive the same seeded
 fp16 inputs and compute independently.
 
 What it computes (Kog Laneformer 2B blog, "Designing the architecture"): a
-basically standard decoder-only transformer, pre-norm, with causal
+largely ordinary decoder-only transformer, pre-norm, with causal
 grouped-query attention (32 query / 16 key-value heads), sliding-window
 attention on some layers, and a KV cache that every new token reads in full
 (the cache, like the weights, is what the blog says each token must stream).
