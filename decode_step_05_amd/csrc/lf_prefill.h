@@ -461,11 +461,13 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   // Workgroup b runs on XCD b mod 8. With n_kv a multiple of 8, the query
   // blocks of kv head kvh all go to XCD kvh / (n_kv / 8), so a kv head's keys
   // and values are read through one L2 (2 heads of a 3584-position cache:
-  // 3.7 MB); the query blocks come in order, kv heads innermost.
+  // 3.7 MB); kv heads innermost, the query blocks in reverse, so that the
+  // blocks with the most keys (causal rows grow with the position) start
+  // first and the short ones fill in behind them.
   int kvh, qb;
   {
     const int b = blockIdx.x, r = b % a.n_kv;
-    qb = b / a.n_kv;
+    qb = (gridDim.x / a.n_kv) - 1 - b / a.n_kv;
     kvh = (a.n_kv & 7) ? r : (r & 7) * (a.n_kv >> 3) + (r >> 3);
   }
   const int head = kvh * G + w % G;
