@@ -705,29 +705,47 @@ struct PfQkvArgs {
   int M, rows, hd, qpl, kpl, n_q, max_ctx, pos0;
 };
 
+// Thread i takes column pairs 4 i .. 4 i + 3 of row t: dimensions c .. c + 3
+// and c + hd/2 .. c + hd/2 + 3 of one head (hd a multiple of 8), 16-byte
+// loads and 16- / 8-byte stores.
 __global__ __launch_bounds__(kBlock) void k_pf_qkv(PfQkvArgs a) {
   const int i = blockIdx.x * kBlock + threadIdx.x, t = blockIdx.y;
-  if (2 * i >= a.rows) return;
-  const float2 y = reinterpret_cast<const float2*>(a.y + static_cast<size_t>(t) * a.rows)[i];
-  const int r = 2 * i, half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl, p = a.pos0 + t;
+  if (8 * i >= a.rows) return;
+  const float* yr = a.y + static_cast<size_t>(t) * a.rows + 8 * i;
+  const f32x4 ya = *reinterpret_cast<const f32x4*>(yr), yb = *reinterpret_cast<const f32x4*>(yr + 4);
+  const int r = 8 * i, half_hd = a.hd >> 1, upl = a.qpl + 2 * a.kpl, p = a.pos0 + t;
   const int u = r / a.hd, c = (r % a.hd) >> 1;
   const int ln = u / upl, j = u % upl;
-  float y0 = y.x, y1 = y.y;
+  const float y0[4] = {ya[0], ya[2], yb[0], yb[2]}, y1[4] = {ya[1], ya[3], yb[1], yb[3]};
+  f32x4 o0, o1;  // dimensions c .. c + 3 and c + hd/2 ..
   if (j < a.qpl + a.kpl) {
-    const float2 cs = a.rope[static_cast<size_t>(p) * half_hd + c];
-    y0 = y.x * cs.x - y.y * cs.y;
-    y1 = y.x * cs.y + y.y * cs.x;
+    const f32x4* rp = reinterpret_cast<const f32x4*>(a.rope + static_cast<size_t>(p) * half_hd + c);
+    const f32x4 ca = rp[0], cb = rp[1];  // (cos, sin) of pairs c, c + 1 and c + 2, c + 3
+    const float cs[4] = {ca[0], ca[2], cb[0], cb[2]}, sn[4] = {ca[1], ca[3], cb[1], cb[3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = y0[e] * cs[e] - y1[e] * sn[e];
+      o1[e] = y0[e] * sn[e] + y1[e] * cs[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = y0[e];
+      o1[e] = y1[e];
+    }
   }
   if (j < a.qpl) {
     float* qh = a.q + (static_cast<size_t>(t) * a.n_q + ln * a.qpl + j) * a.hd;
-    qh[c] = y0;
-    qh[c + half_hd] = y1;
+    *reinterpret_cast<f32x4*>(qh + c) = o0;
+    *reinterpret_cast<f32x4*>(qh + c + half_hd) = o1;
   } else {
     const bool is_k = j < a.qpl + a.kpl;
     const int h = is_k ? j - a.qpl : j - a.qpl - a.kpl;
     half_t* dst = (is_k ? a.kc : a.vc) + ((static_cast<size_t>(ln) * a.max_ctx + p) * a.kpl + h) * a.hd;
-    dst[c] = static_cast<half_t>(y0);
-    dst[c + half_hd] = static_cast<half_t>(y1);
+    const h4 k0 = {static_cast<half_t>(o0[0]), static_cast<half_t>(o0[1]), static_cast<half_t>(o0[2]), static_cast<half_t>(o0[3])};
+    const h4 k1 = {static_cast<half_t>(o1[0]), static_cast<half_t>(o1[1]), static_cast<half_t>(o1[2]), static_cast<half_t>(o1[3])};
+    *reinterpret_cast<h4*>(dst + c) = k0;
+    *reinterpret_cast<h4*>(dst + c + half_hd) = k1;
   }
 }
 

@@ -1043,7 +1043,7 @@ void enqueue_pf_chunk(lf_model* m, lf_kv* kv, char* ws, const PfLayout& P, int M
     launch_pf_gemm<lf::kPfStore>(h, m->at<half_t>(W.wqkv[l]), y, M, D.qkv_rows, D.d, m->ncu, past_norm, st);
     lf::PfQkvArgs qa{y, q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, m->at<float2>(W.rope),
                      M, D.qkv_rows, D.hd, D.qpl, D.kpl, D.hq, D.ctx, pos0};
-    hipLaunchKernelGGL(lf::k_pf_qkv, dim3((D.qkv_rows / 2 + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, qa);
+    hipLaunchKernelGGL(lf::k_pf_qkv, dim3((D.qkv_rows / 8 + lf::kBlock - 1) / lf::kBlock, M), dim3(lf::kBlock), 0, st, qa);
     lf::PfAttnArgs aa{q, kv->kc() + l * layer_cache, kv->vc() + l * layer_cache, h, M, pos0, D.ctx, c.window[l], D.kpl,
                       D.hq, D.hkv, static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D.hd)))};
     launch_pf_attn(aa, D.hd, D.G, D.hkv, st);
