@@ -303,6 +303,17 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
     half_t* Al = As + kPfBM * kPfLd;
     half_t* Bs = Al + kPfBM * kPfLd;
     const int k0 = step * kPfBK;
+    if (k0 + kPfBK <= kend) {  // the whole step inside K (uniform): plain copies
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const u32x2 hi = {ra[i][0], ra[i][1]}, lo = {ra[i][2], ra[i][3]};
+        *reinterpret_cast<u32x2*>(&As[(arow + ARS * i) * kPfLd + acol]) = hi;
+        *reinterpret_cast<u32x2*>(&Al[(arow + ARS * i) * kPfLd + acol]) = lo;
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4*>(&Bs[(lrow + BRS * i) * kPfLd + lcol]) = rb[i];
+      return;
+    }
     const bool ina = k0 + acol < kend, inb = k0 + lcol < kend;  // K is a multiple of 8
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
