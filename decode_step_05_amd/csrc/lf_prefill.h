@@ -218,10 +218,11 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfGemmArgs a) {
 // with one barrier per step. The wider tile reads a third fewer bytes of
 // operands from L2 per flop. Loads go through buffer descriptors (one per
 // operand, from the tile's first row) with a 32-bit per-lane offset, which
-// keeps 64-bit addresses out of the vector registers. K steps past the last
-// (an odd count is rounded up to even) and the k past K of the last step
-// load clamped in-range data (the row's last chunk) and are written to LDS
-// as zeros.
+// keeps 64-bit addresses out of the vector registers; the K step is a scalar
+// offset. K steps past the last (an odd count is rounded up to even) load the
+// last step again, and the k past K of a part-filled last step read past the
+// row (the next row, or zeros past the descriptor's range); both are written
+// to LDS as zeros.
 constexpr int kPf2BN = 256, kPf2Threads = 512;
 constexpr int kPf2Stage = (2 * kPfBM + kPf2BN) * kPfLd;  // halves per LDS stage (A hi, A lo, W)
 constexpr int kPf2Lds = 2 * kPf2Stage * static_cast<int>(sizeof(half_t));
@@ -279,24 +280,25 @@ __global__ __launch_bounds__(kPf2Threads) void k_pf_gemm_db(PfGemmArgs a) {
   const size_t bbytes = static_cast<size_t>(a.N - n0) * a.K * sizeof(half_t);
   const rsrc_t ar = rsrc_of(a.A + static_cast<size_t>(m0) * a.K * 2, static_cast<int>(min(abytes, size_t(0x7fffffff))));
   const rsrc_t br = rsrc_of(a.W + static_cast<size_t>(n0) * a.K, static_cast<int>(min(bbytes, size_t(0x7fffffff))));
-  int arow_off[NA], brow_off[NB];  // elements from the descriptor's base to the row
+  // byte offsets of this thread's chunks at k = 0 from the descriptors' bases;
+  // a step adds k0 as the scalar offset. Chunks of the last step past K read
+  // the next row, or zeros past a descriptor's range, and are zeroed in LDS.
+  int avo[NA], bvo[NB];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) arow_off[i] = min(arow + ARS * i, a.M - 1 - m0) * a.K;
+  for (int i = 0; i < NA; ++i) avo[i] = (min(arow + ARS * i, a.M - 1 - m0) * a.K + acol) * 4;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) brow_off[i] = min(lrow + BRS * i, a.N - 1 - n0) * a.K;
+  for (int i = 0; i < NB; ++i) bvo[i] = (min(lrow + BRS * i, a.N - 1 - n0) * a.K + lcol) * static_cast<int>(sizeof(half_t));
   const int kend = min(a.K, s_end * kPfBK);  // k past this are zero (a piece's K run ends here)
 
   u32x4 ra0[NA], ra1[NA];
   u32x4 rb0[NB], rb1[NB];
   auto load = [&](u32x4 (&ra)[NA], u32x4 (&rb)[NB], int step) {
     const int k0 = max(min(step, s_end - 1), 0) * kPfBK;
-    const int ka = min(k0 + acol, a.K - 4), kb = min(k0 + lcol, a.K - 8);
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, (arow_off[i] + ka) * 4, 0, 0);
+    for (int i = 0; i < NA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, avo[i], k0 * 4, 0);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, (brow_off[i] + kb) * static_cast<int>(sizeof(half_t)), 0, 0);
+      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, bvo[i], k0 * static_cast<int>(sizeof(half_t)), 0);
   };
   auto store = [&](const u32x4 (&ra)[NA], const u32x4 (&rb)[NB], int step, half_t* stage) {
     half_t* As = stage;
