@@ -489,6 +489,7 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
   const int q_last = min(q_first + QB * 32 - 1, a.pos0 + a.M - 1);
   const int qrow = (qb * QB + w / G) * 32 + (lane & 31);  // chunk row of this lane's query (may pass M)
   const int qpos = a.pos0 + qrow;
+  const int qbase = qpos - (lane & 31);  // the wave's 32 queries: positions qbase .. qbase + 31
   const int grp = lane >> 5;
 
   // This lane's query fragments (B operand of S^T: query l % 32, head
@@ -581,12 +582,20 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
 
     float s[16];
     float mx = -INFINITY;
+    if (k0 + 31 <= qbase && (a.window == 0 || k0 > qbase + 31 - a.window)) {  // the wave sees every key of the tile
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
-      const bool vis = key <= qpos && (a.window == 0 || key > qpos - a.window);
-      s[r] = vis ? (sa[r] + sb[r]) * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[r]);
+      for (int r = 0; r < 16; ++r) {
+        s[r] = (sa[r] + sb[r]) * a.scale_log2;
+        mx = fmaxf(mx, s[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
+        const bool vis = key <= qpos && (a.window == 0 || key > qpos - a.window);
+        s[r] = vis ? (sa[r] + sb[r]) * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
@@ -603,10 +612,11 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
     m_run = m_new;
+    if (__ballot(alpha != 1.f))  // a running max moved (once the maxima settle, most tiles skip this)
 #pragma unroll
-    for (int th = 0; th < HD / 32; ++th)
+      for (int th = 0; th < HD / 32; ++th)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ot[th][r] *= alpha;
+        for (int r = 0; r < 16; ++r) ot[th][r] *= alpha;
     // P^T in B-operand order: register r = 8 mm + s holds key 16 mm + 8 (s / 4) + 4 grp + s % 4,
     // which is where the A operand (V^T) takes its k slot s from
 #pragma unroll
