@@ -599,12 +599,17 @@ __global__ __launch_bounds__(QB * G * kWave) __attribute__((amdgpu_waves_per_eu(
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
+    // v_exp_f32 directly: exp2(-inf) = 0, and results below 2^-126, whose
+    // handling is what the library's exp2f adds, vanish in the fp16 parts
+    // and the sums anyway. A query that has seen no key yet (m_new = -inf)
+    // subtracts 0 instead, so that its masked scores give 0, not NaN.
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
     h8 pf[2], pl[2];
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = s[r] == -INFINITY ? 0.f : exp2f(s[r] - m_new);
+      const float p = __builtin_amdgcn_exp2f(s[r] - m_ref);
       ps += p;
       pf[r >> 3][r & 7] = static_cast<half_t>(p);
       pl[r >> 3][r & 7] = static_cast<half_t>(p - static_cast<float>(pf[r >> 3][r & 7]));
